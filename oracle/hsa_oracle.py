@@ -1,0 +1,406 @@
+"""CPU oracle for Heterogeneous Step Allocation (HSA): one global denoising iteration.
+
+TEST INFRASTRUCTURE ONLY.  Only tests/, __graft_entry__.smoke() and bench.py's
+cpu_baseline leg may import or call this module.  The product path (the HIP
+library and its Python binding) never does.
+
+Plain, slow and meant to be read against the source pages: "Not All Tokens Need
+40 Steps: Heterogeneous Step Allocation in Diffusion Transformers for Efficient
+Video Generation" (gist.science technical summary; section numbers below refer
+to it).  All arithmetic is float64.  Values are rounded only at the points where
+the method's data are stored (latents, caches, activations handed from one
+operation to the next): float32 in float32 workloads, bfloat16 for the
+activations and caches of bfloat16 workloads (see `Store`).
+
+Readings where the pages leave a step open (each is listed in the design doc):
+  * iteration index i is 0-based, i in [0, T): every group is active at i = 0;
+  * sigma_i = 1 - i/T;
+  * block = pre-LayerNorm (no affine, eps 1e-6) multi-head self-attention
+    (scale 1/sqrt(Dh), no mask, no biases), optional pre-LN cross-attention,
+    pre-LN GELU(tanh) MLP, residual adds; embed C->D, unembed LN then D->C;
+  * L1 relative change r_n = sum_c |v_new - v_hat| / (sum_c |v_hat| + eps),
+    eps = 1e-6, updated for active tokens at i >= 1, +inf before;
+  * regrouping ranks tokens by (score descending, index ascending), NaN as
+    +inf and -0 as +0; the first n_1 go to G_1, the next n_2 to G_2, ...
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+
+LN_EPS = 1e-6
+SCORE_EPS = 1e-6
+
+
+# ----------------------------------------------------------------------------
+# Storage rounding.
+# ----------------------------------------------------------------------------
+
+def round_to_bf16(a: np.ndarray) -> np.ndarray:
+    """Nearest bfloat16 value (ties to even) of each element, returned as float64.
+
+    Written with frexp/ldexp: a = f * 2^e with 0.5 <= |f| < 1; bfloat16 keeps
+    8 significant bits, so the spacing of representable values near a is
+    2^(e-8), but never below the subnormal spacing 2^-133 (bfloat16 has
+    float32's exponent range and 7 stored fraction bits).  a is rounded to a
+    multiple of that spacing with numpy's round-half-even.  Finite inputs
+    only (the method produces no inf/NaN in activations).
+    """
+    a = np.asarray(a, dtype=np.float64)
+    a32 = a.astype(np.float32).astype(np.float64)   # storage goes through fp32 first
+    _, e = np.frexp(a32)
+    quantum = np.ldexp(1.0, np.maximum(e - 8, -133))
+    return np.round(a32 / quantum) * quantum
+
+
+def round_to_f32(a: np.ndarray) -> np.ndarray:
+    return np.asarray(a, dtype=np.float64).astype(np.float32).astype(np.float64)
+
+
+@dataclasses.dataclass
+class Store:
+    """Where values are rounded: `act` for GEMM operands, q/k/v/o, MLP hidden
+    and the K/V caches; `res` for the residual stream, latents and velocities."""
+    bf16: bool
+
+    def act(self, a):
+        return round_to_bf16(a) if self.bf16 else round_to_f32(a)
+
+    def res(self, a):
+        return round_to_f32(a)
+
+
+# ----------------------------------------------------------------------------
+# Token partitioning and scheduling (section 2.1) and phase window (2.4).
+# ----------------------------------------------------------------------------
+
+def active_mask(group: np.ndarray, budgets: Sequence[int], T: int, i: int,
+                m: int = 0) -> np.ndarray:
+    """Token n is active at iteration i iff i mod (T / s_{g(n)}) == 0.
+
+    G_1 has s_1 = T (period 1) and is active every iteration.  With a phase
+    window m > 0 every token is active in the first and last m iterations.
+    """
+    budgets = np.asarray(budgets, dtype=np.int64)
+    assert budgets[0] == T and np.all(T % budgets == 0)
+    if i < m or i >= T - m:
+        return np.ones(group.shape[0], dtype=bool)
+    period = T // budgets[group.astype(np.int64)]
+    return (i % period) == 0
+
+
+def active_set(group, budgets, T, i, m=0):
+    """Ascending list A_i of active token indices and its inverse map
+    pos[n] = j if A_i[j] == n, else -1 (section 2.2, item 1)."""
+    mask = active_mask(group, budgets, T, i, m)
+    idx = np.flatnonzero(mask).astype(np.int32)
+    pos = np.full(group.shape[0], -1, dtype=np.int32)
+    pos[idx] = np.arange(idx.size, dtype=np.int32)
+    return idx, pos
+
+
+def n_active_closed_form(counts, budgets, T, i, m=0) -> int:
+    """|A_i| = sum_k n_k [i mod (T/s_k) == 0]; every token in the phase window."""
+    if i < m or i >= T - m:
+        return int(sum(counts))
+    return int(sum(n for n, s in zip(counts, budgets) if i % (T // s) == 0))
+
+
+# ----------------------------------------------------------------------------
+# Dynamic token selection (section 2.1): rank by L1 relative change.
+# ----------------------------------------------------------------------------
+
+def select_groups(score: np.ndarray, counts: Sequence[int]) -> np.ndarray:
+    """Group of each token: tokens ranked by (score desc, index asc); ranks
+    [0, n_1) -> group 0, [n_1, n_1 + n_2) -> group 1, ...  NaN ranks as +inf,
+    -0 as +0."""
+    s = np.asarray(score, dtype=np.float32).astype(np.float64)
+    s = np.where(np.isnan(s), np.inf, s)
+    s = np.where(s == 0.0, 0.0, s)
+    N = s.shape[0]
+    assert sum(counts) == N
+    order = np.lexsort((np.arange(N), -s))
+    group = np.empty(N, dtype=np.uint8)
+    start = 0
+    for k, n in enumerate(counts):
+        group[order[start:start + n]] = k
+        start += n
+    return group
+
+
+def l1_relative_change(v_new: np.ndarray, v_old: np.ndarray, eps=SCORE_EPS) -> np.ndarray:
+    """r = ||v_new - v_old||_1 / (||v_old||_1 + eps) per row, over channels."""
+    v_new = np.asarray(v_new, np.float64)
+    v_old = np.asarray(v_old, np.float64)
+    num = np.abs(v_new - v_old).sum(axis=-1)
+    den = np.abs(v_old).sum(axis=-1) + eps
+    return num / den
+
+
+# ----------------------------------------------------------------------------
+# Model pieces.
+# ----------------------------------------------------------------------------
+
+def layer_norm(y: np.ndarray, eps=LN_EPS) -> np.ndarray:
+    """(y - mean) / sqrt(var + eps) over the last axis, population variance, no affine."""
+    y = np.asarray(y, np.float64)
+    mu = y.mean(axis=-1, keepdims=True)
+    var = ((y - mu) ** 2).mean(axis=-1, keepdims=True)
+    return (y - mu) / np.sqrt(var + eps)
+
+
+def gelu_tanh(u: np.ndarray) -> np.ndarray:
+    """GELU, tanh form: 0.5 u (1 + tanh(sqrt(2/pi) (u + 0.044715 u^3)))."""
+    u = np.asarray(u, np.float64)
+    return 0.5 * u * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (u + 0.044715 * u ** 3)))
+
+
+def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, H: int, Dh: int,
+              scale: Optional[float] = None) -> np.ndarray:
+    """Multi-head softmax attention of M query rows over all Nk key/value rows.
+
+    q: [M][H*Dh], k, v: [Nk][H*Dh] -> [M][H*Dh].  Per head h:
+    o = softmax(q_h k_h^T * scale) v_h with the row max subtracted first.
+    No mask: every query sees every row (section 2.2, item 3).
+    """
+    if scale is None:
+        scale = 1.0 / np.sqrt(Dh)
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    M, Nk = q.shape[0], k.shape[0]
+    out = np.empty((M, H * Dh), dtype=np.float64)
+    for h in range(H):
+        sl = slice(h * Dh, (h + 1) * Dh)
+        s = (q[:, sl] @ k[:, sl].T) * scale
+        s = s - s.max(axis=1, keepdims=True)
+        p = np.exp(s)
+        p = p / p.sum(axis=1, keepdims=True)
+        out[:, sl] = p @ v[:, sl]
+    return out
+
+
+@dataclasses.dataclass
+class Dims:
+    N: int
+    C: int
+    D: int
+    H: int
+    Dh: int
+    F: int
+    L: int
+    bf16: bool
+    n_text: int = 0
+
+
+@dataclasses.dataclass
+class Model:
+    """Weights as float64 copies of the stored values, all out-major [out][in]:
+    w_in [D][C], w_out [C][D]; per block w_qkv [3D][D], w_o [D][D], w_1 [F][D],
+    w_2 [D][F]; cross-attention w_qx, w_ox [D][D] and per-layer text K/V."""
+    dims: Dims
+    w_in: np.ndarray
+    w_out: np.ndarray
+    blocks: List[Dict[str, np.ndarray]]
+
+    @property
+    def store(self) -> Store:
+        return Store(self.dims.bf16)
+
+
+def make_model(dims: Dims, io: Dict[str, np.ndarray], blocks: List[Dict[str, np.ndarray]],
+               text: Optional[Dict[str, np.ndarray]] = None) -> Model:
+    f64 = lambda a: np.asarray(a, dtype=np.float64)
+    bl = [{k: f64(v) for k, v in b.items()} for b in blocks]
+    m = Model(dims, f64(io["w_in"]), f64(io["w_out"]), bl)
+    if dims.n_text:
+        assert text is not None
+        st = m.store
+        E = st.act(f64(text["text"]) @ f64(text["w_t"]).T)   # text embedding, once per run
+        for b in m.blocks:
+            b["k_text"] = st.act(E @ b["w_kx"].T)
+            b["v_text"] = st.act(E @ b["w_vx"].T)
+    return m
+
+
+def embed(model: Model, x: np.ndarray, idx: np.ndarray) -> np.ndarray:
+    """h = x[A] W_in^T, the residual stream of the active rows."""
+    return model.store.res(np.asarray(x, np.float64)[idx] @ model.w_in.T)
+
+
+def unembed(model: Model, h: np.ndarray) -> np.ndarray:
+    """v_new = LN(h) W_out^T (float32 velocities)."""
+    return round_to_f32(layer_norm(h) @ model.w_out.T)
+
+
+def block_forward(model: Model, l: int, h: np.ndarray, idx: np.ndarray,
+                  k_cache: np.ndarray, v_cache: np.ndarray,
+                  rows: Optional[np.ndarray] = None) -> np.ndarray:
+    """One transformer block on the active rows with KV-cache synchronisation
+    (section 2.2):
+      1. only active rows go through the QKV projection;
+      2. their fresh K/V overwrite rows A_i of this layer's cache (in place);
+      3. active queries attend over all N cached rows, fresh and stale;
+      4. out-projection, cross-attention and MLP run on active rows only.
+    `rows` (indices into A_i) restricts steps 3-4 to a sample of the active
+    rows; the cache update always covers every active row.  Returns the new
+    residual rows ([len(rows)][D], or [|A|][D] when rows is None).
+    """
+    d = model.dims
+    st = model.store
+    b = model.blocks[l]
+    D = d.D
+    h = np.asarray(h, np.float64)
+    a = st.act(layer_norm(h))
+    kv = a @ b["w_qkv"][D:].T
+    k_cache[idx] = st.act(kv[:, :D])
+    v_cache[idx] = st.act(kv[:, D:])
+    if rows is not None:
+        h = h[rows]
+        a = a[rows]
+    q = st.act(a @ b["w_qkv"][:D].T)
+    o = st.act(attention(q, k_cache, v_cache, d.H, d.Dh))
+    h = st.res(h + o @ b["w_o"].T)
+    if d.n_text:
+        ax = st.act(layer_norm(h))
+        qx = st.act(ax @ b["w_qx"].T)
+        ox = st.act(attention(qx, b["k_text"], b["v_text"], d.H, d.Dh))
+        h = st.res(h + ox @ b["w_ox"].T)
+    a2 = st.act(layer_norm(h))
+    u = st.act(gelu_tanh(a2 @ b["w_1"].T))
+    h = st.res(h + u @ b["w_2"].T)
+    return h
+
+
+# ----------------------------------------------------------------------------
+# Cached Euler update (section 2.3) with the L1 score of section 2.1.
+# ----------------------------------------------------------------------------
+
+def euler_update(x, v_hat, score, v_new, idx, dsigma, update_score, eps=SCORE_EPS):
+    """Returns new (x, v_hat, score).
+
+    For active tokens (rows idx, with fresh velocities v_new in the same order):
+    if update_score, score = L1 relative change between v_new and the cached
+    v_hat; then v_hat <- v_new.  Every token then advances by
+    x <- x + dsigma * v_hat: fresh velocity if active, cached if skipped.
+    """
+    x = np.asarray(x, np.float64)
+    v_hat = np.array(v_hat, np.float64)
+    score = np.array(score, np.float64)
+    v_new = np.asarray(v_new, np.float64)
+    if update_score:
+        score[idx] = round_to_f32(l1_relative_change(v_new, v_hat[idx], eps))
+    v_hat[idx] = v_new
+    x_new = round_to_f32(x + np.float64(dsigma) * v_hat)
+    return x_new, round_to_f32(v_hat), round_to_f32(score)
+
+
+# ----------------------------------------------------------------------------
+# One HSA iteration and the sampling loop.
+# ----------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class Schedule:
+    T: int
+    budgets: List[int]
+    counts: List[int]
+    m: int = 0
+    regroup: Sequence[int] = ()
+
+
+@dataclasses.dataclass
+class State:
+    x: np.ndarray            # [N][C] float32 values
+    v_hat: np.ndarray        # [N][C]
+    score: np.ndarray        # [N]
+    group: np.ndarray        # [N] uint8
+    k_cache: np.ndarray      # [L][N][D]
+    v_cache: np.ndarray      # [L][N][D]
+
+    def copy(self) -> "State":
+        return State(*(np.array(a) for a in dataclasses.astuple(self)))
+
+
+def init_state(dims: Dims, x0: np.ndarray, group0: np.ndarray) -> State:
+    N, C, D, L = dims.N, dims.C, dims.D, dims.L
+    return State(x=np.asarray(x0, np.float64).copy(),
+                 v_hat=np.zeros((N, C)), score=np.full(N, np.inf),
+                 group=np.asarray(group0, np.uint8).copy(),
+                 k_cache=np.zeros((L, N, D)), v_cache=np.zeros((L, N, D)))
+
+
+def dsigma_f32(sigma_i, sigma_next) -> np.float32:
+    """The Euler increment sigma_{i+1} - sigma_i as a float32 scalar."""
+    return np.float32(np.float32(sigma_next) - np.float32(sigma_i))
+
+
+def hsa_iteration(model: Model, sched: Schedule, state: State, i: int,
+                  sigma_i: float, sigma_next: float, regroup: bool,
+                  v_field: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+    """One global iteration, in place on `state`:
+      regroup (at the start of i, before A_i) -> A_i -> embed -> L blocks ->
+      unembed -> cached Euler with score update.
+    `v_field` ([N][C]) replaces the model's velocity for the active tokens in
+    the Euler/score path when given (the model still runs).
+    Returns the per-iteration intermediates (active list, pos, v_new)."""
+    if regroup:
+        state.group = select_groups(state.score, sched.counts)
+    idx, pos = active_set(state.group, sched.budgets, sched.T, i, sched.m)
+    h = embed(model, state.x, idx)
+    for l in range(model.dims.L):
+        h = block_forward(model, l, h, idx, state.k_cache[l], state.v_cache[l])
+    v_new = unembed(model, h)
+    if v_field is not None:
+        v_new = np.asarray(v_field, np.float64)[idx]
+    state.x, state.v_hat, state.score = euler_update(
+        state.x, state.v_hat, state.score, v_new, idx, dsigma_f32(sigma_i, sigma_next),
+        update_score=(i >= 1))
+    return {"active_idx": idx, "pos": pos, "v_new": v_new}
+
+
+def sample(model: Model, sched: Schedule, state: State, sigma: np.ndarray,
+           field=None, iters: Optional[Sequence[int]] = None) -> List[Dict[str, np.ndarray]]:
+    """Run iterations (default 0..T-1), regrouping at the start of each
+    iteration listed in sched.regroup."""
+    trace = []
+    for i in (range(sched.T) if iters is None else iters):
+        vf = field(i) if field is not None else None
+        trace.append(hsa_iteration(model, sched, state, i, sigma[i], sigma[i + 1],
+                                   regroup=(i in set(sched.regroup)), v_field=vf))
+    return trace
+
+
+# ----------------------------------------------------------------------------
+# Dense reference: the plain DiT forward over all N tokens, no cache, no
+# active list.  With every s_k = T the HSA iteration must reduce to this.
+# ----------------------------------------------------------------------------
+
+def dense_velocity(model: Model, x: np.ndarray) -> np.ndarray:
+    d = model.dims
+    st = model.store
+    D = d.D
+    h = st.res(np.asarray(x, np.float64) @ model.w_in.T)
+    for b in model.blocks:
+        a = st.act(layer_norm(h))
+        q = st.act(a @ b["w_qkv"][:D].T)
+        k = st.act(a @ b["w_qkv"][D:2 * D].T)
+        v = st.act(a @ b["w_qkv"][2 * D:].T)
+        h = st.res(h + st.act(attention(q, k, v, d.H, d.Dh)) @ b["w_o"].T)
+        if d.n_text:
+            ax = st.act(layer_norm(h))
+            qx = st.act(ax @ b["w_qx"].T)
+            h = st.res(h + st.act(attention(qx, b["k_text"], b["v_text"], d.H, d.Dh)) @ b["w_ox"].T)
+        a2 = st.act(layer_norm(h))
+        h = st.res(h + st.act(gelu_tanh(a2 @ b["w_1"].T)) @ b["w_2"].T)
+    return round_to_f32(layer_norm(h) @ model.w_out.T)
+
+
+def dense_euler_sample(model: Model, x0: np.ndarray, sigma: np.ndarray, T: int) -> np.ndarray:
+    """Plain Euler flow-matching loop: x_{i+1} = x_i + (sigma_{i+1} - sigma_i) v(x_i)."""
+    x = round_to_f32(x0)
+    for i in range(T):
+        v = dense_velocity(model, x)
+        x = round_to_f32(x + np.float64(dsigma_f32(sigma[i], sigma[i + 1])) * v)
+    return x
