@@ -1,0 +1,316 @@
+"""GPU parity of each HIP kernel against the CPU oracle, through the C ABI.
+
+Integer results (active set, groups, scatter positions) must match bit for
+bit; floating results within relative L2 1e-4 (float32) or 2e-2 (bfloat16).
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import hsa_oracle as O
+from tests.gpu_common import DEV, TOL_BF16, TOL_F32, dev, host, rel_l2, say
+
+pytestmark = pytest.mark.gpu
+
+H = None
+
+
+@pytest.fixture(scope="module", autouse=True)
+def lib():
+    global H
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from token_sparse_attention_compact_amd import hsa
+    hsa.load()
+    H = hsa
+    yield hsa
+
+
+def bf(a):
+    return synth.to_bf16_values(np.asarray(a, np.float32))
+
+
+# ---------------------------------------------------------------- active set
+
+@pytest.mark.parametrize("N", [1, 255, 4096, 4097, 32760, 75600])
+def test_active_set_bit_exact(N):
+    say(f"active_set N={N}")
+    rs = np.random.default_rng(N)
+    T, budgets = 40, [40, 20, 10]
+    group = rs.integers(0, 3, N).astype(np.uint8)
+    counts = np.bincount(group, minlength=3).tolist()
+    sched = H.make_schedule(T, budgets, counts)
+    g = dev(group, torch.uint8)
+    idx = torch.full((N,), -7, dtype=torch.int32, device=DEV)
+    pos = torch.full((N,), -7, dtype=torch.int32, device=DEV)
+    nd = torch.zeros(1, dtype=torch.int32, device=DEV)
+    for i in [0, 1, 2, 3, 4, 39]:
+        H.hsa_active_set(g, sched, i, idx, pos, nd)
+        torch.cuda.synchronize()
+        ref_idx, ref_pos = O.active_set(group, budgets, T, i)
+        nA = H.hsa_n_active(sched, i)
+        assert nA == ref_idx.size == int(nd.item())
+        np.testing.assert_array_equal(idx[:nA].cpu().numpy(), ref_idx)
+        np.testing.assert_array_equal(pos.cpu().numpy(), ref_pos)
+
+
+def test_active_set_phase_window():
+    N, T = 1000, 40
+    rs = np.random.default_rng(5)
+    group = rs.integers(0, 3, N).astype(np.uint8)
+    counts = np.bincount(group, minlength=3).tolist()
+    sched = H.make_schedule(T, [40, 20, 10], counts, m=3)
+    g = dev(group, torch.uint8)
+    idx = torch.zeros(N, dtype=torch.int32, device=DEV)
+    pos = torch.zeros(N, dtype=torch.int32, device=DEV)
+    nd = torch.zeros(1, dtype=torch.int32, device=DEV)
+    for i in [0, 2, 3, 5, 36, 37, 39]:
+        H.hsa_active_set(g, sched, i, idx, pos, nd)
+        ref_idx, ref_pos = O.active_set(group, [40, 20, 10], T, i, m=3)
+        assert int(nd.item()) == ref_idx.size == H.hsa_n_active(sched, i)
+        np.testing.assert_array_equal(pos.cpu().numpy(), ref_pos)
+
+
+# ---------------------------------------------------------------- selection
+
+def _select_case(score, counts):
+    s = dev(score, torch.float32)
+    out = torch.full((score.size,), 255, dtype=torch.uint8, device=DEV)
+    H.hsa_select(s, counts, out)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out.cpu().numpy(), O.select_groups(score, counts))
+
+
+@pytest.mark.parametrize("N,K", [(1, 1), (10, 2), (1000, 3), (1000, 8), (32760, 3), (75600, 3), (4099, 5)])
+def test_select_bit_exact(N, K):
+    say(f"select N={N} K={K}")
+    rs = np.random.default_rng(N * 10 + K)
+    cuts = np.sort(rs.integers(0, N + 1, K - 1))
+    counts = np.diff(np.concatenate([[0], cuts, [N]])).astype(int).tolist()
+    # continuous scores
+    _select_case(np.abs(rs.standard_normal(N)).astype(np.float32), counts)
+    # heavy ties and special values across the boundaries
+    s = (rs.integers(0, 4, N) * 0.5).astype(np.float32)
+    sp = rs.choice(N, size=min(N, 7), replace=False)
+    s[sp] = np.array([np.nan, np.inf, -0.0, 0.0, -1.0, np.inf, np.nan], np.float32)[: sp.size]
+    _select_case(s, counts)
+    # all equal
+    _select_case(np.full(N, 0.25, np.float32), counts)
+
+
+def test_select_golden_fixtures():
+    import json, os
+    for name in ("select_adversarial.json", "select_ties.json"):
+        g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", name)))
+        s = np.array([float(x) for x in g["score"]], np.float32)
+        out = torch.zeros(s.size, dtype=torch.uint8, device=DEV)
+        H.hsa_select(dev(s), g["counts"], out)
+        assert out.cpu().tolist() == g["group"]
+
+
+def test_select_zero_count_groups():
+    rs = np.random.default_rng(11)
+    N = 3000
+    s = rs.standard_normal(N).astype(np.float32)
+    for counts in ([0, 1000, 2000], [1000, 0, 2000], [1000, 2000, 0], [3000, 0, 0], [0, 0, 3000]):
+        _select_case(s, counts)
+
+
+# ---------------------------------------------------------------- cached Euler
+
+@pytest.mark.parametrize("N,C", [(1, 16), (333, 16), (32760, 16), (100, 8)])
+def test_euler_matches_oracle(N, C):
+    say(f"euler N={N} C={C}")
+    rs = np.random.default_rng(N + C)
+    x = rs.standard_normal((N, C)).astype(np.float32)
+    vh = rs.standard_normal((N, C)).astype(np.float32)
+    sc = np.abs(rs.standard_normal(N)).astype(np.float32)
+    act = np.sort(rs.choice(N, size=max(1, N // 3), replace=False)).astype(np.int32)
+    pos = np.full(N, -1, np.int32)
+    pos[act] = np.arange(act.size)
+    vn = rs.standard_normal((act.size, C)).astype(np.float32)
+    ds = np.float32(-0.025)
+    for upd in (False, True):
+        tx, tv, ts = dev(x), dev(vh), dev(sc)
+        H.hsa_euler(tx, tv, ts, dev(vn), dev(pos, torch.int32), float(ds), upd)
+        rx, rv, rsc = O.euler_update(x, vh, sc, vn, act, ds, update_score=upd)
+        np.testing.assert_allclose(host(tx), rx, rtol=1e-6, atol=1e-6)
+        np.testing.assert_array_equal(host(tv), rv)
+        np.testing.assert_allclose(host(ts), rsc, rtol=2e-6, atol=0)
+        skipped = np.setdiff1d(np.arange(N), act)
+        np.testing.assert_array_equal(host(tv)[skipped], vh[skipped])
+        np.testing.assert_array_equal(host(ts)[skipped], sc[skipped])
+
+
+def test_euler_hand_values():
+    import json, os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "euler_hand.json")))
+    C = g["C"]
+    x = np.repeat(np.array(g["x"], np.float32)[:, None], C, 1)
+    vh = np.repeat(np.array(g["v_hat"], np.float32)[:, None], C, 1)
+    vn = np.repeat(np.array(g["v_new"], np.float32)[:, None], C, 1)
+    pos = np.full(3, -1, np.int32)
+    pos[g["active"]] = np.arange(len(g["active"]))
+    tx, tv, ts = dev(x), dev(vh), dev(np.array(g["score"], np.float32))
+    H.hsa_euler(tx, tv, ts, dev(vn), dev(pos, torch.int32), g["dsigma"], True)
+    np.testing.assert_array_equal(host(tx)[:, 0], g["expect_x"])
+    np.testing.assert_array_equal(host(tv)[:, 0], g["expect_v_hat"])
+    np.testing.assert_allclose(host(ts), g["expect_score"], rtol=1e-6)
+
+
+# ---------------------------------------------------------------- row ops
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_layernorm_embed_unembed(dtype):
+    rs = np.random.default_rng(3)
+    rows, D, C, N = 301, 1536, 16, 1000
+    h = (rs.standard_normal((rows, D)) * 2 + 0.5).astype(np.float32)
+    out = torch.empty(rows, D, dtype=dtype, device=DEV)
+    H.hsa_layernorm(dev(h), out)
+    ref = O.layer_norm(h)
+    tol = 1e-5 if dtype == torch.float32 else 4e-3
+    assert rel_l2(host(out), ref) < tol
+    # embed (gather of active latents)
+    x = rs.standard_normal((N, C)).astype(np.float32)
+    w_in = rs.standard_normal((D, C)).astype(np.float32) / 4
+    if dtype == torch.bfloat16:
+        w_in = bf(w_in)
+    idx = np.sort(rs.choice(N, rows, replace=False)).astype(np.int32)
+    th = torch.empty(rows, D, device=DEV)
+    H.hsa_embed(dev(x), dev(idx, torch.int32), rows, dev(w_in, dtype), th)
+    assert rel_l2(host(th), x[idx].astype(np.float64) @ w_in.T.astype(np.float64)) < 1e-6
+    # unembed
+    w_out = rs.standard_normal((C, D)).astype(np.float32) / 40
+    if dtype == torch.bfloat16:
+        w_out = bf(w_out)
+    vn = torch.empty(rows, C, device=DEV)
+    H.hsa_unembed(dev(h), dev(w_out, dtype), vn, rows)
+    assert rel_l2(host(vn), O.layer_norm(h) @ w_out.T.astype(np.float64)) < 1e-5
+
+
+# ---------------------------------------------------------------- GEMMs
+
+@pytest.mark.parametrize("M,N,K", [(1, 128, 64), (100, 384, 192), (300, 256, 128), (257, 200, 64),
+                                   (1000, 1536, 1536)])
+def test_linear_bf16(M, N, K):
+    say(f"linear bf16 M={M} N={N} K={K}")
+    rs = np.random.default_rng(M * 7 + N + K)
+    a = bf(rs.standard_normal((M, K)))
+    w = bf(rs.standard_normal((N, K)) / np.sqrt(K))
+    ref = a.astype(np.float64) @ w.T.astype(np.float64)
+    out = torch.empty(M, N, dtype=torch.bfloat16, device=DEV)
+    H.hsa_linear(dev(a, torch.bfloat16), dev(w, torch.bfloat16), out, act=0)
+    assert rel_l2(host(out), ref) < 5e-3
+    H.hsa_linear(dev(a, torch.bfloat16), dev(w, torch.bfloat16), out, act=1)
+    assert rel_l2(host(out), O.gelu_tanh(ref)) < 5e-3
+    h0 = rs.standard_normal((M, N)).astype(np.float32)
+    th = dev(h0)
+    H.hsa_linear_residual(dev(a, torch.bfloat16), dev(w, torch.bfloat16), th)
+    assert rel_l2(host(th), h0 + ref) < 1e-5
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 64, 4), (77, 384, 128), (256, 512, 512), (130, 100, 36)])
+def test_linear_f32(M, N, K):
+    rs = np.random.default_rng(M + N + K)
+    a = rs.standard_normal((M, K)).astype(np.float32)
+    w = (rs.standard_normal((N, K)) / np.sqrt(K)).astype(np.float32)
+    ref = a.astype(np.float64) @ w.T.astype(np.float64)
+    out = torch.empty(M, N, device=DEV)
+    H.hsa_linear(dev(a), dev(w), out, act=0)
+    assert rel_l2(host(out), ref) < 1e-6
+    H.hsa_linear(dev(a), dev(w), out, act=1)
+    assert rel_l2(host(out), O.gelu_tanh(ref)) < 1e-5
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_qkv_scatter_positions(dtype):
+    rs = np.random.default_rng(21)
+    N, D, nA = 700, 256, 233
+    a = rs.standard_normal((nA, D)).astype(np.float32)
+    w = (rs.standard_normal((3 * D, D)) / 16).astype(np.float32)
+    if dtype == torch.bfloat16:
+        a, w = bf(a), bf(w)
+    idx = np.sort(rs.choice(N, nA, replace=False)).astype(np.int32)
+    sentinel = -1024.0  # exactly representable in bfloat16 and float32
+    kc = torch.full((N, D), sentinel, dtype=dtype, device=DEV)
+    vc = torch.full((N, D), sentinel, dtype=dtype, device=DEV)
+    q = torch.empty(nA, D, dtype=dtype, device=DEV)
+    H.hsa_qkv_scatter(dev(a, dtype), dev(idx, torch.int32), nA, dev(w, dtype), q, kc, vc)
+    ref = a.astype(np.float64) @ w.T.astype(np.float64)
+    k_h, v_h = host(kc), host(vc)
+    touched = np.flatnonzero(np.any(k_h != sentinel, axis=1))
+    np.testing.assert_array_equal(touched, idx)           # positions: bit-exact
+    np.testing.assert_array_equal(np.flatnonzero(np.any(v_h != sentinel, axis=1)), idx)
+    assert np.all(k_h[np.setdiff1d(np.arange(N), idx)] == sentinel)
+    tol = 5e-3 if dtype == torch.bfloat16 else 1e-6
+    assert rel_l2(host(q), ref[:, :D]) < tol
+    assert rel_l2(k_h[idx], ref[:, D:2 * D]) < tol
+    assert rel_l2(v_h[idx], ref[:, 2 * D:]) < tol
+
+
+# ---------------------------------------------------------------- attention
+
+def _attn_case(nA, nkv, Hh, Dh, dtype, tol, seed=0):
+    rs = np.random.default_rng(seed + nA * 3 + nkv)
+    q = rs.standard_normal((nA, Hh * Dh)).astype(np.float32)
+    k = rs.standard_normal((nkv, Hh * Dh)).astype(np.float32)
+    v = rs.standard_normal((nkv, Hh * Dh)).astype(np.float32)
+    if dtype == torch.bfloat16:
+        q, k, v = bf(q), bf(k), bf(v)
+    o = torch.empty(nA, Hh * Dh, dtype=dtype, device=DEV)
+    H.hsa_attn_active(dev(q, dtype), dev(k, dtype), dev(v, dtype), o, Hh, Dh)
+    ref = O.attention(q, k, v, Hh, Dh)
+    err = rel_l2(host(o), ref)
+    assert err < tol, err
+    return err
+
+
+@pytest.mark.parametrize("nA,nkv", [(1, 1), (37, 63), (128, 64), (129, 65), (300, 1000), (64, 4097),
+                                    (2, 20000), (700, 5000)])
+def test_attention_bf16_d128(nA, nkv):
+    say(f"attention bf16 nA={nA} nkv={nkv}")
+    err = _attn_case(nA, nkv, 2, 128, torch.bfloat16, TOL_BF16)
+    assert err < 1e-2
+
+
+@pytest.mark.parametrize("nA,nkv,Dh", [(1, 1, 64), (77, 256, 64), (256, 256, 64), (50, 300, 128)])
+def test_attention_f32(nA, nkv, Dh):
+    _attn_case(nA, nkv, 2, Dh, torch.float32, 1e-5)
+
+
+def test_attention_bf16_d64_plain():
+    _attn_case(99, 500, 2, 64, torch.bfloat16, TOL_BF16)
+
+
+def test_attention_closed_forms_bf16():
+    # q = 0 -> mean of V rows; all V rows equal -> that row
+    nkv, Hh, Dh = 3000, 2, 128
+    rs = np.random.default_rng(9)
+    k = bf(rs.standard_normal((nkv, Hh * Dh)))
+    v = bf(rs.standard_normal((nkv, Hh * Dh)))
+    o = torch.empty(5, Hh * Dh, dtype=torch.bfloat16, device=DEV)
+    H.hsa_attn_active(dev(np.zeros((5, Hh * Dh)), torch.bfloat16), dev(k, torch.bfloat16),
+                      dev(v, torch.bfloat16), o, Hh, Dh)
+    assert rel_l2(host(o), np.broadcast_to(v.astype(np.float64).mean(0), (5, Hh * Dh))) < 2e-2
+    c = bf(rs.standard_normal(Hh * Dh))
+    H.hsa_attn_active(dev(bf(rs.standard_normal((5, Hh * Dh))), torch.bfloat16), dev(k, torch.bfloat16),
+                      dev(np.tile(c, (nkv, 1)), torch.bfloat16), o, Hh, Dh)
+    np.testing.assert_allclose(host(o), np.broadcast_to(c, (5, Hh * Dh)), rtol=8e-3, atol=1e-6)
+
+
+@pytest.mark.parametrize("frac", [0.25, 0.0625, 1.0])
+def test_attention_full_size_sampled_rows(frac):
+    """Wan-1.3B-shaped layer: N = 32760 cached rows, 12 heads x 128, the launch
+    configuration of the timed path; 64 sampled query rows against the oracle."""
+    c = synth.CONFIGS[2]
+    nA = synth.n_active_for_fraction(c.N, frac)
+    say(f"attention full-size nA={nA}")
+    kc, vc = synth.kv_cache(c)
+    rs = np.random.default_rng(77)
+    q = bf(rs.standard_normal((nA, c.D)))
+    o = torch.empty(nA, c.D, dtype=torch.bfloat16, device=DEV)
+    H.hsa_attn_active(dev(q, torch.bfloat16), dev(kc, torch.bfloat16), dev(vc, torch.bfloat16), o,
+                      c.H, c.Dh)
+    rows = np.sort(rs.choice(nA, 64, replace=False))
+    ref = O.attention(q[rows], kc, vc, c.H, c.Dh)
+    assert rel_l2(host(o)[rows], ref) < TOL_BF16

@@ -1,0 +1,275 @@
+"""GPU parity of whole blocks and whole HSA iterations against the CPU oracle,
+through the C ABI (hsa_block_forward, hsa_step)."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import hsa_oracle as O
+from tests.gpu_common import DEV, TOL_BF16, TOL_F32, dev, host, rel_l2, say
+
+pytestmark = pytest.mark.gpu
+
+H = None
+
+
+@pytest.fixture(scope="module", autouse=True)
+def lib():
+    global H
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from token_sparse_attention_compact_amd import hsa
+    hsa.load()
+    H = hsa
+    yield hsa
+
+
+def tdt(c):
+    return torch.bfloat16 if c.dtype == "bf16" else torch.float32
+
+
+def oracle_model(c):
+    dims = O.Dims(N=c.N, C=c.C, D=c.D, H=c.H, Dh=c.Dh, F=c.F, L=c.L, bf16=(c.dtype == "bf16"),
+                  n_text=c.n_text)
+    text = synth.text_inputs(c) if c.n_text else None
+    return O.make_model(dims, synth.io_weights(c), [synth.block_weights(c, l) for l in range(c.L)], text)
+
+
+def device_model(c, om, k_cache=None, v_cache=None):
+    """Device copy of the same seeded weights; caches zero or given [L][N][D]."""
+    dt = tdt(c)
+    dims = H.make_dims(c.N, c.C, c.D, c.H, c.Dh, c.F, c.L, c.n_text, dt)
+    io = synth.io_weights(c)
+    blocks = []
+    for l in range(c.L):
+        w = synth.block_weights(c, l)
+        b = {k: dev(v, dt) for k, v in w.items() if k in ("w_qkv", "w_o", "w_1", "w_2", "w_qx", "w_ox")}
+        b["k_cache"] = (torch.zeros(c.N, c.D, dtype=dt, device=DEV) if k_cache is None
+                        else dev(k_cache[l], dt))
+        b["v_cache"] = (torch.zeros(c.N, c.D, dtype=dt, device=DEV) if v_cache is None
+                        else dev(v_cache[l], dt))
+        if c.n_text:
+            # text K/V: the oracle's once-per-run projection is recomputed here with the library
+            tx = synth.text_inputs(c)
+            E = torch.empty(c.n_text, c.D, dtype=dt, device=DEV)
+            H.hsa_linear(dev(tx["text"], dt), dev(tx["w_t"], dt), E)
+            b["k_text"] = torch.empty(c.n_text, c.D, dtype=dt, device=DEV)
+            b["v_text"] = torch.empty(c.n_text, c.D, dtype=dt, device=DEV)
+            H.hsa_linear(E, dev(w["w_kx"], dt), b["k_text"])
+            H.hsa_linear(E, dev(w["w_vx"], dt), b["v_text"])
+        blocks.append(b)
+    return H.DeviceModel(dims, dev(io["w_in"], dt), dev(io["w_out"], dt), blocks)
+
+
+def small_bf16(**kw):
+    base = dict(grid=(2, 20, 16), C=16, D=256, H=2, Dh=128, F=512, L=2, dtype="bf16", T=40,
+                budgets=(40, 20, 10), shares=(0.25, 0.25, 0.5), regroup=(10, 20, 30))
+    base.update(kw)
+    return synth.CONFIGS[3].with_(**base)
+
+
+# ---------------------------------------------------------------- one block
+
+@pytest.mark.parametrize("n_text", [0, 16])
+def test_block_forward_small_bf16(n_text):
+    c = small_bf16(L=1, n_text=n_text, text_dim=64 if n_text else 0)
+    say(f"block_forward small bf16 n_text={n_text}")
+    om = oracle_model(c)
+    kc, vc = synth.kv_cache(c)
+    rs = np.random.default_rng(1)
+    idx = np.sort(rs.choice(c.N, 211, replace=False)).astype(np.int32)
+    h = rs.standard_normal((idx.size, c.D)).astype(np.float32)
+    m = device_model(c, om, kc[None], vc[None])
+    dims = m.dims
+    ws = torch.empty(H.hsa_workspace_size(dims), dtype=torch.uint8, device=DEV)
+    th = dev(h)
+    H.hsa_block_forward(m, 0, th, dev(idx, torch.int32), idx.size, ws)
+    kref, vref = kc.astype(np.float64), vc.astype(np.float64)
+    ref = O.block_forward(om, 0, h, idx, kref, vref)
+    assert rel_l2(host(th), ref) < TOL_BF16
+    assert rel_l2(host(th), ref) < 5e-3
+    k_gpu = host(m.blocks[0]["k_cache"])
+    skipped = np.setdiff1d(np.arange(c.N), idx)
+    np.testing.assert_array_equal(k_gpu[skipped], kc[skipped])
+    assert rel_l2(k_gpu[idx], kref[idx]) < 5e-3
+    assert rel_l2(host(m.blocks[0]["v_cache"])[idx], vref[idx]) < 5e-3
+
+
+@pytest.mark.parametrize("frac", [0.25])
+def test_block_forward_full_size_sampled_rows(frac):
+    """Wan-1.3B-shaped block (D 1536, 12x128 heads, F 8960) over N = 32760 cached
+    rows with 25% active: every active row's K/V goes through the oracle, the
+    block output is checked on 48 sampled active rows."""
+    c = synth.CONFIGS[2]
+    nA = synth.n_active_for_fraction(c.N, frac)
+    say(f"block_forward full-size nA={nA}")
+    om = oracle_model(c)
+    kc, vc = synth.kv_cache(c)
+    idx = synth.active_random(c, nA)
+    h = synth.hidden_states(c, nA)
+    m = device_model(c, om, kc[None], vc[None])
+    ws = torch.empty(H.hsa_workspace_size(m.dims), dtype=torch.uint8, device=DEV)
+    th = dev(h)
+    H.hsa_block_forward(m, 0, th, dev(idx, torch.int32), nA, ws)
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(5).choice(nA, 48, replace=False))
+    kref, vref = kc.astype(np.float64), vc.astype(np.float64)
+    ref = O.block_forward(om, 0, h, idx, kref, vref, rows=rows)
+    assert rel_l2(host(th)[rows], ref) < TOL_BF16
+    k_gpu = host(m.blocks[0]["k_cache"])
+    skipped = np.setdiff1d(np.arange(c.N), idx)
+    np.testing.assert_array_equal(k_gpu[skipped], kc[skipped])
+    assert rel_l2(k_gpu[idx], kref[idx]) < TOL_BF16
+
+
+# ---------------------------------------------------------------- whole iterations
+
+def run_gpu(c, m, sched, state, iters, sigma, field=None):
+    for i in iters:
+        vf = None if field is None else dev(field(i))
+        H.hsa_step(m, sched, state, i, float(sigma[i]), float(sigma[i + 1]), i in set(c.regroup), vf)
+    torch.cuda.synchronize()
+
+
+def select_margin(score, counts):
+    """Smallest relative gap between the scores on either side of a group boundary."""
+    s = np.sort(np.asarray(score, np.float64))[::-1]
+    gaps = []
+    b = 0
+    for n in counts[:-1]:
+        b += n
+        if 0 < b < s.size:
+            hi, lo = s[b - 1], s[b]
+            gaps.append(abs(hi - lo) / max(abs(hi), 1e-30))
+    return min(gaps) if gaps else np.inf
+
+
+def test_step_cfg1_full_run_f32():
+    """DiT-lite float32: 8 iterations, budgets {8,4}, regrouping from i = 3 on."""
+    c = synth.CONFIGS[1]
+    say("hsa_step cfg1 fp32 full run")
+    om = oracle_model(c)
+    m = device_model(c, om)
+    sched = H.make_schedule(c.T, c.budgets, c.counts())
+    osched = O.Schedule(c.T, list(c.budgets), c.counts(), regroup=c.regroup)
+    sigma = synth.sigma_schedule(c.T)
+    x0, g0 = synth.x0(c), synth.group0(c)
+    st = H.DeviceState(m.dims, dev(x0), dev(g0, torch.uint8))
+    ost = O.init_state(om.dims, x0, g0)
+    for i in range(c.T):
+        if i in c.regroup:
+            # Both sides rank their own float32 scores: the decision is the same when the gap at
+            # every group boundary exceeds the GPU/oracle score deviation by a wide margin.
+            fin = np.isfinite(ost.score)
+            dev_rel = np.max(np.abs(host(st.score)[fin] - ost.score[fin]) / np.abs(ost.score[fin]))
+            assert select_margin(ost.score, c.counts()) > 10 * dev_rel
+        run_gpu(c, m, sched, st, [i], sigma)
+        O.sample(om, osched, ost, sigma, iters=[i])
+        np.testing.assert_array_equal(st.group.cpu().numpy(), ost.group)
+        assert rel_l2(host(st.x), ost.x) < TOL_F32
+        assert rel_l2(host(st.v_hat), ost.v_hat) < TOL_F32
+        fin = np.isfinite(ost.score)
+        np.testing.assert_array_equal(np.isfinite(host(st.score)), fin)
+        if fin.any():
+            assert rel_l2(host(st.score)[fin], ost.score[fin]) < TOL_F32
+        assert rel_l2(host(m.blocks[0]["k_cache"]), ost.k_cache[0]) < TOL_F32
+
+
+def test_step_full_budget_is_dense_euler_f32():
+    c = synth.CONFIGS[1].with_(budgets=(8, 8))
+    om = oracle_model(c)
+    m = device_model(c, om)
+    sched = H.make_schedule(c.T, c.budgets, c.counts())
+    sigma = synth.sigma_schedule(c.T)
+    st = H.DeviceState(m.dims, dev(synth.x0(c)), dev(synth.group0(c), torch.uint8))
+    run_gpu(c, m, sched, st, range(c.T), sigma)
+    assert rel_l2(host(st.x), O.dense_euler_sample(om, synth.x0(c), sigma, c.T)) < TOL_F32
+
+
+def test_step_constant_velocity_closed_form():
+    c = synth.CONFIGS[1]
+    om = oracle_model(c)
+    m = device_model(c, om)
+    sched = H.make_schedule(c.T, c.budgets, c.counts())
+    sigma = synth.sigma_schedule(c.T)
+    v = np.random.default_rng(4).standard_normal((c.N, c.C)).astype(np.float32)
+    st = H.DeviceState(m.dims, dev(synth.x0(c)), dev(synth.group0(c), torch.uint8))
+    run_gpu(c, m, sched, st, range(c.T), sigma, field=lambda i: v)
+    expect = synth.x0(c).astype(np.float64) + (float(sigma[-1]) - float(sigma[0])) * v
+    np.testing.assert_allclose(host(st.x), expect, rtol=0, atol=1e-5)
+
+
+@pytest.mark.parametrize("i,regroup", [(10, True), (11, False), (12, False)])
+def test_step_mid_run_bf16(i, regroup):
+    """One iteration from a synthetic mid-run state (caches, v_hat, scores, groups)."""
+    c = small_bf16()
+    say(f"hsa_step mid-run bf16 i={i}")
+    om = oracle_model(c)
+    s0 = synth.mid_run_state(c)
+    m = device_model(c, om, s0["k_cache"], s0["v_cache"])
+    sched = H.make_schedule(c.T, c.budgets, c.counts())
+    sigma = synth.sigma_schedule(c.T)
+    st = H.DeviceState(m.dims, dev(s0["x"]), dev(s0["group"], torch.uint8), dev(s0["v_hat"]),
+                       dev(s0["score"]))
+    H.hsa_step(m, sched, st, i, float(sigma[i]), float(sigma[i + 1]), regroup)
+    torch.cuda.synchronize()
+    ost = O.State(s0["x"].astype(np.float64), s0["v_hat"].astype(np.float64),
+                  s0["score"].astype(np.float64), s0["group"].copy(),
+                  s0["k_cache"].astype(np.float64), s0["v_cache"].astype(np.float64))
+    osched = O.Schedule(c.T, list(c.budgets), c.counts())
+    out = O.hsa_iteration(om, osched, ost, i, sigma[i], sigma[i + 1], regroup)
+    np.testing.assert_array_equal(st.group.cpu().numpy(), ost.group)
+    nA = out["active_idx"].size
+    np.testing.assert_array_equal(st.active_idx[:nA].cpu().numpy(), out["active_idx"])
+    np.testing.assert_array_equal(st.pos.cpu().numpy(), out["pos"])
+    assert rel_l2(host(st.x), ost.x) < 1e-3
+    assert rel_l2(host(st.v_hat), ost.v_hat) < TOL_BF16
+    assert rel_l2(host(st.score), ost.score) < TOL_BF16
+    skipped = np.setdiff1d(np.arange(c.N), out["active_idx"])
+    for l in range(c.L):
+        kg = host(m.blocks[l]["k_cache"])
+        np.testing.assert_array_equal(kg[skipped], s0["k_cache"][l][skipped])
+        assert rel_l2(kg[out["active_idx"]], ost.k_cache[l][out["active_idx"]]) < TOL_BF16
+    # skipped tokens advance with their cached velocity, bit-for-bit as an FMA
+    ds = np.float32(np.float32(sigma[i + 1]) - np.float32(sigma[i]))
+    xs = (s0["x"][skipped].astype(np.float64) + np.float64(ds) * s0["v_hat"][skipped]).astype(np.float32)
+    np.testing.assert_array_equal(host(st.x)[skipped].astype(np.float32), xs)
+
+
+def test_step_full_size_iteration_properties():
+    """Wan-1.3B shapes (N 32760, D 1536, F 8960), 2 blocks, 25%-active iteration
+    from a synthetic mid-run state: exact properties that hold at any size."""
+    c = synth.CONFIGS[3].with_(L=2)
+    say("hsa_step full-size properties")
+    i = 11
+    om = oracle_model(c)
+    s0 = synth.mid_run_state(c)
+    m = device_model(c, om, s0["k_cache"], s0["v_cache"])
+    sched = H.make_schedule(c.T, c.budgets, c.counts())
+    sigma = synth.sigma_schedule(c.T)
+    st = H.DeviceState(m.dims, dev(s0["x"]), dev(s0["group"], torch.uint8), dev(s0["v_hat"]),
+                       dev(s0["score"]))
+    H.hsa_step(m, sched, st, i, float(sigma[i]), float(sigma[i + 1]), False)
+    torch.cuda.synchronize()
+    idx, pos = O.active_set(s0["group"], c.budgets, c.T, i)
+    assert idx.size == 8190
+    np.testing.assert_array_equal(st.active_idx[:idx.size].cpu().numpy(), idx)
+    np.testing.assert_array_equal(st.pos.cpu().numpy(), pos)
+    skipped = np.setdiff1d(np.arange(c.N), idx)
+    np.testing.assert_array_equal(host(st.v_hat)[skipped], s0["v_hat"][skipped])
+    np.testing.assert_array_equal(host(st.score)[skipped], s0["score"][skipped])
+    ds = np.float32(np.float32(sigma[i + 1]) - np.float32(sigma[i]))
+    xs = (s0["x"][skipped].astype(np.float64) + np.float64(ds) * s0["v_hat"][skipped]).astype(np.float32)
+    np.testing.assert_array_equal(host(st.x)[skipped].astype(np.float32), xs)
+    # active rows: x advanced with their fresh velocity, v_hat replaced
+    xa = host(st.x)[idx]
+    np.testing.assert_allclose(xa, s0["x"][idx] + float(ds) * host(st.v_hat)[idx], rtol=1e-5, atol=1e-6)
+    for l in range(c.L):
+        kg = host(m.blocks[l]["k_cache"])
+        np.testing.assert_array_equal(kg[skipped], s0["k_cache"][l][skipped])
+    # layer-0 fresh K/V rows depend only on the row itself: sampled rows vs oracle
+    rows = np.sort(np.random.default_rng(3).choice(idx.size, 64, replace=False))
+    hx = O.embed(om, s0["x"], idx[rows])
+    a = om.store.act(O.layer_norm(hx))
+    kv = a @ om.blocks[0]["w_qkv"][c.D:].T
+    assert rel_l2(host(m.blocks[0]["k_cache"])[idx[rows]], om.store.act(kv[:, :c.D])) < TOL_BF16
+    assert rel_l2(host(m.blocks[0]["v_cache"])[idx[rows]], om.store.act(kv[:, c.D:])) < TOL_BF16

@@ -1,0 +1,189 @@
+// Row operations on the active rows: LayerNorm (pre-norm of every sub-layer),
+// gather + embed of the active latents (the active rows enter the model,
+// section 2.2 item 1) and final LayerNorm + unembed to the velocity.
+// All three are bandwidth-bound; one 64-wide wavefront per row with float4
+// accesses, statistics in float32 from two passes over the row.
+#include "common.h"
+
+namespace hsa {
+namespace {
+
+constexpr int kRowsPerBlock = 4;  // 4 wavefronts of 64 lanes
+
+__device__ __forceinline__ void row_stats(const f32x4* hr, int nv, int lane, int D, float& mean,
+                                          float& rstd) {
+  float s = 0.f;
+  for (int i = lane; i < nv; i += kWave) {
+    const f32x4 v = hr[i];
+    s += (v[0] + v[1]) + (v[2] + v[3]);
+  }
+  mean = wave_sum(s) / (float)D;
+  float q = 0.f;
+  for (int i = lane; i < nv; i += kWave) {
+    const f32x4 v = hr[i];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float d = v[c] - mean;
+      q += d * d;
+    }
+  }
+  const float var = wave_sum(q) / (float)D;
+  rstd = 1.0f / sqrtf(var + kLnEps);
+}
+
+template <typename OutT>
+__device__ __forceinline__ void store4(OutT* p, f32x4 v);
+template <>
+__device__ __forceinline__ void store4<float>(float* p, f32x4 v) {
+  *reinterpret_cast<f32x4*>(p) = v;
+}
+template <>
+__device__ __forceinline__ void store4<bf16>(bf16* p, f32x4 v) {
+  bf16x4 b = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+  *reinterpret_cast<bf16x4*>(p) = b;
+}
+
+template <typename OutT>
+__global__ __launch_bounds__(256) void layernorm_kernel(const float* __restrict__ h,
+                                                        OutT* __restrict__ out, int32_t rows,
+                                                        int32_t D) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int32_t row = blockIdx.x * kRowsPerBlock + threadIdx.x / kWave;
+  if (row >= rows) return;
+  const int nv = D / 4;
+  const f32x4* hr = reinterpret_cast<const f32x4*>(h + (size_t)row * D);
+  float mean, rstd;
+  row_stats(hr, nv, lane, D, mean, rstd);
+  OutT* orow = out + (size_t)row * D;
+  for (int i = lane; i < nv; i += kWave) {
+    f32x4 v = hr[i];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) v[c] = (v[c] - mean) * rstd;
+    store4<OutT>(orow + 4 * i, v);
+  }
+}
+
+// h[j][d] = sum_c x[idx[j]][c] * w_in[d][c]
+template <typename WT>
+__global__ __launch_bounds__(256) void embed_kernel(const float* __restrict__ x,
+                                                    const int32_t* __restrict__ idx,
+                                                    const WT* __restrict__ w_in,
+                                                    float* __restrict__ h, int32_t rows, int32_t C,
+                                                    int32_t D) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= (int64_t)rows * D) return;
+  const int32_t j = (int32_t)(t / D), d = (int32_t)(t % D);
+  const float* xr = x + (size_t)idx[j] * C;
+  const WT* wr = w_in + (size_t)d * C;
+  float acc = 0.f;
+  for (int c = 0; c < C; ++c) acc = __builtin_fmaf(xr[c], to_f32(wr[c]), acc);
+  h[t] = acc;
+}
+
+// v_new[j][c] = sum_d LN(h[j])[d] * w_out[c][d], C == CC known at compile time.
+template <typename WT, int CC>
+__global__ __launch_bounds__(256) void unembed_kernel(const float* __restrict__ h,
+                                                      const WT* __restrict__ w_out,
+                                                      float* __restrict__ v_new, int32_t rows,
+                                                      int32_t D) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int32_t row = blockIdx.x * kRowsPerBlock + threadIdx.x / kWave;
+  if (row >= rows) return;
+  const int nv = D / 4;
+  const f32x4* hr = reinterpret_cast<const f32x4*>(h + (size_t)row * D);
+  float mean, rstd;
+  row_stats(hr, nv, lane, D, mean, rstd);
+  float acc[CC];
+#pragma unroll
+  for (int c = 0; c < CC; ++c) acc[c] = 0.f;
+  for (int i = lane; i < nv; i += kWave) {
+    f32x4 v = hr[i];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = (v[e] - mean) * rstd;
+#pragma unroll
+    for (int c = 0; c < CC; ++c) {
+      const WT* w = w_out + (size_t)c * D + 4 * i;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[c] = __builtin_fmaf(v[e], to_f32(w[e]), acc[c]);
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < CC; ++c) acc[c] = wave_sum(acc[c]);
+  if (lane < CC) {
+    float mine = 0.f;
+#pragma unroll
+    for (int c = 0; c < CC; ++c) mine = (lane == c) ? acc[c] : mine;
+    v_new[(size_t)row * CC + lane] = mine;
+  }
+}
+
+// Any C: one wave reduction per output channel.
+template <typename WT>
+__global__ __launch_bounds__(256) void unembed_kernel_any(const float* __restrict__ h,
+                                                          const WT* __restrict__ w_out,
+                                                          float* __restrict__ v_new, int32_t rows,
+                                                          int32_t D, int32_t C) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int32_t row = blockIdx.x * kRowsPerBlock + threadIdx.x / kWave;
+  if (row >= rows) return;
+  const int nv = D / 4;
+  const f32x4* hr = reinterpret_cast<const f32x4*>(h + (size_t)row * D);
+  float mean, rstd;
+  row_stats(hr, nv, lane, D, mean, rstd);
+  for (int c = 0; c < C; ++c) {
+    float acc = 0.f;
+    for (int i = lane; i < nv; i += kWave) {
+      const f32x4 v = hr[i];
+      const WT* w = w_out + (size_t)c * D + 4 * i;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc = __builtin_fmaf((v[e] - mean) * rstd, to_f32(w[e]), acc);
+    }
+    acc = wave_sum(acc);
+    if (lane == 0) v_new[(size_t)row * C + c] = acc;
+  }
+}
+
+}  // namespace
+
+hsa_status launch_layernorm(const float* h, void* out, int32_t rows, int32_t D, hsa_dtype dt,
+                            hipStream_t s) {
+  if (rows == 0) return HSA_OK;
+  const int blocks = cdiv(rows, kRowsPerBlock);
+  if (dt == HSA_BF16)
+    layernorm_kernel<bf16><<<blocks, 256, 0, s>>>(h, (bf16*)out, rows, D);
+  else
+    layernorm_kernel<float><<<blocks, 256, 0, s>>>(h, (float*)out, rows, D);
+  return launch_status();
+}
+
+hsa_status launch_embed(const float* x, const int32_t* idx, const void* w_in, float* h,
+                        int32_t rows, int32_t C, int32_t D, hsa_dtype dt, hipStream_t s) {
+  if (rows == 0) return HSA_OK;
+  const int64_t total = (int64_t)rows * D;
+  const unsigned blocks = (unsigned)((total + 255) / 256);
+  if (dt == HSA_BF16)
+    embed_kernel<bf16><<<blocks, 256, 0, s>>>(x, idx, (const bf16*)w_in, h, rows, C, D);
+  else
+    embed_kernel<float><<<blocks, 256, 0, s>>>(x, idx, (const float*)w_in, h, rows, C, D);
+  return launch_status();
+}
+
+hsa_status launch_unembed(const float* h, const void* w_out, float* v_new, int32_t rows,
+                          int32_t D, int32_t C, hsa_dtype dt, hipStream_t s) {
+  if (rows == 0) return HSA_OK;
+  const int blocks = cdiv(rows, kRowsPerBlock);
+  if (C == 16) {
+    if (dt == HSA_BF16)
+      unembed_kernel<bf16, 16><<<blocks, 256, 0, s>>>(h, (const bf16*)w_out, v_new, rows, D);
+    else
+      unembed_kernel<float, 16><<<blocks, 256, 0, s>>>(h, (const float*)w_out, v_new, rows, D);
+  } else {
+    if (dt == HSA_BF16)
+      unembed_kernel_any<bf16><<<blocks, 256, 0, s>>>(h, (const bf16*)w_out, v_new, rows, D, C);
+    else
+      unembed_kernel_any<float><<<blocks, 256, 0, s>>>(h, (const float*)w_out, v_new, rows, D, C);
+  }
+  return launch_status();
+}
+
+}  // namespace hsa

@@ -1,0 +1,333 @@
+"""Python binding of libhsa (ctypes).  Argument marshalling only: every step of
+the HSA iteration runs in the library's HIP kernels.  torch is used for device
+memory and streams.
+
+Function names mirror include/hsa.h.  Each wrapper takes torch tensors, checks
+dtype/device/contiguity, passes raw pointers and the current HIP stream, and
+raises HsaError on a non-zero status.  If libhsa.so is missing the import
+fails loudly: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes as ct
+import os
+from typing import List, Optional, Sequence
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libhsa.so")
+
+HSA_F32, HSA_BF16 = 0, 1
+MAX_GROUPS = 8
+EXPORTED = [
+    "hsa_status_str", "hsa_abi_version", "hsa_workspace_size", "hsa_attn_workspace_size",
+    "hsa_select_workspace_size", "hsa_n_active", "hsa_active_set", "hsa_select", "hsa_euler",
+    "hsa_attn_active", "hsa_layernorm", "hsa_embed", "hsa_unembed", "hsa_linear",
+    "hsa_linear_residual", "hsa_qkv_scatter", "hsa_block_forward", "hsa_step",
+]
+
+
+class HsaError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed: status {status} ({msg})")
+        self.status = status
+
+
+# ---------------------------------------------------------------- C structs
+class Dims(ct.Structure):
+    _fields_ = [("N", ct.c_int32), ("C", ct.c_int32), ("D", ct.c_int32), ("H", ct.c_int32),
+                ("Dh", ct.c_int32), ("F", ct.c_int32), ("L", ct.c_int32), ("n_text", ct.c_int32),
+                ("dtype", ct.c_int)]
+
+
+class Schedule(ct.Structure):
+    _fields_ = [("T", ct.c_int32), ("K", ct.c_int32), ("m", ct.c_int32),
+                ("budget", ct.c_int32 * MAX_GROUPS), ("count", ct.c_int32 * MAX_GROUPS)]
+
+
+class Block(ct.Structure):
+    _fields_ = [(n, ct.c_void_p) for n in ("w_qkv", "w_o", "w_1", "w_2", "w_qx", "w_ox",
+                                           "k_cache", "v_cache", "k_text", "v_text")]
+
+
+class Model(ct.Structure):
+    _fields_ = [("dims", Dims), ("w_in", ct.c_void_p), ("w_out", ct.c_void_p),
+                ("blocks", ct.POINTER(Block))]
+
+
+class State(ct.Structure):
+    _fields_ = [("x", ct.c_void_p), ("v_hat", ct.c_void_p), ("score", ct.c_void_p),
+                ("group", ct.c_void_p), ("active_idx", ct.c_void_p), ("pos", ct.c_void_p),
+                ("workspace", ct.c_void_p), ("workspace_bytes", ct.c_size_t)]
+
+
+# ---------------------------------------------------------------- loading
+_lib = None
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load() -> ct.CDLL:
+    """Load libhsa.so (built in-tree by token_sparse_attention_compact_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"libhsa.so not found at {_LIB_PATH}: build it with "
+                          f"`python -m token_sparse_attention_compact_amd.build`")
+    L = ct.CDLL(_LIB_PATH)
+    P, I, F, S = ct.c_void_p, ct.c_int32, ct.c_float, ct.c_size_t
+    PS = ct.POINTER(ct.c_size_t)
+    PI = ct.POINTER(ct.c_int32)
+    sig = {
+        "hsa_status_str": ([I], ct.c_char_p),
+        "hsa_abi_version": ([], I),
+        "hsa_workspace_size": ([ct.POINTER(Dims), PS], I),
+        "hsa_attn_workspace_size": ([I, I, I, I, PS], I),
+        "hsa_select_workspace_size": ([I, I, PS], I),
+        "hsa_n_active": ([ct.POINTER(Schedule), I, PI], I),
+        "hsa_active_set": ([P, I, ct.POINTER(Schedule), I, P, P, P, P], I),
+        "hsa_select": ([P, I, PI, I, P, P, S, P], I),
+        "hsa_euler": ([P, P, P, P, P, I, I, F, F, I, P], I),
+        "hsa_attn_active": ([P, P, P, P, I, I, I, I, F, ct.c_int, P, S, P], I),
+        "hsa_layernorm": ([P, P, I, I, ct.c_int, P], I),
+        "hsa_embed": ([P, P, P, P, I, I, I, ct.c_int, P], I),
+        "hsa_unembed": ([P, P, P, I, I, I, ct.c_int, P], I),
+        "hsa_linear": ([P, P, P, I, I, I, I, ct.c_int, P], I),
+        "hsa_linear_residual": ([P, P, P, I, I, I, ct.c_int, P], I),
+        "hsa_qkv_scatter": ([P, P, P, P, P, P, I, I, I, ct.c_int, P], I),
+        "hsa_block_forward": ([ct.POINTER(Model), I, P, P, I, P, S, P], I),
+        "hsa_step": ([ct.POINTER(Model), ct.POINTER(Schedule), ct.POINTER(State), I, F, F, I, P, P], I),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(L, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = L
+    return L
+
+
+def status_str(status: int) -> str:
+    return load().hsa_status_str(status).decode()
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise HsaError(fn, status, status_str(status))
+
+
+def _stream(stream=None) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return t.data_ptr()
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return HSA_BF16
+    if t.dtype == torch.float32:
+        return HSA_F32
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def _need(t: torch.Tensor, dtype, name: str):
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: expected {dtype}, got {t.dtype}")
+
+
+# ---------------------------------------------------------------- structs from python
+def make_dims(N, C, D, H, Dh, F, L, n_text=0, dtype=torch.bfloat16) -> Dims:
+    return Dims(N, C, D, H, Dh, F, L, n_text, HSA_BF16 if dtype == torch.bfloat16 else HSA_F32)
+
+
+def make_schedule(T: int, budgets: Sequence[int], counts: Sequence[int], m: int = 0) -> Schedule:
+    if len(budgets) != len(counts) or not 1 <= len(budgets) <= MAX_GROUPS:
+        raise ValueError("budgets/counts: 1..8 groups of equal length")
+    s = Schedule()
+    s.T, s.K, s.m = T, len(budgets), m
+    for k, (b, c) in enumerate(zip(budgets, counts)):
+        s.budget[k] = b
+        s.count[k] = c
+    return s
+
+
+# ---------------------------------------------------------------- entry points
+def hsa_abi_version() -> int:
+    return load().hsa_abi_version()
+
+
+def hsa_workspace_size(dims: Dims) -> int:
+    n = ct.c_size_t()
+    _check("hsa_workspace_size", load().hsa_workspace_size(ct.byref(dims), ct.byref(n)))
+    return n.value
+
+
+def hsa_attn_workspace_size(n_active: int, n_kv: int, H: int, Dh: int) -> int:
+    n = ct.c_size_t()
+    _check("hsa_attn_workspace_size", load().hsa_attn_workspace_size(n_active, n_kv, H, Dh, ct.byref(n)))
+    return n.value
+
+
+def hsa_n_active(sched: Schedule, it: int) -> int:
+    n = ct.c_int32()
+    _check("hsa_n_active", load().hsa_n_active(ct.byref(sched), it, ct.byref(n)))
+    return n.value
+
+
+def hsa_active_set(group: torch.Tensor, sched: Schedule, it: int, active_idx: torch.Tensor,
+                   pos: torch.Tensor, n_active_dev: torch.Tensor, stream=None):
+    _need(group, torch.uint8, "group")
+    for t, n in ((active_idx, "active_idx"), (pos, "pos"), (n_active_dev, "n_active_dev")):
+        _need(t, torch.int32, n)
+    _check("hsa_active_set", load().hsa_active_set(_ptr(group), group.numel(), ct.byref(sched), it,
+                                                   _ptr(active_idx), _ptr(pos), _ptr(n_active_dev),
+                                                   _stream(stream)))
+
+
+def hsa_select(score: torch.Tensor, counts: Sequence[int], group_out: torch.Tensor, stream=None):
+    _need(score, torch.float32, "score")
+    _need(group_out, torch.uint8, "group_out")
+    arr = (ct.c_int32 * len(counts))(*counts)
+    _check("hsa_select", load().hsa_select(_ptr(score), score.numel(), arr, len(counts),
+                                           _ptr(group_out), None, 0, _stream(stream)))
+
+
+def hsa_euler(x, v_hat, score, v_new, pos, dsigma: float, update_score: bool, eps: float = 1e-6,
+              stream=None):
+    for t, n in ((x, "x"), (v_hat, "v_hat"), (score, "score")):
+        _need(t, torch.float32, n)
+    if v_new is not None:
+        _need(v_new, torch.float32, "v_new")
+    _need(pos, torch.int32, "pos")
+    N, C = x.shape
+    _check("hsa_euler", load().hsa_euler(_ptr(x), _ptr(v_hat), _ptr(score), _ptr(v_new), _ptr(pos),
+                                         N, C, dsigma, eps, int(update_score), _stream(stream)))
+
+
+def hsa_attn_active(q, k, v, o, H: int, Dh: int, scale: Optional[float] = None,
+                    ws: Optional[torch.Tensor] = None, stream=None):
+    dt = _dt(q)
+    for t in (k, v, o):
+        _need(t, q.dtype, "k/v/o")
+    nA, nkv = q.shape[0], k.shape[0]
+    if scale is None:
+        scale = Dh ** -0.5
+    need = hsa_attn_workspace_size(nA, nkv, H, Dh)
+    if need and (ws is None or ws.numel() * ws.element_size() < need):
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    _check("hsa_attn_active", load().hsa_attn_active(_ptr(q), _ptr(k), _ptr(v), _ptr(o), nA, nkv, H, Dh,
+                                                     scale, dt, _ptr(ws), wsb, _stream(stream)))
+
+
+def hsa_layernorm(h, out, stream=None):
+    _need(h, torch.float32, "h")
+    rows, D = h.shape
+    _check("hsa_layernorm", load().hsa_layernorm(_ptr(h), _ptr(out), rows, D, _dt(out), _stream(stream)))
+
+
+def hsa_embed(x, active_idx, n_active: int, w_in, h, stream=None):
+    _need(x, torch.float32, "x")
+    _need(h, torch.float32, "h")
+    _need(active_idx, torch.int32, "active_idx")
+    D, C = w_in.shape
+    _check("hsa_embed", load().hsa_embed(_ptr(x), _ptr(active_idx), _ptr(w_in), _ptr(h), n_active, C, D,
+                                         _dt(w_in), _stream(stream)))
+
+
+def hsa_unembed(h, w_out, v_new, n_active: int, stream=None):
+    _need(h, torch.float32, "h")
+    _need(v_new, torch.float32, "v_new")
+    C, D = w_out.shape
+    _check("hsa_unembed", load().hsa_unembed(_ptr(h), _ptr(w_out), _ptr(v_new), n_active, D, C,
+                                             _dt(w_out), _stream(stream)))
+
+
+def hsa_linear(a, w, out, act: int = 0, M: Optional[int] = None, stream=None):
+    M = a.shape[0] if M is None else M
+    Nout, K = w.shape
+    _check("hsa_linear", load().hsa_linear(_ptr(a), _ptr(w), _ptr(out), M, Nout, K, act, _dt(a),
+                                           _stream(stream)))
+
+
+def hsa_linear_residual(a, w, h, M: Optional[int] = None, stream=None):
+    _need(h, torch.float32, "h")
+    M = a.shape[0] if M is None else M
+    Nout, K = w.shape
+    _check("hsa_linear_residual", load().hsa_linear_residual(_ptr(a), _ptr(w), _ptr(h), M, Nout, K,
+                                                             _dt(a), _stream(stream)))
+
+
+def hsa_qkv_scatter(a, active_idx, n_active: int, w_qkv, q_out, k_cache, v_cache, stream=None):
+    _need(active_idx, torch.int32, "active_idx")
+    N, D = k_cache.shape
+    _check("hsa_qkv_scatter", load().hsa_qkv_scatter(_ptr(a), _ptr(active_idx), _ptr(w_qkv), _ptr(q_out),
+                                                     _ptr(k_cache), _ptr(v_cache), n_active, N, D,
+                                                     _dt(a), _stream(stream)))
+
+
+# ---------------------------------------------------------------- owning helpers
+class DeviceModel:
+    """Device weights + per-layer K/V caches, and the hsa_model struct over them.
+
+    Weight layouts are those of include/hsa.h (out-major [out][in]).  Tensors are
+    kept referenced here so the raw pointers in the struct stay valid."""
+
+    def __init__(self, dims: Dims, w_in: torch.Tensor, w_out: torch.Tensor, blocks: List[dict]):
+        self.dims = dims
+        self.w_in, self.w_out = w_in.contiguous(), w_out.contiguous()
+        self.blocks = [{k: (v.contiguous() if v is not None else None) for k, v in b.items()} for b in blocks]
+        arr = (Block * dims.L)()
+        for l, b in enumerate(self.blocks):
+            for name in ("w_qkv", "w_o", "w_1", "w_2", "w_qx", "w_ox", "k_cache", "v_cache",
+                         "k_text", "v_text"):
+                t = b.get(name)
+                setattr(arr[l], name, None if t is None else _ptr(t))
+        self._arr = arr
+        self.c = Model(dims, _ptr(self.w_in), _ptr(self.w_out), arr)
+
+
+class DeviceState:
+    """Sampler state buffers and the workspace, plus the hsa_state struct."""
+
+    def __init__(self, dims: Dims, x0: torch.Tensor, group0: torch.Tensor,
+                 v_hat: Optional[torch.Tensor] = None, score: Optional[torch.Tensor] = None):
+        dev = x0.device
+        N, C = dims.N, dims.C
+        self.x = x0.to(torch.float32).contiguous().clone()
+        self.v_hat = (torch.zeros(N, C, device=dev) if v_hat is None else v_hat.clone().contiguous())
+        self.score = (torch.full((N,), float("inf"), device=dev) if score is None
+                      else score.clone().contiguous())
+        self.group = group0.to(torch.uint8).contiguous().clone()
+        self.active_idx = torch.zeros(N, dtype=torch.int32, device=dev)
+        self.pos = torch.zeros(N, dtype=torch.int32, device=dev)
+        nbytes = hsa_workspace_size(dims)
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        self.c = State(_ptr(self.x), _ptr(self.v_hat), _ptr(self.score), _ptr(self.group),
+                       _ptr(self.active_idx), _ptr(self.pos), _ptr(self.workspace), nbytes)
+
+
+def hsa_block_forward(model: DeviceModel, layer: int, h, active_idx, n_active: int,
+                      ws: torch.Tensor, stream=None):
+    _need(h, torch.float32, "h")
+    _check("hsa_block_forward", load().hsa_block_forward(ct.byref(model.c), layer, _ptr(h), _ptr(active_idx),
+                                                         n_active, _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def hsa_step(model: DeviceModel, sched: Schedule, state: DeviceState, it: int, sigma_i: float,
+             sigma_next: float, regroup: bool, v_field: Optional[torch.Tensor] = None, stream=None):
+    _check("hsa_step", load().hsa_step(ct.byref(model.c), ct.byref(sched), ct.byref(state.c), it,
+                                       float(sigma_i), float(sigma_next), int(regroup), _ptr(v_field),
+                                       _stream(stream)))
