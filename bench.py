@@ -1,0 +1,207 @@
+"""Benchmark: one HSA global iteration on one MI355X.
+
+Workload: Wan-1.3B-shaped stack of 30 bf16 blocks (D 1536, 12 heads x 128,
+MLP 8960, C 16 latent channels) over N = 32760 tokens (21 x 30 x 52), three
+groups with budgets {40, 20, 10} and 25/25/50% shares.  A step is one call of
+hsa_step at an odd iteration (i = 11: only G_1 is active, |A_i| = 8190 = 25%)
+with regrouping switched on, so every stage of the hot path runs: select,
+active set, gather + embed, 30 x (LN, QKV + K/V scatter, active-query
+attention over all 32760 cached rows, out-projection, LN, GELU MLP), unembed,
+cached Euler + score.  Inputs (random-init weights, mid-run K/V caches and
+sampler state) are generated on the device before timing.
+
+Prints one JSON line.  `value` is HSA iterations per second.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+METRIC = "active-query attn TFLOP/s + HSA iterations/s at N=32760, 25% active (1 GPU)"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+ITER = 11
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--blocks", type=int, default=30, help="number of blocks (the workload uses 30)")
+    p.add_argument("--attn-reps", type=int, default=20)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-rows", type=int, default=2048)
+    return p.parse_args()
+
+
+def device_inputs(c, H, seed_base):
+    """Random-init weights N(0, 1/fan_in) and a mid-run state, generated on the device."""
+    dev = "cuda"
+    g = torch.Generator(device=dev)
+    dt = torch.bfloat16
+
+    def randn(shape, std, sub):
+        g.manual_seed(seed_base * 1000 + sub)
+        return (torch.randn(shape, generator=g, device=dev, dtype=torch.float32) * std).to(dt)
+
+    D, F, N, C = c.D, c.F, c.N, c.C
+    blocks = []
+    for l in range(c.L):
+        s = 100 * (l + 1)
+        blocks.append({
+            "w_qkv": randn((3 * D, D), D ** -0.5, s + 1),
+            "w_o": randn((D, D), D ** -0.5, s + 2),
+            "w_1": randn((F, D), D ** -0.5, s + 3),
+            "w_2": randn((D, F), F ** -0.5, s + 4),
+            "k_cache": randn((N, D), 1.0, s + 5),
+            "v_cache": randn((N, D), 1.0, s + 6),
+        })
+    dims = H.make_dims(N, C, D, c.H, c.Dh, F, c.L, 0, dt)
+    model = H.DeviceModel(dims, randn((D, C), C ** -0.5, 1), randn((C, D), D ** -0.5, 2), blocks)
+    g.manual_seed(seed_base * 1000 + 3)
+    x = torch.randn((N, C), generator=g, device=dev)
+    v_hat = torch.randn((N, C), generator=g, device=dev)
+    score = torch.rand((N,), generator=g, device=dev)
+    group = torch.from_numpy(synth.group0(c)).to(dev)
+    state = H.DeviceState(dims, x, group, v_hat, score)
+    return model, state
+
+
+def timed_steps(H, model, sched, state, sigma, steps, warmup):
+    for _ in range(warmup):
+        H.hsa_step(model, sched, state, ITER, float(sigma[ITER]), float(sigma[ITER + 1]), True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        H.hsa_step(model, sched, state, ITER, float(sigma[ITER]), float(sigma[ITER + 1]), True)
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0
+
+
+def time_attention(H, model, c, n_active, reps):
+    """Average duration of the attention kernel at the step's launch configuration,
+    with HIP events on the stream the kernel runs on.  Layers' caches rotate so
+    K/V come from HBM as in the stack."""
+    q = torch.randn((n_active, c.D), device="cuda").to(torch.bfloat16)
+    o = torch.empty_like(q)
+    ws = torch.empty(max(1, H.hsa_attn_workspace_size(n_active, c.N, c.H, c.Dh)), dtype=torch.uint8,
+                     device="cuda")
+    L = len(model.blocks)
+    for l in range(min(L, 3)):
+        b = model.blocks[l]
+        H.hsa_attn_active(q, b["k_cache"], b["v_cache"], o, c.H, c.Dh, ws=ws)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for r in range(reps):
+        b = model.blocks[r % L]
+        H.hsa_attn_active(q, b["k_cache"], b["v_cache"], o, c.H, c.Dh, ws=ws)
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / 1e3 / reps
+
+
+def cpu_baseline(c, rows: int):
+    """The oracle on a bounded sample of the same iteration: one block with `rows`
+    active tokens over all N cached rows (its cost is linear in the number of
+    active rows), scaled to 8190 rows x 30 blocks, plus the oracle's Euler +
+    select over all N tokens."""
+    from oracle import hsa_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    cs = c.with_(L=1)
+    dims = O.Dims(N=cs.N, C=cs.C, D=cs.D, H=cs.H, Dh=cs.Dh, F=cs.F, L=1, bf16=True)
+    om = O.make_model(dims, synth.io_weights(cs), [synth.block_weights(cs, 0)])
+    kc, vc = synth.kv_cache(cs)
+    kc, vc = kc.astype(np.float64), vc.astype(np.float64)
+    idx = synth.active_random(cs, rows)
+    h = synth.hidden_states(cs, rows)
+    t0 = time.perf_counter()
+    O.block_forward(om, 0, h, idx, kc, vc)
+    t_block = time.perf_counter() - t0
+    st = synth.mid_run_state(cs.with_(L=1))
+    t0 = time.perf_counter()
+    grp = O.select_groups(st["score"], cs.counts())
+    aidx, _ = O.active_set(grp, cs.budgets, cs.T, ITER)
+    O.euler_update(st["x"], st["v_hat"], st["score"], st["v_hat"][aidx], aidx, -0.025, True)
+    t_tail = time.perf_counter() - t0
+    n_active = O.n_active_closed_form(cs.counts(), cs.budgets, cs.T, ITER)
+    t_iter = t_block * (n_active / rows) * c.L + t_tail
+    return {"value": 1.0 / t_iter, "unit": "iter/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"1 block with {rows} of {n_active} active rows over N={cs.N} cached rows "
+                      f"({t_block:.2f} s), scaled x{n_active / rows:.1f} rows x {c.L} blocks, "
+                      f"+ select/active-set/Euler over all N ({t_tail:.2f} s); projected "
+                      f"{t_iter:.1f} s per iteration"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): this build has no "
+              f"multi-GPU path; the per-GPU kernel is what is measured.", file=sys.stderr)
+        sys.exit(2)
+    from token_sparse_attention_compact_amd import hsa as H
+    H.load()
+    c = synth.CONFIGS[3].with_(L=args.blocks)
+    sched = H.make_schedule(c.T, c.budgets, c.counts())
+    n_active = H.hsa_n_active(sched, ITER)
+    sigma = synth.sigma_schedule(c.T)
+    model, state = device_inputs(c, H, seed_base=3)
+    torch.cuda.synchronize()
+
+    elapsed = timed_steps(H, model, sched, state, sigma, args.steps, args.warmup)
+    ms = elapsed / args.steps * 1e3
+    it_s = args.steps / elapsed
+
+    t_attn = time_attention(H, model, c, n_active, args.attn_reps)
+    attn_flop = 4.0 * n_active * c.N * c.D
+    attn_tflops = attn_flop / t_attn / 1e12
+    gemm_flop = 2.0 * n_active * c.D * (3 * c.D + c.D + 2 * c.F) * c.L
+    iter_flop = attn_flop * c.L + gemm_flop
+
+    out = {
+        "metric": METRIC,
+        "value": round(it_s, 4),
+        "unit": "iter/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (random-init weights N(0,1/fan_in), N(0,1) caches and latents)",
+        "config": {"workload": f"wan1.3b-shaped {c.L}-block stack, N=32760 (21x30x52), 25% active "
+                               f"(iteration {ITER} of T=40, budgets 40/20/10, regroup on)",
+                   "N": c.N, "n_active": n_active, "blocks": c.L, "D": c.D, "heads": c.H,
+                   "head_dim": c.Dh, "F": c.F, "C": c.C},
+        "attn_tflops": round(attn_tflops, 2),
+        "iter_tflops": round(iter_flop * it_s / 1e12, 2),
+        "roofline": {"bound": "mfma", "kernel": "attn_bf16_d128_kernel",
+                     "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "avg_launch_us": round(t_attn * 1e6, 2),
+                     "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(c, args.cpu_rows)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
