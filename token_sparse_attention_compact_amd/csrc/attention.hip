@@ -4,39 +4,51 @@
 // O(|A_i| * N) instead of O(N^2).  No mask.
 //
 // bf16, Dh = 128: flash-style online softmax on v_mfma_f32_32x32x16_bf16.
-//  * One workgroup = one head x 128 queries (4 wavefronts x 32); it streams
-//    the head's K/V in tiles of 64 rows through double-buffered LDS, the next
-//    tile's global loads in flight while the current one is consumed.
+//  * One workgroup = one head x 256 queries (8 wavefronts x 32, two per SIMD
+//    so one wave's softmax overlaps the other's MFMAs).  It streams the
+//    head's K/V in tiles of 64 rows through a 4-stage LDS ring.
+//  * Tiles move HBM -> LDS with buffer_load ... lds (no register staging, no
+//    per-load VALU work; rows past the end read as zero).  Each 16-byte chunk
+//    lands at an XOR-swizzled position of its 256-byte row, so the operand
+//    reads below hit distinct banks.
 //  * Each wavefront computes S^T = K Q^T (keys as MFMA rows, its 32 queries
-//    as columns), so a lane holds one query's scores: the row max and row
-//    sum are in-lane except for one exchange between the two lane halves.
-//  * P^T goes straight from the S^T accumulators into the B operand of
-//    O^T = V^T P^T; the key order inside each 16-wide MFMA step follows the
-//    accumulator layout, and the V^T operand is read in the same order from a
-//    transposed copy of the V tile in LDS (chunks of 4 keys, XOR-swizzled by
-//    the row so both the transposing writes and the operand reads spread
-//    over the banks).
+//    as columns): a lane holds one query's scores, so the row max and row
+//    sum are in-lane except one exchange between the lane halves
+//    (v_permlane32_swap).
+//  * P^T goes from the S^T accumulators into the B operand of O^T = V^T P^T;
+//    the key order of each 16-key MFMA step follows the accumulator layout.
+//    The V^T operand is read from the row-major V tile with the transposing
+//    LDS read ds_read_b64_tr_b16: per 16-lane group it takes a 4-key x
+//    16-dim block and gives lane i dim i of those 4 keys.
 //  * exp2 with scale*log2(e) folded into one FMA; the running max is only
 //    raised (and O, l rescaled) when a tile's max exceeds it by more than 8,
-//    which is exact after the final division and keeps P <= 2^8.
+//    which is exact after the final division and keeps P <= 2^8.  Row sums
+//    use v_dot2 over the bf16 P that also feeds the MFMA.
 //  * When |A_i| is small the KV range is split across workgroups; partial
 //    (O, max, sum) are merged in a fixed split order (deterministic).
 //  * Workgroup ids are remapped so each XCD runs a contiguous range of
-//    (head, query tile) pairs: the workgroups sharing an XCD's L2 stream the
-//    same head's K/V at the same time.
+//    (split, head, query tile): the workgroups sharing an XCD's L2 stream
+//    the same head's K/V at the same time.
 // Other head sizes / float32: a plain LDS-tiled kernel (float32 arithmetic).
 #include "common.h"
 
 namespace hsa {
 namespace {
 
-constexpr int kAttnThreads = 256;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr int NW = 8;                      // wavefronts per workgroup
+constexpr int kAttnThreads = NW * 64;
 constexpr int DH = 128;
-constexpr int BKV = 64;
-constexpr int BQ = 128;
-constexpr int KSTR = DH + 8;              // bf16 per K row in LDS
-constexpr int KCHUNKS = BKV * DH / 8 / kAttnThreads;  // 16-byte chunks per thread (= 4)
-constexpr float kRescaleSlack = 8.0f;     // log2 units
+constexpr int BKV = 64;                    // keys per tile
+constexpr int BQ = NW * 32;                // queries per workgroup
+constexpr int NST = 4;                     // LDS stages
+constexpr int ROWB = DH * 2;               // bytes per K/V row of one head (256)
+constexpr int TILEB = BKV * ROWB;          // 16 KiB per K or V tile
+constexpr int LOADS = TILEB / 16 / kAttnThreads;   // 16-byte loads per lane per tile and operand (2)
+constexpr float kRescaleSlack = 8.0f;      // log2 units
 
 __device__ __forceinline__ int32_t xcd_remap(int32_t bid, int32_t total) {
   constexpr int32_t kXcd = 8;
@@ -46,22 +58,70 @@ __device__ __forceinline__ int32_t xcd_remap(int32_t bid, int32_t total) {
   return (bid % kXcd) * per + bid / kXcd;
 }
 
-// Swizzled 4-key chunk index of row d of the transposed V tile.
-__device__ __forceinline__ int vt_chunk(int d, int kc) { return kc ^ ((d ^ (d >> 3)) & 15); }
+// Position of 16-byte chunk c (0..15) within row r of a K / V tile in LDS.
+__device__ __forceinline__ int k_pos(int r, int c) { return c ^ (r & 15); }
+__device__ __forceinline__ int v_pos(int r, int c) { return c ^ ((r & 3) << 2); }
 
-__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {  // low halves of a, b
-  return (a & 0xffffu) | (b << 16);
-}
-__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {  // high halves of a, b
-  return (a >> 16) | (b & 0xffff0000u);
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource for `bytes` bytes from `base` (raw buffer, stride 0):
+// loads at offsets >= bytes return zero.
+__device__ __forceinline__ i32x4 buffer_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return i32x4{(int)(uint32_t)a, (int)(uint32_t)(a >> 32), (int)bytes, 0x00020000};
 }
 
-__global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_d128_kernel(
+// One 16-byte-per-lane buffer load straight into LDS at lds_addr + 16*lane.
+// Written as inline asm so the compiler does not treat the LDS stage as
+// written by an unknown DMA (it would wait for every load in flight before
+// each LDS read); completion is tracked by hand with vmcnt before the barrier.
+// The instruction has no register result.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(uint32_t lds_addr, uint32_t voff, i32x4 rsrc) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Issue the loads of one K and one V tile (rows row0.. of head h) into LDS.
+__device__ __forceinline__ void issue_tile(const bf16* k, const bf16* v, int32_t row0, int32_t nkv,
+                                           int32_t ldk, int32_t h, uint32_t sk, uint32_t sv,
+                                           const uint32_t* voff_k, const uint32_t* voff_v,
+                                           int wave) {
+  const int32_t rows_left = nkv - row0;
+  const uint32_t nbytes = rows_left > 0 ? (uint32_t)rows_left * (uint32_t)ldk * 2u : 0u;
+  const size_t off = ((size_t)row0 * ldk + (size_t)h * DH) * 2;
+  const i32x4 rk = buffer_rsrc(reinterpret_cast<const char*>(k) + off, nbytes);
+  const i32x4 rv = buffer_rsrc(reinterpret_cast<const char*>(v) + off, nbytes);
+#pragma unroll
+  for (int j = 0; j < LOADS; ++j) {
+    // this wave's 1 KiB slice of the tile (wave-uniform: scalar for M0)
+    const uint32_t blk = (uint32_t)__builtin_amdgcn_readfirstlane((j * NW + wave) * 1024);
+    dma16(sk + blk, voff_k[j], rk);
+    dma16(sv + blk, voff_v[j], rv);
+  }
+}
+
+// Wait until at most OUT tiles' loads of this wave are in flight, then
+// synchronise the workgroup.  No memory fence: the only LDS writes are the
+// tile loads, whose completion vmcnt reports.
+template <int OUT>
+__device__ __forceinline__ void wait_tiles_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"(OUT * 2 * LOADS) : "memory");
+}
+
+__global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_d128_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     bf16* __restrict__ o, float* __restrict__ part_o, float* __restrict__ part_ml, int32_t nA,
     int32_t nkv, int32_t H, float c, int32_t n_qt, int32_t splits, int32_t tiles_per_split) {
-  __shared__ __attribute__((aligned(16))) bf16 sK[2][BKV * KSTR];
-  __shared__ __attribute__((aligned(16))) bf16 sVt[2][DH * BKV];
+  __shared__ __attribute__((aligned(1024))) char smem[2 * NST * TILEB];
+  const char* const sK = smem;
+  const char* const sV = smem + NST * TILEB;
+  const uint32_t sK_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
+  const uint32_t sV_lds = sK_lds + NST * TILEB;
 
   const int32_t total = n_qt * H * splits;
   const int32_t t = xcd_remap(blockIdx.x, total);
@@ -80,64 +140,41 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_d128_kernel(
   const int32_t kv_end = min(nkv, kv_begin + tiles_per_split * BKV);
   const int32_t ntiles = (kv_end - kv_begin + BKV - 1) / BKV;
 
-  // ---- Q^T fragments (B operand): lane = query column, 8 consecutive dims.
+  // ---- per-lane load offsets (bytes within a tile of this head), fixed for all tiles
+  uint32_t voff_k[LOADS], voff_v[LOADS];
+#pragma unroll
+  for (int j = 0; j < LOADS; ++j) {
+    const int s = (j * NW + wave) * 64 + lane;   // 16-byte slot in the tile
+    const int r = s >> 4, p = s & 15;
+    voff_k[j] = (uint32_t)(r * D * 2 + k_pos(r, p) * 16);   // k_pos is an involution
+    voff_v[j] = (uint32_t)(r * D * 2 + v_pos(r, p) * 16);
+  }
+
+  // ---- Q^T fragments (B operand): lane = query column, 8 consecutive dims
   const int32_t qi = qt * BQ + wave * 32 + l32;
   const bool q_ok = qi < nA;
   bf16x8 qf[DH / 16];
   {
-    const bf16* qrow = q + (size_t)(q_ok ? qi : 0) * D + h * DH + half * 8;
+    const bf16* qrow = q + (size_t)(q_ok ? qi : nA - 1) * D + h * DH + half * 8;
 #pragma unroll
-    for (int dk = 0; dk < DH / 16; ++dk) {
-      u32x4 raw = q_ok ? *reinterpret_cast<const u32x4*>(qrow + dk * 16) : u32x4{0u, 0u, 0u, 0u};
-      qf[dk] = __builtin_bit_cast(bf16x8, raw);
-    }
+    for (int dk = 0; dk < DH / 16; ++dk)
+      qf[dk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + dk * 16));
   }
 
-  // ---- global -> register staging of one K/V tile
-  u32x4 rk[KCHUNKS], rv[4];
-  const int vdc = tid & 15;   // V: 8-dim chunk
-  const int vkg = tid >> 4;   // V: group of 4 keys
-  auto load_tile = [&](int32_t base) {
+  // ---- per-lane LDS read offsets
+  // K (A operand of S^T): row kb*32 + l32, chunk 2*dk + half
+  uint32_t koff[DH / 16];
 #pragma unroll
-    for (int i = 0; i < KCHUNKS; ++i) {
-      const int cidx = tid + i * kAttnThreads;
-      const int r = cidx >> 4, ch = cidx & 15;
-      const int32_t key = base + r;
-      rk[i] = (key < kv_end) ? *reinterpret_cast<const u32x4*>(k + (size_t)key * D + h * DH + ch * 8)
-                             : u32x4{0u, 0u, 0u, 0u};
-    }
+  for (int dk = 0; dk < DH / 16; ++dk) koff[dk] = (uint32_t)(l32 * ROWB + k_pos(l32, 2 * dk + half) * 16);
+  // V (transposing reads): 16-lane group g points at keys kbase + i/4, dims d0 + 4*(i%4)
+  const int grp = lane >> 4, gi = lane & 15;
+  const int vrow = 4 * (grp >> 1) + (gi >> 2);   // key within a 8-key step (plus 16*jp + 8*second + 32*kb)
+  uint32_t voffr[DH / 32];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int32_t key = base + vkg * 4 + r;
-      rv[r] = (key < kv_end) ? *reinterpret_cast<const u32x4*>(v + (size_t)key * D + h * DH + vdc * 8)
-                             : u32x4{0u, 0u, 0u, 0u};
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < KCHUNKS; ++i) {
-      const int cidx = tid + i * kAttnThreads;
-      const int r = cidx >> 4, ch = cidx & 15;
-      *reinterpret_cast<u32x4*>(&sK[buf][r * KSTR + ch * 8]) = rk[i];
-    }
-    // transpose 4 keys x 8 dims -> 8 rows of V^T, 4 keys (8 bytes) each
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-#pragma unroll
-      for (int hi = 0; hi < 2; ++hi) {
-        const int d = vdc * 8 + w * 2 + hi;
-        u32x2 val;
-        if (hi == 0) {
-          val[0] = pack_lo(rv[0][w], rv[1][w]);
-          val[1] = pack_lo(rv[2][w], rv[3][w]);
-        } else {
-          val[0] = pack_hi(rv[0][w], rv[1][w]);
-          val[1] = pack_hi(rv[2][w], rv[3][w]);
-        }
-        *reinterpret_cast<u32x2*>(&sVt[buf][d * BKV + vt_chunk(d, vkg) * 4]) = val;
-      }
-    }
-  };
+  for (int db = 0; db < DH / 32; ++db) {
+    const int chunk = 4 * db + 2 * (grp & 1) + ((gi & 3) >> 1);
+    voffr[db] = (uint32_t)(vrow * ROWB + v_pos(vrow, chunk) * 16 + 8 * (gi & 1));
+  }
 
   f32x16 acc_o[DH / 32];
 #pragma unroll
@@ -146,17 +183,33 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_d128_kernel(
     for (int r = 0; r < 16; ++r) acc_o[db][r] = 0.f;
   float m_run = -INFINITY;   // running max, log2 units (scaled)
   float l_run = 0.f;         // this lane's partial row sum
+  const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
 
-  if (ntiles > 0) {
-    load_tile(kv_begin);
-    store_tile(0);
-  }
-  __syncthreads();
+  // Q in registers before the LDS pipeline starts (a builtin, so the compiler's own
+  // wait accounting sees it and adds no vmcnt waits for Q inside the loop)
+  __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0), expcnt/lgkmcnt unconstrained
+#pragma unroll
+  for (int st = 0; st < NST - 1; ++st)
+    if (st < ntiles)
+      issue_tile(k, v, kv_begin + st * BKV, nkv, D, h, sK_lds + st * TILEB, sV_lds + st * TILEB,
+                 voff_k, voff_v, wave);
 
   for (int it = 0; it < ntiles; ++it) {
-    const int buf = it & 1;
+    const int stage = it % NST;
+    // tile `it` landed (later tiles may still be in flight), visible to every wave;
+    // every wave is also done reading tile it-1, whose stage is refilled next
+    const int ahead = min(NST - 2, ntiles - 1 - it);
+    if (ahead >= 2) wait_tiles_barrier<2>();
+    else if (ahead == 1) wait_tiles_barrier<1>();
+    else wait_tiles_barrier<0>();
+    if (it + NST - 1 < ntiles) {
+      const int ns = (it + NST - 1) % NST;
+      issue_tile(k, v, kv_begin + (it + NST - 1) * BKV, nkv, D, h, sK_lds + ns * TILEB,
+                 sV_lds + ns * TILEB, voff_k, voff_v, wave);
+    }
     const int32_t base = kv_begin + it * BKV;
-    if (it + 1 < ntiles) load_tile(base + BKV);
+    const char* kt = sK + stage * TILEB;
+    const char* vt = sV + stage * TILEB;
 
     // ---- S^T = K Q^T for 64 keys x 32 queries: two 32x32 blocks
     f32x16 s[2];
@@ -164,10 +217,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_d128_kernel(
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-      const bf16* krow = &sK[buf][(kb * 32 + l32) * KSTR + half * 8];
 #pragma unroll
       for (int dk = 0; dk < DH / 16; ++dk) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(krow + dk * 16);
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kt + kb * 32 * ROWB + koff[dk]);
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[dk], s[kb], 0, 0, 0);
       }
     }
@@ -181,12 +233,15 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_d128_kernel(
           if (key >= kv_end) s[kb][r] = -INFINITY;
         }
     }
-    float mx = s[0][0];
+    float mx = fmaxf(s[0][0], s[0][1]);
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
+    for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
     const float mxs = mx * c;
     const bool need = mxs > m_run + kRescaleSlack;
     if (__ballot(need) != 0ull) {
@@ -200,44 +255,44 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_d128_kernel(
       m_run = m_new;
     }
     bf16x8 pb[4];
-    float lsum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int jp = 0; jp < 2; ++jp) {
         bf16x8 pv;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][jp * 8 + e], c, -m_run));
-          lsum += p;
-          pv[e] = (bf16)p;
-        }
+        for (int e = 0; e < 8; ++e)
+          pv[e] = (bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][jp * 8 + e], c, -m_run));
         pb[kb * 2 + jp] = pv;
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const bf16x2 pair = {pv[e], pv[e + 1]};
+          l_run = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, l_run, false);
+        }
       }
-    l_run += lsum;
 
-    // ---- O^T += V^T P^T: k-step ts covers keys kb*32 + 16*jp + {0..3, 8..11} + 4*half
+    // ---- O^T += V^T P^T: k-step ts = (kb, jp) covers keys kb*32 + 16*jp + 4*half + {0..3, 8..11}
 #pragma unroll
-    for (int db = 0; db < DH / 32; ++db) {
-      const int d = db * 32 + l32;
-      const bf16* vrow = &sVt[buf][d * BKV];
+    for (int ts = 0; ts < 4; ++ts) {
+      const int kb = ts >> 1, jp = ts & 1;
+      const char* vk = vt + (kb * 32 + 16 * jp) * ROWB;
 #pragma unroll
-      for (int ts = 0; ts < 4; ++ts) {
-        const int kb = ts >> 1, jp = ts & 1;
-        const int kc1 = 8 * kb + 4 * jp + half;
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + vt_chunk(d, kc1) * 4);
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + vt_chunk(d, kc1 + 2) * 4);
-        const u32x4 raw = {lo[0], lo[1], hi[0], hi[1]};
+      for (int db = 0; db < DH / 32; ++db) {
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vk + voffr[db]));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vk + 8 * ROWB + voffr[db]));
+        const u32x4 raw = {__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
+                           __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]};
         acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, raw), pb[ts],
                                                              acc_o[db], 0, 0, 0);
       }
     }
-
-    if (it + 1 < ntiles) store_tile(buf ^ 1);
-    __syncthreads();
   }
 
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  float l_tot;
+  {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
+    l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+  }
   if (!q_ok) return;
   // acc_o[db][r] <-> dim db*32 + 8*(r/4) + 4*half + r%4, query l32
   if (splits == 1) {
@@ -364,15 +419,25 @@ struct SplitPlan {
 };
 
 SplitPlan plan_split(int32_t nA, int32_t nkv, int32_t H) {
+  // One workgroup per CU at a time (128 KiB of LDS each): pick the number of
+  // KV splits s that minimises (rounds of 256 workgroups) x (tiles per split),
+  // the smallest such s (least merge work), with at least 8 tiles per split.
+  constexpr int32_t kCus = 256;
   SplitPlan p;
   p.n_qt = cdiv(nA, BQ);
   const int32_t ntiles = cdiv(nkv, BKV);
   const int32_t base = p.n_qt * H;
-  constexpr int32_t kTargetWgs = 1024;  // 2 resident workgroups on each of 256 CUs, x2
-  int32_t s = 1;
-  if (base < kTargetWgs / 2) s = min(16, cdiv(kTargetWgs, base));
-  s = max(1, min(s, ntiles / 4));       // keep >= 4 tiles per split
-  p.tiles_per_split = cdiv(ntiles, s);
+  const int32_t smax = max(1, min(16, ntiles / 8));
+  int64_t best = -1;
+  int32_t best_s = 1;
+  for (int32_t s = 1; s <= smax; ++s) {
+    const int64_t cost = (int64_t)cdiv((int64_t)base * s, kCus) * cdiv(ntiles, s);
+    if (best < 0 || cost < best) {
+      best = cost;
+      best_s = s;
+    }
+  }
+  p.tiles_per_split = cdiv(ntiles, best_s);
   p.splits = cdiv(ntiles, p.tiles_per_split);
   return p;
 }
