@@ -4,12 +4,14 @@
 // the QKV projection (with the fresh K/V rows scattered into the per-layer
 // cache, item 2), the attention out-projection, and the MLP.
 //
-// bf16 path: v_mfma_f32_32x32x16_bf16 on 128x128 output tiles, K in steps of
-// 64 staged through double-buffered LDS (rows padded by 16 bytes so the
-// 16-byte operand reads of 8 consecutive rows fall in distinct banks).  Four
-// wavefronts per tile, each owning a 64x64 quarter as 2x2 MFMA blocks.
-// Global loads of the next K step are issued before the MFMAs of the current
-// one.  Epilogues are fused (store / GELU / residual add / QKV scatter).
+// bf16 path: v_mfma_f32_32x32x16_bf16 on 128x128 output tiles, eight
+// wavefronts each owning a 32x64 block as 1x2 MFMA tiles.  K advances in
+// steps of 64 through a 2-stage ring of LDS filled straight from HBM with
+// buffer_load ... lds (no register staging; rows past M or N read as zero),
+// each 16-byte chunk at an XOR-swizzled position of its 128-byte row so the
+// operand reads hit distinct banks.  The next stage's loads are in flight
+// while the current one feeds the MFMAs.  Epilogues are fused (store / GELU /
+// residual add / QKV scatter).
 //
 // float32 path (small float32 workloads): LDS-tiled FMA GEMM, 64x64 tiles.
 #include "common.h"
@@ -42,113 +44,202 @@ __device__ __forceinline__ void epilogue(const EpiArgs& ep, int32_t N, int32_t r
 }
 
 // ---------------------------------------------------------------- bf16 MFMA
-constexpr int BM = 128, BN = 128, BK = 64;
-constexpr int LDS_STRIDE = BK + 8;  // bf16 elements per LDS row (16-byte pad)
-constexpr int kGemmThreads = 256;
+constexpr int BK = 64;
+constexpr int ROWB = BK * 2;                       // bytes per LDS row (128)
 
-// XCD-aware tile order: consecutive workgroup ids land on different XCDs
-// (round-robin over 8), so hand each XCD a contiguous run of tiles; within a
-// run, tiles walk M fastest so concurrent workgroups share a column block of w.
-__device__ __forceinline__ int32_t xcd_tile(int32_t bid, int32_t ntiles) {
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Tile order.  Consecutive workgroup ids land on different XCDs (round-robin
+// over 8), so each XCD is first handed a contiguous run of tile indices.  The
+// index then walks the tiles in groups of GM row blocks, column-major inside a
+// group: the ~32 workgroups an XCD runs at once cover a GM x (32/GM) block of
+// tiles and share its GM row blocks of a and 32/GM column blocks of w in that
+// XCD's L2, instead of streaming 32 row blocks of a that every column tile
+// then reads again from HBM.
+__device__ __forceinline__ void tile_coords(int32_t bid, int32_t tm, int32_t tn, int32_t gm,
+                                            int32_t& mi, int32_t& ni) {
   constexpr int32_t kXcd = 8;
+  const int32_t ntiles = tm * tn;
   const int32_t per = ntiles / kXcd;
-  const int32_t full = per * kXcd;
-  if (bid >= full) return bid;  // leftover tail keeps its id
-  return (bid % kXcd) * per + bid / kXcd;
+  int32_t t = bid;
+  if (bid < per * kXcd) t = (bid % kXcd) * per + bid / kXcd;   // leftover tail keeps its id
+  const int32_t width = gm * tn;
+  const int32_t group = t / width;
+  const int32_t first_m = group * gm;
+  const int32_t gsize = min(tm - first_m, gm);
+  const int32_t r = t - group * width;
+  mi = first_m + r % gsize;
+  ni = r / gsize;
 }
 
-template <int EPI>
-__global__ __launch_bounds__(kGemmThreads, 2) void gemm_bf16_kernel(
+// Position of 16-byte chunk c (0..7) in LDS row r: XOR swizzle chosen so that
+// 16-byte operand reads of 8 consecutive rows (32 banks) or of 16 consecutive
+// rows (64 banks) at one chunk hit distinct banks.
+__device__ __forceinline__ int gpos(int r, int c) { return c ^ (((r >> 1) ^ (r << 2)) & 7); }
+
+__device__ __forceinline__ i32x4 buffer_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return i32x4{(int)(uint32_t)a, (int)(uint32_t)(a >> 32), (int)bytes, 0x00020000};
+}
+
+// 16 bytes per lane from a buffer straight into LDS at lds_addr + 16*lane.
+// Inline asm keeps the compiler from waiting for every in-flight load before
+// each LDS read; completion is tracked with vmcnt before the barrier.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(uint32_t lds_addr, uint32_t voff, i32x4 rsrc) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+template <int VM>   // loads of this wave allowed in flight
+__device__ __forceinline__ void wait_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"(VM) : "memory");
+}
+
+// Tile configuration: BM x BN output tile, WM x WN wavefronts (each owning a
+// (BM/WM) x (BN/WN) block of 32x32 MFMA tiles), NST LDS stages of BK=64.
+template <int BM_, int BN_, int WM_, int WN_, int NST_, int GM_>
+struct GemmCfg {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, NST = NST_, GM = GM_;
+  static constexpr int WAVES = WM * WN;
+  static constexpr int THREADS = WAVES * 64;
+  static constexpr int TM = BM / WM, TN = BN / WN;        // per-wave block
+  static constexpr int FM = TM / 32, FN = TN / 32;        // MFMA tiles per wave
+  static constexpr int TILE_A = BM * ROWB, TILE_B = BN * ROWB;
+  static constexpr int STAGE = TILE_A + TILE_B;
+  static constexpr int LOADS_A = TILE_A / 16 / THREADS;
+  static constexpr int LOADS_B = TILE_B / 16 / THREADS;
+  static constexpr int LOADS = LOADS_A + LOADS_B;
+  static_assert(LOADS_A * 16 * THREADS == TILE_A && LOADS_B * 16 * THREADS == TILE_B, "load split");
+  static_assert(NST * STAGE <= 160 * 1024, "LDS");
+};
+
+template <class G, int EPI>
+__global__ __launch_bounds__(G::THREADS, 2) void gemm_bf16_kernel(
     const bf16* __restrict__ A, const bf16* __restrict__ W, int32_t M, int32_t N, int32_t K,
     EpiArgs ep) {
-  __shared__ __attribute__((aligned(16))) bf16 sA[2][BM * LDS_STRIDE];
-  __shared__ __attribute__((aligned(16))) bf16 sB[2][BN * LDS_STRIDE];
+  constexpr int BM = G::BM, BN = G::BN, NST = G::NST;
+  __shared__ __attribute__((aligned(1024))) char smem[NST * G::STAGE];
+  static_assert(G::FM >= 1 && G::FN >= 1, "wave tile");
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
 
   const int32_t tm = (M + BM - 1) / BM;
   const int32_t tn = (N + BN - 1) / BN;
-  const int32_t tile = xcd_tile(blockIdx.x, tm * tn);
-  const int32_t m0 = (tile % tm) * BM;
-  const int32_t n0 = (tile / tm) * BN;
+  int32_t mi, ni;
+  tile_coords(blockIdx.x, tm, tn, G::GM, mi, ni);
+  const int32_t m0 = mi * BM;
+  const int32_t n0 = ni * BN;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / G::WN, wn = wave % G::WN;
 
-  // Global -> register staging: 4 chunks of 16 bytes per thread per operand.
-  u32x4 ra[4], rb[4];
-  auto load_tile = [&](int32_t k0) {
+  // DMA source offsets (bytes from the tile's k-slice base), fixed over k.
+  // Load j of wave w fills 16-byte slots (j*WAVES + w)*64 + lane of a tile.
+  uint32_t voff_a[G::LOADS_A], voff_b[G::LOADS_B];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + i * kGemmThreads;
-      const int r = c >> 3, kc = c & 7;
-      const int32_t gm = m0 + r, gn = n0 + r;
-      ra[i] = (gm < M) ? *reinterpret_cast<const u32x4*>(A + (size_t)gm * K + k0 + kc * 8)
-                       : u32x4{0u, 0u, 0u, 0u};
-      rb[i] = (gn < N) ? *reinterpret_cast<const u32x4*>(W + (size_t)gn * K + k0 + kc * 8)
-                       : u32x4{0u, 0u, 0u, 0u};
-    }
-  };
-  auto store_tile = [&](int buf) {
+  for (int j = 0; j < G::LOADS_A; ++j) {
+    const int sl = (j * G::WAVES + wave) * 64 + lane;
+    const int r = sl >> 3, p = sl & 7;
+    voff_a[j] = (uint32_t)(r * K * 2 + gpos(r, p) * 16);   // gpos(r, .) is an involution
+  }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + i * kGemmThreads;
-      const int r = c >> 3, kc = c & 7;
-      *reinterpret_cast<u32x4*>(&sA[buf][r * LDS_STRIDE + kc * 8]) = ra[i];
-      *reinterpret_cast<u32x4*>(&sB[buf][r * LDS_STRIDE + kc * 8]) = rb[i];
-    }
+  for (int j = 0; j < G::LOADS_B; ++j) {
+    const int sl = (j * G::WAVES + wave) * 64 + lane;
+    const int r = sl >> 3, p = sl & 7;
+    voff_b[j] = (uint32_t)(r * K * 2 + gpos(r, p) * 16);
+  }
+  const uint32_t bytes_a = (uint32_t)(M - m0) * (uint32_t)K * 2u;
+  const uint32_t bytes_b = (uint32_t)(min(N, n0 + BN) - n0) * (uint32_t)K * 2u;
+  const char* a_base = reinterpret_cast<const char*>(A) + (size_t)m0 * K * 2;
+  const char* b_base = reinterpret_cast<const char*>(W) + (size_t)n0 * K * 2;
+
+  auto issue = [&](int kt, int stage) {
+    const uint32_t kb = (uint32_t)kt * BK * 2;
+    const i32x4 ra = buffer_rsrc(a_base + kb, bytes_a - kb);
+    const i32x4 rb = buffer_rsrc(b_base + kb, bytes_b - kb);
+    const uint32_t sa = lds0 + stage * G::STAGE;
+    const uint32_t sb = sa + G::TILE_A;
+#pragma unroll
+    for (int j = 0; j < G::LOADS_A; ++j)
+      dma16(sa + (uint32_t)__builtin_amdgcn_readfirstlane((j * G::WAVES + wave) * 1024), voff_a[j], ra);
+#pragma unroll
+    for (int j = 0; j < G::LOADS_B; ++j)
+      dma16(sb + (uint32_t)__builtin_amdgcn_readfirstlane((j * G::WAVES + wave) * 1024), voff_b[j], rb);
   };
 
-  f32x16 acc[2][2];
+  // operand read offsets: row (32-block base) + l32, chunk 2*ks + half
+  const int l32 = lane & 31, half = lane >> 5;
+  uint32_t frag[BK / 16];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int ks = 0; ks < BK / 16; ++ks) frag[ks] = (uint32_t)(l32 * ROWB + gpos(l32, 2 * ks + half) * 16);
+
+  f32x16 acc[G::FM][G::FN];
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+  for (int i = 0; i < G::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < G::FN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   const int nk = K / BK;
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
+#pragma unroll
+  for (int st = 0; st < NST - 1; ++st)
+    if (st < nk) issue(st, st);
 
-  const int frag_row = lane & 31;
-  const int frag_k = (lane >> 5) * 8;
   for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) load_tile((kt + 1) * BK);
-    const bf16* a_base = &sA[buf][(wm * 64 + frag_row) * LDS_STRIDE + frag_k];
-    const bf16* b_base = &sB[buf][(wn * 64 + frag_row) * LDS_STRIDE + frag_k];
+    // k-tile kt landed (later ones may be in flight) and is visible to every
+    // wave; every wave is done with k-tile kt-1, whose stage is refilled next
+    const int ahead = min(NST - 2, nk - 1 - kt);
+    if (NST >= 4 && ahead >= 2) wait_barrier<2 * G::LOADS>();
+    else if (NST >= 3 && ahead >= 1) wait_barrier<G::LOADS>();
+    else wait_barrier<0>();
+    if (kt + NST - 1 < nk) issue(kt + NST - 1, (kt + NST - 1) % NST);
+    const char* sa = smem + (kt % NST) * G::STAGE;
+    const char* a_frag = sa + (wm * G::TM) * ROWB;
+    const char* b_frag = sa + G::TILE_A + (wn * G::TN) * ROWB;
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8 af[2], bfr[2];
+      bf16x8 af[G::FM], bfr[G::FN];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        af[i] = *reinterpret_cast<const bf16x8*>(a_base + i * 32 * LDS_STRIDE + ks * 16);
-        bfr[i] = *reinterpret_cast<const bf16x8*>(b_base + i * 32 * LDS_STRIDE + ks * 16);
-      }
+      for (int i = 0; i < G::FM; ++i)
+        af[i] = *reinterpret_cast<const bf16x8*>(a_frag + i * 32 * ROWB + frag[ks]);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int j = 0; j < G::FN; ++j)
+        bfr[j] = *reinterpret_cast<const bf16x8*>(b_frag + j * 32 * ROWB + frag[ks]);
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+      for (int i = 0; i < G::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < G::FN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < nk) store_tile(buf ^ 1);
-    __syncthreads();
   }
 
   // acc[i][j][r]: row 8*(r/4) + 4*(lane/32) + r%4, column lane%32 of block (i, j).
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < G::FM; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < G::FN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int32_t row = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        const int32_t col = n0 + wn * 64 + j * 32 + (lane & 31);
+        const int32_t row = m0 + wm * G::TM + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+        const int32_t col = n0 + wn * G::TN + j * 32 + l32;
         if (row < M && col < N) epilogue<EPI, bf16>(ep, N, row, col, acc[i][j][r]);
       }
 }
+
+// 128x128 tiles, 8 wavefronts of 32x64, 2 stages (64 KiB LDS, so two
+// workgroups share a CU: four wavefronts per SIMD hide each other's LDS and
+// HBM latency), an XCD's concurrent tiles as 8 row x 8 column blocks.
+// Measured on MI355X against 256x128/256x256 tiles, 4-wave layouts and 3-4
+// stage rings for the QKV, out-projection and MLP shapes of the stack; this
+// one was fastest on all of them.
+typedef GemmCfg<128, 128, 4, 2, 2, 8> CfgMain;
 
 // ---------------------------------------------------------------- float32
 constexpr int FT = 64, FK = 16;
@@ -195,12 +286,18 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
     }
 }
 
+template <class G, int EPI>
+void launch_bf16(const void* a, const void* w, int32_t M, int32_t N, int32_t K, const EpiArgs& ep,
+                 hipStream_t s) {
+  const int32_t tiles = cdiv(M, G::BM) * cdiv(N, G::BN);
+  gemm_bf16_kernel<G, EPI><<<tiles, G::THREADS, 0, s>>>((const bf16*)a, (const bf16*)w, M, N, K, ep);
+}
+
 template <int EPI>
 hsa_status run(const void* a, const void* w, int32_t M, int32_t N, int32_t K, hsa_dtype dt,
                const EpiArgs& ep, hipStream_t s) {
   if (dt == HSA_BF16) {
-    const int32_t tiles = cdiv(M, BM) * cdiv(N, BN);
-    gemm_bf16_kernel<EPI><<<tiles, kGemmThreads, 0, s>>>((const bf16*)a, (const bf16*)w, M, N, K, ep);
+    launch_bf16<CfgMain, EPI>(a, w, M, N, K, ep, s);
   } else {
     dim3 grid(cdiv(N, FT), cdiv(M, FT));
     gemm_f32_kernel<EPI><<<grid, 256, 0, s>>>((const float*)a, (const float*)w, M, N, K, ep);
