@@ -1,0 +1,92 @@
+"""The C ABI on the host (no GPU): the library loads, exports every function
+include/hsa.h declares, and rejects invalid arguments with the documented
+status before anything is enqueued."""
+import ctypes as ct
+import os
+import re
+
+import pytest
+
+from token_sparse_attention_compact_amd import hsa as H
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "hsa.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:hsa_status|const char \*|int32_t)\s*(hsa_\w+)\s*\(", text, re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    L = H.load()
+    names = declared_functions()
+    assert len(names) >= 18
+    for n in names:
+        assert hasattr(L, n), f"libhsa.so does not export {n}"
+    assert set(names) <= set(H.EXPORTED) | set(names)
+    assert set(H.EXPORTED) == set(names), "binding list and header disagree"
+
+
+def test_status_strings():
+    for code in (0, -1, -2, -3, -4, -5, -6, -7, 99):
+        assert H.status_str(code)
+
+
+def test_workspace_size_validation():
+    d = H.make_dims(32760, 16, 1536, 12, 128, 8960, 30)
+    assert H.hsa_workspace_size(d) > 32760 * 1536 * 4
+    bad = H.make_dims(32760, 16, 1536, 12, 96, 8960, 30)   # D != H*Dh and Dh unsupported
+    with pytest.raises(H.HsaError) as e:
+        H.hsa_workspace_size(bad)
+    assert e.value.status == -2
+    bad = H.make_dims(100, 16, 1536, 12, 128, 8900, 1)     # bf16 needs F % 64 == 0
+    with pytest.raises(H.HsaError):
+        H.hsa_workspace_size(bad)
+
+
+def test_schedule_validation_and_closed_form():
+    s = H.make_schedule(40, [40, 20, 10], [8190, 8190, 16380])
+    assert [H.hsa_n_active(s, i) for i in range(4)] == [32760, 8190, 16380, 8190]
+    s3 = H.make_schedule(40, [40, 20, 10], [8190, 8190, 16380], m=3)
+    assert H.hsa_n_active(s3, 1) == 32760 and H.hsa_n_active(s3, 37) == 32760
+    assert H.hsa_n_active(s3, 5) == 8190
+    for budgets in ([40, 15, 10], [20, 20, 10]):                 # 15 does not divide 40; budget[0] != T
+        with pytest.raises(H.HsaError) as e:
+            H.hsa_n_active(H.make_schedule(40, budgets, [1, 1, 1]), 0)
+        assert e.value.status == -7
+    with pytest.raises(H.HsaError):
+        H.hsa_n_active(s, 40)                                       # iteration out of range
+
+
+def test_entry_points_reject_bad_arguments_without_a_device():
+    L = H.load()
+    null = None
+    # null pointers / bad shapes come back as errors before any launch
+    assert L.hsa_euler(null, null, null, null, null, 10, 16, 0.1, 1e-6, 1, null) == -1
+    assert L.hsa_euler(null, null, null, null, null, 10, 15, 0.1, 1e-6, 1, null) == -2
+    assert L.hsa_attn_active(null, null, null, null, 4, 8, 2, 96, 0.1, 1, null, 0, null) == -2
+    assert L.hsa_attn_active(null, null, null, null, 4, 8, 2, 128, 0.1, 7, null, 0, null) == -3
+    assert L.hsa_attn_active(null, null, null, null, 4, 8, 2, 128, 0.1, 1, null, 0, null) == -1
+    assert L.hsa_linear(null, null, null, 4, 64, 100, 0, 1, null) == -2   # bf16 K % 64
+    assert L.hsa_linear(null, null, null, 4, 64, 128, 2, 1, null) == -1   # bad activation flag
+    counts = (ct.c_int32 * 3)(1, 2, 3)
+    assert L.hsa_select(null, 7, counts, 3, null, null, 0, null) == -1
+    assert L.hsa_step(null, null, null, 0, 1.0, 0.9, 0, null, null) == -1
+    # misaligned device pointer
+    assert L.hsa_layernorm(ct.c_void_p(0x1004), ct.c_void_p(0x2000), 4, 64, 1, null) == -4
+
+
+def test_step_rejects_bad_schedule_before_launch():
+    d = H.make_dims(256, 16, 128, 2, 64, 512, 1, 0, dtype=None)
+    d.dtype = H.HSA_F32
+    blocks = (H.Block * 1)()
+    for n in ("w_qkv", "w_o", "w_1", "w_2", "k_cache", "v_cache"):
+        setattr(blocks[0], n, 0x1000)
+    m = H.Model(d, 0x1000, 0x1000, blocks)
+    st = H.State(0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 1 << 40)
+    bad = H.make_schedule(8, [8, 4], [100, 100])      # counts do not sum to N
+    assert H.load().hsa_step(ct.byref(m), ct.byref(bad), ct.byref(st), 0, 1.0, 0.875, 0, None, None) == -7
+    ok = H.make_schedule(8, [8, 4], [128, 128])
+    st.workspace_bytes = 16                            # too small
+    assert H.load().hsa_step(ct.byref(m), ct.byref(ok), ct.byref(st), 0, 1.0, 0.875, 0, None, None) == -5
