@@ -15,6 +15,7 @@ Prints one JSON line.  `value` is HSA iterations per second.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -43,7 +44,66 @@ def parse():
     p.add_argument("--attn-reps", type=int, default=20)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=2048)
+    p.add_argument("--euler-tokens", type=int, default=1 << 24,
+                   help="tokens for the Euler-pass bandwidth measurement (>= 1 GiB working set)")
     return p.parse_args()
+
+
+ATTN_SRC = os.path.join(ROOT, "token_sparse_attention_compact_amd", "csrc", "attention.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_d128_n32760_a25_hbm_traffic.json")
+
+
+def source_hash(path: str) -> str:
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def recorded_traffic():
+    """HBM bytes per attention launch from the committed FETCH_SIZE/WRITE_SIZE
+    passes, only while the kernel source is the one those counters measured."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("attention_source_sha256_16") != source_hash(ATTN_SRC):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def calibration_copy():
+    """A plain device copy of exactly 256 MiB, run once before the timed region:
+    the reference dispatch for scaling HBM byte counters (FETCH_SIZE, WRITE_SIZE)."""
+    src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+
+
+def time_euler(H, n_tokens: int, C: int = 16, frac: float = 0.25, reps: int = 10):
+    """The fused Euler + v_hat + score kernel on a working set well past the
+    256 MB Infinity Cache: GB/s of algorithmic bytes."""
+    dev = "cuda"
+    nA = int(n_tokens * frac)
+    x = torch.randn((n_tokens, C), device=dev)
+    vh = torch.randn((n_tokens, C), device=dev)
+    sc = torch.rand((n_tokens,), device=dev)
+    vn = torch.randn((nA, C), device=dev)
+    pos = torch.full((n_tokens,), -1, dtype=torch.int32, device=dev)
+    act = torch.randperm(n_tokens, device=dev)[:nA].sort().values
+    pos[act] = torch.arange(nA, dtype=torch.int32, device=dev)
+    for _ in range(2):
+        H.hsa_euler(x, vh, sc, vn, pos, -0.025, True)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        H.hsa_euler(x, vh, sc, vn, pos, -0.025, True)
+    e.record()
+    torch.cuda.synchronize()
+    t = s.elapsed_time(e) / 1e3 / reps
+    nbytes = n_tokens * (4 + 3 * 4 * C) + nA * (2 * 4 * C + 4)
+    del x, vh, sc, vn, pos, act
+    return {"tokens": n_tokens, "active_frac": frac, "bytes": nbytes, "us": round(t * 1e6, 1),
+            "gbs": round(nbytes / t / 1e9, 1), "frac_of_hbm_peak": round(nbytes / t / 1e9 / PEAK_HBM_GBS, 4)}
 
 
 def device_inputs(c, H, seed_base):
@@ -162,6 +222,7 @@ def main():
     n_active = H.hsa_n_active(sched, ITER)
     sigma = synth.sigma_schedule(c.T)
     model, state = device_inputs(c, H, seed_base=3)
+    calibration_copy()
     torch.cuda.synchronize()
 
     elapsed = timed_steps(H, model, sched, state, sigma, args.steps, args.warmup)
@@ -196,8 +257,10 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "attn_bf16_d128_kernel",
                      "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "avg_launch_us": round(t_attn * 1e6, 2),
-                     "traffic": None},
+                     "traffic": recorded_traffic()},
     }
+    if args.euler_tokens > 0:
+        out["euler_hbm"] = time_euler(H, args.euler_tokens)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(c, args.cpu_rows)
     print(json.dumps(out), flush=True)
