@@ -20,6 +20,10 @@
 //    The V^T operand is read from the row-major V tile with the transposing
 //    LDS read ds_read_b64_tr_b16: per 16-lane group it takes a 4-key x
 //    16-dim block and gives lane i dim i of those 4 keys.
+//  * Inside each wavefront the loop is software-pipelined one tile deep: each
+//    S^T MFMA of tile t+1 is written next to the softmax work of two score
+//    elements of tile t, so the MFMA unit and the VALU work on different
+//    tiles at the same time.
 //  * exp2 with scale*log2(e) folded into one FMA; the running max is only
 //    raised (and O, l rescaled) when a tile's max exceeds it by more than 8,
 //    which is exact after the final division and keeps P <= 2^8.  Row sums
@@ -185,34 +189,11 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_d128_kernel(
   float l_run = 0.f;         // this lane's partial row sum
   const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
 
-  // Q in registers before the LDS pipeline starts (a builtin, so the compiler's own
-  // wait accounting sees it and adds no vmcnt waits for Q inside the loop)
-  __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0), expcnt/lgkmcnt unconstrained
-#pragma unroll
-  for (int st = 0; st < NST - 1; ++st)
-    if (st < ntiles)
-      issue_tile(k, v, kv_begin + st * BKV, nkv, D, h, sK_lds + st * TILEB, sV_lds + st * TILEB,
-                 voff_k, voff_v, wave);
-
-  for (int it = 0; it < ntiles; ++it) {
-    const int stage = it % NST;
-    // tile `it` landed (later tiles may still be in flight), visible to every wave;
-    // every wave is also done reading tile it-1, whose stage is refilled next
-    const int ahead = min(NST - 2, ntiles - 1 - it);
-    if (ahead >= 2) wait_tiles_barrier<2>();
-    else if (ahead == 1) wait_tiles_barrier<1>();
-    else wait_tiles_barrier<0>();
-    if (it + NST - 1 < ntiles) {
-      const int ns = (it + NST - 1) % NST;
-      issue_tile(k, v, kv_begin + (it + NST - 1) * BKV, nkv, D, h, sK_lds + ns * TILEB,
-                 sV_lds + ns * TILEB, voff_k, voff_v, wave);
-    }
-    const int32_t base = kv_begin + it * BKV;
+  // ---- phases of one tile
+  // S^T = K Q^T for 64 keys x 32 queries: two 32x32 blocks;
+  // s[kb][r] <-> key kb*32 + 8*(r/4) + 4*half + r%4 of the tile, query l32
+  auto scores = [&](int stage, f32x16* s) {
     const char* kt = sK + stage * TILEB;
-    const char* vt = sV + stage * TILEB;
-
-    // ---- S^T = K Q^T for 64 keys x 32 queries: two 32x32 blocks
-    f32x16 s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -223,7 +204,10 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_d128_kernel(
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[dk], s[kb], 0, 0, 0);
       }
     }
-    // s[kb][r] <-> key base + kb*32 + 8*(r/4) + 4*half + r%4, query l32
+  };
+  // mask keys past the end (partial last tile only), raise the running max
+  // lazily and rescale O and l when it moves
+  auto prepare = [&](f32x16* s, int32_t base) {
     if (base + BKV > kv_end) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -254,7 +238,9 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_d128_kernel(
         for (int r = 0; r < 16; ++r) acc_o[db][r] *= alpha;
       m_run = m_new;
     }
-    bf16x8 pb[4];
+  };
+  // P^T = exp2(S^T c - m) as bf16 MFMA fragments, row sums over the same bf16 P
+  auto probs = [&](const f32x16* s, bf16x8* pb) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -270,8 +256,10 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_d128_kernel(
           l_run = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, l_run, false);
         }
       }
-
-    // ---- O^T += V^T P^T: k-step ts = (kb, jp) covers keys kb*32 + 16*jp + 4*half + {0..3, 8..11}
+  };
+  // O^T += V^T P^T: k-step ts = (kb, jp) covers keys kb*32 + 16*jp + 4*half + {0..3, 8..11}
+  auto accumulate = [&](int stage, const bf16x8* pb) {
+    const char* vt = sV + stage * TILEB;
 #pragma unroll
     for (int ts = 0; ts < 4; ++ts) {
       const int kb = ts >> 1, jp = ts & 1;
@@ -286,6 +274,100 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_d128_kernel(
                                                              acc_o[db], 0, 0, 0);
       }
     }
+  };
+
+  // Q in registers before the LDS pipeline starts (a builtin, so the compiler's own
+  // wait accounting sees it and adds no vmcnt waits for Q inside the loop)
+  __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0), expcnt/lgkmcnt unconstrained
+#pragma unroll
+  for (int st = 0; st < NST - 1; ++st)
+    if (st < ntiles)
+      issue_tile(k, v, kv_begin + st * BKV, nkv, D, h, sK_lds + st * TILEB, sV_lds + st * TILEB,
+                 voff_k, voff_v, wave);
+
+  // Software pipeline, one tile deep inside each wavefront, written slot by
+  // slot: 16 slots each issue one S^T MFMA of tile it+1 (alternating between
+  // the two accumulator blocks, its K fragment read two slots earlier) next to
+  // the softmax of two score elements of tile it; then 16 slots each issue one
+  // PV MFMA of tile it (its V^T fragments read one slot earlier).  The LDS ring
+  // keeps tiles it and it+1 resident (one more in flight) and refills the
+  // stage of tile it-1.
+  auto step = [&](f32x16* s_cur, f32x16* s_nxt, int it) {
+    prepare(s_cur, kv_begin + it * BKV);
+    // tile it+1 landed (tile it+2 may still be in flight); every wave finished
+    // tile it-1, whose stage is refilled now
+    if (it + 2 < ntiles) wait_tiles_barrier<1>();
+    else wait_tiles_barrier<0>();
+    if (it + NST - 1 < ntiles) {
+      const int ns = (it + NST - 1) % NST;
+      issue_tile(k, v, kv_begin + (it + NST - 1) * BKV, nkv, D, h, sK_lds + ns * TILEB,
+                 sV_lds + ns * TILEB, voff_k, voff_v, wave);
+    }
+    const char* kt = sK + ((it + 1) % NST) * TILEB;
+    const char* vt = sV + (it % NST) * TILEB;
+    auto kfrag = [&](int j) {   // slot j: block kb = j%2, dims dk = j/2
+      return *reinterpret_cast<const bf16x8*>(kt + (j & 1) * 32 * ROWB + koff[j >> 1]);
+    };
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s_nxt[kb][r] = 0.f;
+    bf16x8 kf[3];
+    kf[0] = kfrag(0);
+    kf[1] = kfrag(1);
+    u32x4 pw[4];   // P^T fragments as packed bf16 pairs
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (j + 2 < 16) kf[(j + 2) % 3] = kfrag(j + 2);
+      s_nxt[j & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[j % 3], qf[j >> 1], s_nxt[j & 1], 0, 0, 0);
+      // score elements q = 2j, 2j+1 of tile it: block q/16, accumulator q%16
+      const int q = 2 * j;
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[q >> 4][q & 15], c, -m_run));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[q >> 4][(q & 15) + 1], c, -m_run));
+      const bf16x2 pr = {(bf16)p0, (bf16)p1};
+      pw[q >> 3][(q & 7) >> 1] = __builtin_bit_cast(uint32_t, pr);
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run, false);
+    }
+    auto vfrag = [&](int j) {   // slot j: k-step ts = j/4 (kb = ts/2, jp = ts%2), dims block db = j%4
+      const int ts = j >> 2, db = j & 3;
+      const char* vk = vt + ((ts >> 1) * 32 + 16 * (ts & 1)) * ROWB;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vk + voffr[db]));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vk + 8 * ROWB + voffr[db]));
+      const u32x4 raw = {__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
+                         __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]};
+      return __builtin_bit_cast(bf16x8, raw);
+    };
+    bf16x8 vf[2];
+    vf[0] = vfrag(0);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (j + 1 < 16) vf[(j + 1) & 1] = vfrag(j + 1);
+      acc_o[j & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[j & 1], __builtin_bit_cast(bf16x8, pw[j >> 2]),
+                                                             acc_o[j & 3], 0, 0, 0);
+    }
+  };
+
+  f32x16 sa[2], sb[2];
+  if (min(NST - 2, ntiles - 1) >= 2) wait_tiles_barrier<2>();
+  else if (ntiles - 1 >= 1) wait_tiles_barrier<1>();
+  else wait_tiles_barrier<0>();
+  scores(0, sa);
+  auto last = [&](f32x16* s_cur, int it) {   // no next tile to overlap
+    bf16x8 pb[4];
+    prepare(s_cur, kv_begin + it * BKV);
+    probs(s_cur, pb);
+    accumulate(it % NST, pb);
+  };
+  int it = 0;
+  for (; it + 2 < ntiles; it += 2) {
+    step(sa, sb, it);
+    step(sb, sa, it + 1);
+  }
+  if (it + 1 < ntiles) {
+    step(sa, sb, it);
+    last(sb, it + 1);
+  } else {
+    last(sa, it);
   }
 
   float l_tot;
@@ -501,3 +583,4 @@ hsa_status launch_attention(const void* q, const void* k, const void* v, void* o
 }
 
 }  // namespace hsa
+

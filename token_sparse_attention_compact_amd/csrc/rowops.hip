@@ -80,6 +80,40 @@ __global__ __launch_bounds__(256) void embed_kernel(const float* __restrict__ x,
   h[t] = acc;
 }
 
+// C == 16: each lane produces 4 consecutive outputs of one row from the
+// latent row (4 x float4, shared by the row's lanes through the cache) and
+// four 16-channel weight rows, so the pass is a handful of vector loads per
+// output quad instead of 32 scalar loads per output.
+template <typename WT>
+__global__ __launch_bounds__(256) void embed_kernel_c16(const float* __restrict__ x,
+                                                        const int32_t* __restrict__ idx,
+                                                        const WT* __restrict__ w_in,
+                                                        float* __restrict__ h, int32_t rows,
+                                                        int32_t D) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int32_t quads = D / 4;
+  if (t >= (int64_t)rows * quads) return;
+  const int32_t j = (int32_t)(t / quads), d0 = (int32_t)(t % quads) * 4;
+  const f32x4* xr = reinterpret_cast<const f32x4*>(x + (size_t)idx[j] * 16);
+  float xv[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f32x4 v = xr[i];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) xv[4 * i + e] = v[e];
+  }
+  f32x4 out;
+#pragma unroll
+  for (int o = 0; o < 4; ++o) {
+    const WT* wr = w_in + (size_t)(d0 + o) * 16;
+    float acc = 0.f;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) acc = __builtin_fmaf(xv[c], to_f32(wr[c]), acc);
+    out[o] = acc;
+  }
+  *reinterpret_cast<f32x4*>(h + (size_t)j * D + d0) = out;
+}
+
 // v_new[j][c] = sum_d LN(h[j])[d] * w_out[c][d], C == CC known at compile time.
 template <typename WT, int CC>
 __global__ __launch_bounds__(256) void unembed_kernel(const float* __restrict__ h,
@@ -159,6 +193,15 @@ hsa_status launch_layernorm(const float* h, void* out, int32_t rows, int32_t D, 
 hsa_status launch_embed(const float* x, const int32_t* idx, const void* w_in, float* h,
                         int32_t rows, int32_t C, int32_t D, hsa_dtype dt, hipStream_t s) {
   if (rows == 0) return HSA_OK;
+  if (C == 16 && D % 4 == 0) {
+    const int64_t total = (int64_t)rows * (D / 4);
+    const unsigned blocks = (unsigned)((total + 255) / 256);
+    if (dt == HSA_BF16)
+      embed_kernel_c16<bf16><<<blocks, 256, 0, s>>>(x, idx, (const bf16*)w_in, h, rows, D);
+    else
+      embed_kernel_c16<float><<<blocks, 256, 0, s>>>(x, idx, (const float*)w_in, h, rows, D);
+    return launch_status();
+  }
   const int64_t total = (int64_t)rows * D;
   const unsigned blocks = (unsigned)((total + 255) / 256);
   if (dt == HSA_BF16)
