@@ -43,6 +43,7 @@ def parse():
     p.add_argument("--blocks", type=int, default=30, help="number of blocks (the workload uses 30)")
     p.add_argument("--attn-reps", type=int, default=20)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-scaling", action="store_true", help="skip the iteration-time vs active-fraction sweep")
     p.add_argument("--cpu-rows", type=int, default=2048)
     p.add_argument("--euler-tokens", type=int, default=1 << 24,
                    help="tokens for the Euler-pass bandwidth measurement (>= 1 GiB working set)")
@@ -173,6 +174,36 @@ def time_attention(H, model, c, n_active, reps):
     return start.elapsed_time(end) / 1e3 / reps
 
 
+def step_scaling(H, model, state, c, sigma, reps: int = 5):
+    """Iteration time against the active fraction: hsa_step (no regroup) at
+    |A|/N = 1, 0.5, 0.25 (iterations 0, 2, 1 of the 25/25/50 schedule) and
+    0.0625 (a schedule whose full-budget group holds 2048 tokens, odd
+    iteration); least-squares fit t(f) = t0 + b f."""
+    N = c.N
+    cases = [(1.0, c.counts(), 0), (0.5, c.counts(), 2), (0.25, c.counts(), 1),
+             (0.0625, [2048, 10240, N - 12288], 1)]
+    fr, ms = [], []
+    for f, counts, it in cases:
+        sched = H.make_schedule(c.T, c.budgets, counts)
+        assert H.hsa_n_active(sched, it) == round(f * N)
+        for _ in range(2):
+            H.hsa_step(model, sched, state, it, float(sigma[it]), float(sigma[it + 1]), False)
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(reps):
+            H.hsa_step(model, sched, state, it, float(sigma[it]), float(sigma[it + 1]), False)
+        e.record()
+        torch.cuda.synchronize()
+        fr.append(f)
+        ms.append(s.elapsed_time(e) / reps)
+    b, t0 = np.polyfit(np.array(fr), np.array(ms), 1)
+    pred = t0 + b * np.array(fr)
+    return {"active_frac": fr, "ms_per_step": [round(x, 2) for x in ms], "fit_t0_ms": round(float(t0), 2),
+            "fit_slope_ms": round(float(b), 2),
+            "fit_max_rel_residual": round(float(np.max(np.abs(pred - ms) / np.array(ms))), 4)}
+
+
 def cpu_baseline(c, rows: int):
     """The oracle on a bounded sample of the same iteration: one block with `rows`
     active tokens over all N cached rows (its cost is linear in the number of
@@ -261,6 +292,8 @@ def main():
     }
     if args.euler_tokens > 0:
         out["euler_hbm"] = time_euler(H, args.euler_tokens)
+    if not args.no_scaling:
+        out["scaling_with_active_fraction"] = step_scaling(H, model, state, c, sigma)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(c, args.cpu_rows)
     print(json.dumps(out), flush=True)

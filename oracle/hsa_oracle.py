@@ -404,3 +404,20 @@ def dense_euler_sample(model: Model, x0: np.ndarray, sigma: np.ndarray, T: int) 
         v = dense_velocity(model, x)
         x = round_to_f32(x + np.float64(dsigma_f32(sigma[i], sigma[i + 1])) * v)
     return x
+
+
+def field_iteration(sched: Schedule, state: State, i: int, sigma_i: float, sigma_next: float,
+                    regroup: bool, v_field: np.ndarray) -> Dict[str, np.ndarray]:
+    """One iteration of the sampler state when a velocity field [N][C] replaces
+    the model's prediction in the Euler/score path: regroup (section 2.1) ->
+    A_i -> cached Euler with v_new = v_field[A_i] (section 2.3).  The model's
+    caches are not touched here; x, v_hat, score and group evolve exactly as
+    in hsa_iteration with the same v_field."""
+    if regroup:
+        state.group = select_groups(state.score, sched.counts)
+    idx, pos = active_set(state.group, sched.budgets, sched.T, i, sched.m)
+    v_new = np.asarray(v_field, np.float64)[idx]
+    state.x, state.v_hat, state.score = euler_update(
+        state.x, state.v_hat, state.score, v_new, idx, dsigma_f32(sigma_i, sigma_next),
+        update_score=(i >= 1))
+    return {"active_idx": idx, "pos": pos, "v_new": v_new}

@@ -386,3 +386,33 @@ def test_config_counts_exact():
     assert synth.CONFIGS[5].counts() == [4095, 12285, 16380]
     assert synth.n_active_for_fraction(32760, 0.0625) == 2048
     assert synth.n_active_for_fraction(32760, 0.05) == 1638
+
+
+def test_field_iteration_matches_full_iteration_with_field():
+    # With a velocity field in place of the model, the sampler state does not depend on the model.
+    c = _tiny_cfg(budgets=(8, 4, 2), shares=(0.25, 0.25, 0.5), L=1)
+    m = _model(c)
+    sched = O.Schedule(T=8, budgets=[8, 4, 2], counts=c.counts(), regroup=(3, 5))
+    sigma = synth.sigma_schedule(8)
+    rs = np.random.default_rng(12)
+    fields = [rs.standard_normal((c.N, c.C)) for _ in range(8)]
+    a = O.init_state(m.dims, synth.x0(c), synth.group0(c))
+    b = a.copy()
+    for i in range(8):
+        O.hsa_iteration(m, sched, a, i, sigma[i], sigma[i + 1], i in (3, 5), v_field=fields[i])
+        O.field_iteration(sched, b, i, sigma[i], sigma[i + 1], i in (3, 5), fields[i])
+        np.testing.assert_array_equal(a.x, b.x)
+        np.testing.assert_array_equal(a.group, b.group)
+        np.testing.assert_array_equal(a.score, b.score)
+
+
+def test_churn_field_shape_and_blob():
+    c = synth.CONFIGS[5]
+    f = synth.ChurnField(c)
+    blob = f.blob(3)
+    assert blob.size == 21 * 234                      # 15% of 32760 tokens
+    v3, v4 = f(3), f(4)
+    bg = np.setdiff1d(np.arange(c.N), np.union1d(f.blob(3), f.blob(4)))
+    # background changes by (1 + 0.002*4)/(1 + 0.002*3) - 1 ~ 0.2% per step
+    r = np.abs(v4[bg] - v3[bg]).sum(1) / np.abs(v3[bg]).sum(1)
+    np.testing.assert_allclose(r, 0.002 / 1.006, rtol=1e-4)
