@@ -11,7 +11,9 @@
 // each 16-byte chunk at an XOR-swizzled position of its 128-byte row so the
 // operand reads hit distinct banks.  The next stage's loads are in flight
 // while the current one feeds the MFMAs.  Epilogues are fused (store / GELU /
-// residual add / QKV scatter).
+// residual add / QKV scatter) and work on quads of 4 consecutive output
+// columns: the MFMA computes C^T blocks (w rows as MFMA rows), whose
+// accumulator layout gives each lane runs of 4 consecutive columns of a row.
 //
 // float32 path (small float32 workloads): LDS-tiled FMA GEMM, 64x64 tiles.
 #include "common.h"
@@ -40,6 +42,40 @@ __device__ __forceinline__ void epilogue(const EpiArgs& ep, int32_t N, int32_t r
       T* dst = reinterpret_cast<T*>(which == 1 ? ep.kc : ep.vc);
       dst[r * D + c] = from_f32<T>(v);
     }
+  }
+}
+
+// Epilogue on 4 consecutive output columns col..col+3 of one row (N % 4 == 0).
+__device__ __forceinline__ float gelu_fast(float u) {
+  const float z = 0.7978845608028654f * (u + 0.044715f * u * u * u);
+  return u * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-2.0f * kLog2e * z));
+}
+
+template <int EPI>
+__device__ __forceinline__ void epilogue4(const EpiArgs& ep, int32_t N, int32_t row, int32_t col,
+                                          f32x4 v) {
+  if constexpr (EPI == EPI_STORE || EPI == EPI_GELU) {
+    bf16x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = (bf16)(EPI == EPI_GELU ? gelu_fast(v[e]) : v[e]);
+    *reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(ep.out) + (size_t)row * N + col) = o;
+  } else if constexpr (EPI == EPI_RESID) {
+    f32x4* p = reinterpret_cast<f32x4*>(ep.resid + (size_t)row * N + col);
+    f32x4 h = *p;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) h[e] += v[e];
+    *p = h;
+  } else {  // EPI_QKV_SCATTER: D % 4 == 0, so the 4 columns stay in one of q, k, v
+    const int32_t D = ep.D;
+    const int32_t which = col / D;
+    const int32_t c = col - which * D;
+    bf16x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = (bf16)v[e];
+    bf16* dst;
+    if (which == 0) dst = reinterpret_cast<bf16*>(ep.out) + (size_t)row * D + c;
+    else dst = reinterpret_cast<bf16*>(which == 1 ? ep.kc : ep.vc) + (size_t)ep.idx[row] * D + c;
+    *reinterpret_cast<bf16x4*>(dst) = o;
   }
 }
 
@@ -215,21 +251,27 @@ __global__ __launch_bounds__(G::THREADS, 2) void gemm_bf16_kernel(
 #pragma unroll
       for (int i = 0; i < G::FM; ++i)
 #pragma unroll
-        for (int j = 0; j < G::FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < G::FN; ++j)   // C^T block: w rows as MFMA rows, a rows as columns
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
     }
   }
 
-  // acc[i][j][r]: row 8*(r/4) + 4*(lane/32) + r%4, column lane%32 of block (i, j).
+  // acc[i][j][r] = C[row][col] with row = block (i) row l32 and col = block (j)
+  // column 8*(r/4) + 4*(lane/32) + r%4: each quad r = 4g..4g+3 is 4 consecutive
+  // columns of one row, stored with one 8- or 16-byte access.
+  const int32_t row = m0 + wm * G::TM + l32;
 #pragma unroll
   for (int i = 0; i < G::FM; ++i)
 #pragma unroll
     for (int j = 0; j < G::FN; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int32_t row = m0 + wm * G::TM + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-        const int32_t col = n0 + wn * G::TN + j * 32 + l32;
-        if (row < M && col < N) epilogue<EPI, bf16>(ep, N, row, col, acc[i][j][r]);
+      for (int g = 0; g < 4; ++g) {
+        const int32_t r = row + i * 32;
+        const int32_t col = n0 + wn * G::TN + j * 32 + 8 * g + 4 * half;
+        if (r < M && col < N) {
+          const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+          epilogue4<EPI>(ep, N, r, col, v);
+        }
       }
 }
 
@@ -297,6 +339,7 @@ template <int EPI>
 hsa_status run(const void* a, const void* w, int32_t M, int32_t N, int32_t K, hsa_dtype dt,
                const EpiArgs& ep, hipStream_t s) {
   if (dt == HSA_BF16) {
+    if (N % 4 != 0 || (EPI == EPI_QKV_SCATTER && ep.D % 4 != 0)) return HSA_ERR_SHAPE;
     launch_bf16<CfgMain, EPI>(a, w, M, N, K, ep, s);
   } else {
     dim3 grid(cdiv(N, FT), cdiv(M, FT));
