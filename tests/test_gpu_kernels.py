@@ -298,6 +298,49 @@ def test_attention_closed_forms_bf16():
     np.testing.assert_allclose(host(o), np.broadcast_to(c, (5, Hh * Dh)), rtol=8e-3, atol=1e-6)
 
 
+def _softmax_range_case(pattern, nA, nkv, Hh=2, Dh=128, seed=5):
+    """Inputs whose score maxima move far from where the first keys put them."""
+    rs = np.random.default_rng(seed)
+    D = Hh * Dh
+    q = rs.standard_normal((nA, D))
+    k = rs.standard_normal((nkv, D))
+    v = rs.standard_normal((nkv, D))
+    u = rs.standard_normal(D)
+    u /= np.linalg.norm(u)
+    if pattern == "spike":
+        # a few keys far past the first tile align with every query: scores
+        # ~ 4 * 200 / 2 heads = 400 above the rest (about 50 in log2 units)
+        q += 4.0 * u
+        for j in (nkv // 2 + 7, nkv - 3):
+            k[j] += 200.0 * u
+    elif pattern == "ramp":
+        # key norms grow 9x along the cache: the row max keeps rising
+        k *= (1.0 + 8.0 * np.arange(nkv) / nkv)[:, None]
+        q *= 3.0
+    elif pattern == "negative":
+        # every score ~ -1600 (about -200 in log2 units): exp2 of the raw
+        # scores would underflow; the probabilities are relative to the max
+        q += 8.0 * u
+        k -= 400.0 * u
+    return bf(q), bf(k), bf(v)
+
+
+@pytest.mark.parametrize("pattern", ["spike", "ramp", "negative"])
+@pytest.mark.parametrize("nA,nkv", [(70, 5000), (300, 2113), (1, 9000)])
+def test_attention_softmax_reference_moves(pattern, nA, nkv):
+    """The running max is taken from the first keys and raised only when a
+    later tile's probabilities grow far above 1: spikes, ramps and uniformly
+    very negative scores against the oracle (several KV splits included)."""
+    say(f"attention softmax range {pattern} nA={nA} nkv={nkv}")
+    Hh, Dh = 2, 128
+    q, k, v = _softmax_range_case(pattern, nA, nkv, Hh, Dh)
+    o = torch.empty(nA, Hh * Dh, dtype=torch.bfloat16, device=DEV)
+    H.hsa_attn_active(dev(q, torch.bfloat16), dev(k, torch.bfloat16), dev(v, torch.bfloat16), o, Hh, Dh)
+    out = host(o)
+    assert np.all(np.isfinite(out))
+    assert rel_l2(out, O.attention(q, k, v, Hh, Dh)) < TOL_BF16
+
+
 @pytest.mark.parametrize("frac", [0.25, 0.0625, 1.0])
 def test_attention_full_size_sampled_rows(frac):
     """Wan-1.3B-shaped layer: N = 32760 cached rows, 12 heads x 128, the launch

@@ -20,14 +20,22 @@
 //    The V^T operand is read from the row-major V tile with the transposing
 //    LDS read ds_read_b64_tr_b16: per 16-lane group it takes a 4-key x
 //    16-dim block and gives lane i dim i of those 4 keys.
-//  * Inside each wavefront the loop is software-pipelined one tile deep: each
-//    S^T MFMA of tile t+1 is written next to the softmax work of two score
-//    elements of tile t, so the MFMA unit and the VALU work on different
-//    tiles at the same time.
-//  * exp2 with scale*log2(e) folded into one FMA; the running max is only
-//    raised (and O, l rescaled) when a tile's max exceeds it by more than 8,
-//    which is exact after the final division and keeps P <= 2^8.  Row sums
-//    use v_dot2 over the bf16 P that also feeds the MFMA.
+//  * Inside each wavefront the loop is software-pipelined over 32-key
+//    sub-tiles (two per LDS tile): one step issues the S^T MFMAs of sub-tile
+//    u+1 and the PV MFMAs of sub-tile u-1 alternately, with the softmax of
+//    sub-tile u spread between them, so the MFMA unit always has independent
+//    work while the VALU turns scores into probabilities.  One 32x32 score
+//    block per sub-tile keeps the live registers within the 256 a wave may
+//    hold at two waves per SIMD.
+//  * Softmax in log2 units with little VALU work per score: Q is pre-scaled
+//    by scale*log2(e) and each S^T accumulator is seeded with minus the
+//    running max, so the MFMA itself yields s = c q.k - m and a probability
+//    is one exp2 (plus a pack to bf16 shared by two).  The running max is
+//    taken from the first sub-tile and raised only when a later one's
+//    row-sum partial shows a probability far above 1 (no per-score max);
+//    O and l are then rescaled, which is exact after the final division.
+//    Row sums are float32 adds (v_dot2 over the packed pairs would be fewer
+//    instructions but holds up the MFMA issue far more).
 //  * When |A_i| is small the KV range is split across workgroups; partial
 //    (O, max, sum) are merged in a fixed split order (deterministic).
 //  * Workgroup ids are remapped so each XCD runs a contiguous range of
@@ -46,13 +54,16 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 constexpr int NW = 8;                      // wavefronts per workgroup
 constexpr int kAttnThreads = NW * 64;
 constexpr int DH = 128;
-constexpr int BKV = 64;                    // keys per tile
+constexpr int BKV = 64;                    // keys per tile (LDS stage)
+constexpr int SUB = 32;                    // keys per sub-tile (one S^T MFMA block)
 constexpr int BQ = NW * 32;                // queries per workgroup
 constexpr int NST = 4;                     // LDS stages
 constexpr int ROWB = DH * 2;               // bytes per K/V row of one head (256)
 constexpr int TILEB = BKV * ROWB;          // 16 KiB per K or V tile
 constexpr int LOADS = TILEB / 16 / kAttnThreads;   // 16-byte loads per lane per tile and operand (2)
-constexpr float kRescaleSlack = 8.0f;      // log2 units
+// Largest row-sum partial (32 probabilities of one query in one lane) a tile may
+// reach before the running max is raised: it bounds every probability by 2^32.
+constexpr float kRaiseSum = 4294967296.0f;
 
 __device__ __forceinline__ int32_t xcd_remap(int32_t bid, int32_t total) {
   constexpr int32_t kXcd = 8;
@@ -157,12 +168,16 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_d128_kernel(
   // ---- Q^T fragments (B operand): lane = query column, 8 consecutive dims
   const int32_t qi = qt * BQ + wave * 32 + l32;
   const bool q_ok = qi < nA;
+  // pre-multiplied by c = scale * log2(e), so the MFMA yields scores in log2 units
   bf16x8 qf[DH / 16];
   {
     const bf16* qrow = q + (size_t)(q_ok ? qi : nA - 1) * D + h * DH + half * 8;
 #pragma unroll
-    for (int dk = 0; dk < DH / 16; ++dk)
-      qf[dk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + dk * 16));
+    for (int dk = 0; dk < DH / 16; ++dk) {
+      const bf16x8 raw = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + dk * 16));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[dk][e] = (bf16)((float)raw[e] * c);
+    }
   }
 
   // ---- per-lane LDS read offsets
@@ -185,96 +200,97 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_d128_kernel(
   for (int db = 0; db < DH / 32; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc_o[db][r] = 0.f;
-  float m_run = -INFINITY;   // running max, log2 units (scaled)
+  float m_run;               // running max of this lane's query, log2 units
   float l_run = 0.f;         // this lane's partial row sum
-  const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+  f32x16 negm;               // -m_run in every element: the seed of each S^T accumulator
+  auto set_negm = [&]() {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) negm[r] = -m_run;
+  };
 
-  // ---- phases of one tile
-  // S^T = K Q^T for 64 keys x 32 queries: two 32x32 blocks;
-  // s[kb][r] <-> key kb*32 + 8*(r/4) + 4*half + r%4 of the tile, query l32
-  auto scores = [&](int stage, f32x16* s) {
-    const char* kt = sK + stage * TILEB;
+  // ---- phases of one sub-tile (32 keys: half hb of a 64-key LDS stage)
+  // Scores are held relative to the running max: s = c q.k - m_run, which the
+  // MFMA produces directly from an accumulator seeded with -m_run.
+  // s[r] <-> key 8*(r/4) + 4*half + r%4 of the sub-tile, query l32.
+  auto kfrag = [&](const char* kt, int dk) {
+    return *reinterpret_cast<const bf16x8*>(kt + koff[dk]);
+  };
+  // keys past the end of this split's range (its last sub-tile only) get -inf
+  auto mask_tail = [&](f32x16& s, int32_t base) {
+    if (base + SUB > kv_end) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-#pragma unroll
-      for (int dk = 0; dk < DH / 16; ++dk) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kt + kb * 32 * ROWB + koff[dk]);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[dk], s[kb], 0, 0, 0);
+      for (int r = 0; r < 16; ++r) {
+        const int32_t key = base + 8 * (r >> 2) + 4 * half + (r & 3);
+        if (key >= kv_end) s[r] = -INFINITY;
       }
     }
   };
-  // mask keys past the end (partial last tile only), raise the running max
-  // lazily and rescale O and l when it moves
-  auto prepare = [&](f32x16* s, int32_t base) {
-    if (base + BKV > kv_end) {
+  // this query's max over the sub-tile (the two lane halves hold half of its keys each)
+  auto tile_max = [&](const f32x16& s) {
+    float mx = fmaxf(s[0], s[1]);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+    for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+    return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+  };
+  // The running max is not tracked per sub-tile: one whose scores rise far
+  // above it shows in its row-sum partial (> kRaiseSum), and only then is the
+  // max raised to the sub-tile's, with O, l and the (already shifted) scores
+  // of this sub-tile and of the next one moved to the new reference.  Exact
+  // after the final division; every probability stays <= 2^32.
+  auto raise = [&](f32x16& s_cur, f32x16* s_nxt) {
+    const float d = fmaxf(tile_max(s_cur), 0.f);
+    const float alpha = __builtin_amdgcn_exp2f(-d);
+    m_run += d;
+    l_run *= alpha;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int32_t key = base + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          if (key >= kv_end) s[kb][r] = -INFINITY;
-        }
+    for (int db = 0; db < DH / 32; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc_o[db][r] *= alpha;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s_cur[r] -= d;
+      if (s_nxt != nullptr) (*s_nxt)[r] -= d;
     }
-    float mx = fmaxf(s[0][0], s[0][1]);
+    set_negm();
+  };
+  // P^T = exp2(s) as bf16 MFMA fragments (packed pairs); row-sum partial in
+  // float32 over two independent chains
+  auto probs = [&](const f32x16& s, u32x4* pw) {
+    float l2[2] = {0.f, 0.f};
 #pragma unroll
-    for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
-    {
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    for (int r = 0; r < 16; r += 2) {
+      const float p0 = __builtin_amdgcn_exp2f(s[r]);
+      const float p1 = __builtin_amdgcn_exp2f(s[r + 1]);
+      const bf16x2 pr = {(bf16)p0, (bf16)p1};
+      pw[r >> 3][(r & 7) >> 1] = __builtin_bit_cast(uint32_t, pr);
+      l2[(r >> 1) & 1] += p0 + p1;
     }
-    const float mxs = mx * c;
-    const bool need = mxs > m_run + kRescaleSlack;
-    if (__ballot(need) != 0ull) {
-      const float m_new = need ? mxs : m_run;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
+    return l2[0] + l2[1];
+  };
+  // O^T += V^T P^T over the sub-tile: k-step jp covers keys 16*jp + 4*half + {0..3, 8..11}
+  auto vfrag = [&](const char* vt, int j) {   // j: k-step jp = j/4, dims block db = j%4
+    const int jp = j >> 2, db = j & 3;
+    const char* vk = vt + 16 * jp * ROWB;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vk + voffr[db]));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vk + 8 * ROWB + voffr[db]));
+    const u32x4 raw = {__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
+                       __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]};
+    return __builtin_bit_cast(bf16x8, raw);
+  };
+  auto accumulate = [&](const char* vt, const u32x4* pw) {
+    bf16x8 vf[2];
+    vf[0] = vfrag(vt, 0);
 #pragma unroll
-      for (int db = 0; db < DH / 32; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc_o[db][r] *= alpha;
-      m_run = m_new;
+    for (int j = 0; j < 8; ++j) {
+      if (j + 1 < 8) vf[(j + 1) & 1] = vfrag(vt, j + 1);
+      acc_o[j & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[j & 1], __builtin_bit_cast(bf16x8, pw[j >> 2]),
+                                                             acc_o[j & 3], 0, 0, 0);
     }
   };
-  // P^T = exp2(S^T c - m) as bf16 MFMA fragments, row sums over the same bf16 P
-  auto probs = [&](const f32x16* s, bf16x8* pb) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int jp = 0; jp < 2; ++jp) {
-        bf16x8 pv;
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          pv[e] = (bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][jp * 8 + e], c, -m_run));
-        pb[kb * 2 + jp] = pv;
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const bf16x2 pair = {pv[e], pv[e + 1]};
-          l_run = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, l_run, false);
-        }
-      }
-  };
-  // O^T += V^T P^T: k-step ts = (kb, jp) covers keys kb*32 + 16*jp + 4*half + {0..3, 8..11}
-  auto accumulate = [&](int stage, const bf16x8* pb) {
-    const char* vt = sV + stage * TILEB;
-#pragma unroll
-    for (int ts = 0; ts < 4; ++ts) {
-      const int kb = ts >> 1, jp = ts & 1;
-      const char* vk = vt + (kb * 32 + 16 * jp) * ROWB;
-#pragma unroll
-      for (int db = 0; db < DH / 32; ++db) {
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vk + voffr[db]));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vk + 8 * ROWB + voffr[db]));
-        const u32x4 raw = {__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
-                           __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]};
-        acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, raw), pb[ts],
-                                                             acc_o[db], 0, 0, 0);
-      }
-    }
-  };
+  // LDS addresses of sub-tile u's K and V rows
+  auto k_sub = [&](int u) { return sK + ((u >> 1) % NST) * TILEB + (u & 1) * SUB * ROWB; };
+  auto v_sub = [&](int u) { return sV + ((u >> 1) % NST) * TILEB + (u & 1) * SUB * ROWB; };
 
   // Q in registers before the LDS pipeline starts (a builtin, so the compiler's own
   // wait accounting sees it and adds no vmcnt waits for Q inside the loop)
@@ -285,89 +301,109 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_d128_kernel(
       issue_tile(k, v, kv_begin + st * BKV, nkv, D, h, sK_lds + st * TILEB, sV_lds + st * TILEB,
                  voff_k, voff_v, wave);
 
-  // Software pipeline, one tile deep inside each wavefront, written slot by
-  // slot: 16 slots each issue one S^T MFMA of tile it+1 (alternating between
-  // the two accumulator blocks, its K fragment read two slots earlier) next to
-  // the softmax of two score elements of tile it; then 16 slots each issue one
-  // PV MFMA of tile it (its V^T fragments read one slot earlier).  The LDS ring
-  // keeps tiles it and it+1 resident (one more in flight) and refills the
-  // stage of tile it-1.
-  auto step = [&](f32x16* s_cur, f32x16* s_nxt, int it) {
-    prepare(s_cur, kv_begin + it * BKV);
-    // tile it+1 landed (tile it+2 may still be in flight); every wave finished
-    // tile it-1, whose stage is refilled now
-    if (it + 2 < ntiles) wait_tiles_barrier<1>();
-    else wait_tiles_barrier<0>();
-    if (it + NST - 1 < ntiles) {
-      const int ns = (it + NST - 1) % NST;
-      issue_tile(k, v, kv_begin + (it + NST - 1) * BKV, nkv, D, h, sK_lds + ns * TILEB,
-                 sV_lds + ns * TILEB, voff_k, voff_v, wave);
+  // Software pipeline inside each wavefront over 32-key sub-tiles: step u
+  // issues the 8 S^T MFMAs of sub-tile u+1 and the 8 PV MFMAs of sub-tile
+  // u-1 alternately, with the exp2 / pack / row sum of one score element of
+  // sub-tile u next to each, so the VALU work is spread evenly over the MFMA
+  // stream.  Before the first sub-tile of a stage is scored, the workgroup
+  // synchronises: that stage has landed and every wave is done with the
+  // stage two back, which is refilled with the next tile.  The LDS ring keeps
+  // two stages resident and two in flight.
+  auto step = [&](f32x16& s_cur, f32x16& s_nxt, u32x4* pw_cur, const u32x4* pw_prev, int u,
+                  bool pv) {
+    if (u & 1) {
+      const int it = u >> 1;   // stage of sub-tile u; sub-tile u+1 opens stage it+1
+      if (it + 2 < ntiles) wait_tiles_barrier<1>();
+      else wait_tiles_barrier<0>();
+      if (it + NST - 1 < ntiles) {
+        const int ns = (it + NST - 1) % NST;
+        issue_tile(k, v, kv_begin + (it + NST - 1) * BKV, nkv, D, h, sK_lds + ns * TILEB,
+                   sV_lds + ns * TILEB, voff_k, voff_v, wave);
+      }
     }
-    const char* kt = sK + ((it + 1) % NST) * TILEB;
-    const char* vt = sV + (it % NST) * TILEB;
-    auto kfrag = [&](int j) {   // slot j: block kb = j%2, dims dk = j/2
-      return *reinterpret_cast<const bf16x8*>(kt + (j & 1) * 32 * ROWB + koff[j >> 1]);
-    };
+    const char* kt = k_sub(u + 1);
+    const char* vt = v_sub(u - 1);
+    bf16x8 kf[2], vf[2];
+    kf[0] = kfrag(kt, 0);
+    if (pv) vf[0] = vfrag(vt, 0);
+    float l2[2] = {0.f, 0.f};
+    float p_even = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s_nxt[kb][r] = 0.f;
-    bf16x8 kf[3];
-    kf[0] = kfrag(0);
-    kf[1] = kfrag(1);
-    u32x4 pw[4];   // P^T fragments as packed bf16 pairs
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      if (j + 2 < 16) kf[(j + 2) % 3] = kfrag(j + 2);
-      s_nxt[j & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[j % 3], qf[j >> 1], s_nxt[j & 1], 0, 0, 0);
-      // score elements q = 2j, 2j+1 of tile it: block q/16, accumulator q%16
-      const int q = 2 * j;
-      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[q >> 4][q & 15], c, -m_run));
-      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[q >> 4][(q & 15) + 1], c, -m_run));
-      const bf16x2 pr = {(bf16)p0, (bf16)p1};
-      pw[q >> 3][(q & 7) >> 1] = __builtin_bit_cast(uint32_t, pr);
-      l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run, false);
+    for (int j = 0; j < 8; ++j) {
+      if (j + 1 < 8) kf[(j + 1) & 1] = kfrag(kt, j + 1);
+      s_nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[j & 1], qf[j], j == 0 ? negm : s_nxt, 0, 0, 0);
+      {
+        const int r = 2 * j;   // score element r of sub-tile u
+        p_even = __builtin_amdgcn_exp2f(s_cur[r]);
+      }
+      if (pv) {
+        if (j + 1 < 8) vf[(j + 1) & 1] = vfrag(vt, j + 1);
+        acc_o[j & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[j & 1], __builtin_bit_cast(bf16x8, pw_prev[j >> 2]),
+                                                               acc_o[j & 3], 0, 0, 0);
+      }
+      {
+        const int r = 2 * j + 1;
+        const float p_odd = __builtin_amdgcn_exp2f(s_cur[r]);
+        const bf16x2 pr = {(bf16)p_even, (bf16)p_odd};
+        pw_cur[r >> 3][(r & 7) >> 1] = __builtin_bit_cast(uint32_t, pr);
+        l2[j & 1] += p_even + p_odd;
+      }
     }
-    auto vfrag = [&](int j) {   // slot j: k-step ts = j/4 (kb = ts/2, jp = ts%2), dims block db = j%4
-      const int ts = j >> 2, db = j & 3;
-      const char* vk = vt + ((ts >> 1) * 32 + 16 * (ts & 1)) * ROWB;
-      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vk + voffr[db]));
-      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vk + 8 * ROWB + voffr[db]));
-      const u32x4 raw = {__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
-                         __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]};
-      return __builtin_bit_cast(bf16x8, raw);
-    };
-    bf16x8 vf[2];
-    vf[0] = vfrag(0);
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      if (j + 1 < 16) vf[(j + 1) & 1] = vfrag(j + 1);
-      acc_o[j & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[j & 1], __builtin_bit_cast(bf16x8, pw[j >> 2]),
-                                                             acc_o[j & 3], 0, 0, 0);
+    float lt = l2[0] + l2[1];
+    if (__ballot(lt > kRaiseSum) != 0ull) {   // after PV(u-1): O is complete up to sub-tile u-1
+      raise(s_cur, &s_nxt);
+      lt = probs(s_cur, pw_cur);
     }
+    l_run += lt;
   };
 
-  f32x16 sa[2], sb[2];
+  f32x16 sa, sb;
+  u32x4 pwa[2], pwb[2];   // P^T fragments (packed bf16 pairs) of two consecutive sub-tiles
   if (min(NST - 2, ntiles - 1) >= 2) wait_tiles_barrier<2>();
   else if (ntiles - 1 >= 1) wait_tiles_barrier<1>();
   else wait_tiles_barrier<0>();
-  scores(0, sa);
-  auto last = [&](f32x16* s_cur, int it) {   // no next tile to overlap
-    bf16x8 pb[4];
-    prepare(s_cur, kv_begin + it * BKV);
-    probs(s_cur, pb);
-    accumulate(it % NST, pb);
-  };
-  int it = 0;
-  for (; it + 2 < ntiles; it += 2) {
-    step(sa, sb, it);
-    step(sb, sa, it + 1);
+  // first sub-tile: unshifted scores, whose max is the initial reference
+  {
+    const char* kt = k_sub(0);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sa[r] = 0.f;
+#pragma unroll
+    for (int dk = 0; dk < DH / 16; ++dk)
+      sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag(kt, dk), qf[dk], sa, 0, 0, 0);
   }
-  if (it + 1 < ntiles) {
-    step(sa, sb, it);
-    last(sb, it + 1);
+  mask_tail(sa, kv_begin);
+  m_run = tile_max(sa);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) sa[r] -= m_run;
+  set_negm();
+  // last sub-tile u: its softmax, then the PV of sub-tiles u-1 (if pv) and u
+  auto finish = [&](f32x16& s_cur, u32x4* pw_cur, const u32x4* pw_prev, int u, bool pv) {
+    mask_tail(s_cur, kv_begin + u * SUB);
+    if (pv) accumulate(v_sub(u - 1), pw_prev);
+    float lt = probs(s_cur, pw_cur);
+    if (__ballot(lt > kRaiseSum) != 0ull) {
+      raise(s_cur, nullptr);
+      lt = probs(s_cur, pw_cur);
+    }
+    l_run += lt;
+    accumulate(v_sub(u), pw_cur);
+  };
+  const int nsub = (kv_end - kv_begin + SUB - 1) / SUB;
+  if (nsub == 1) {
+    finish(sa, pwa, pwb, 0, false);
   } else {
-    last(sa, it);
+    step(sa, sb, pwa, pwb, 0, false);
+    int u = 1;
+    for (; u + 2 < nsub; u += 2) {
+      step(sb, sa, pwb, pwa, u, true);
+      step(sa, sb, pwa, pwb, u + 1, true);
+    }
+    if (u + 1 < nsub) {
+      step(sb, sa, pwb, pwa, u, true);
+      finish(sa, pwa, pwb, u + 1, true);
+    } else {
+      finish(sb, pwb, pwa, u, true);
+    }
   }
 
   float l_tot;
