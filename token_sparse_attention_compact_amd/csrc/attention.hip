@@ -36,8 +36,9 @@
 //    O and l are then rescaled, which is exact after the final division.
 //    Row sums are float32 adds (v_dot2 over the packed pairs would be fewer
 //    instructions but holds up the MFMA issue far more).
-//  * When |A_i| is small the KV range is split across workgroups; partial
-//    (O, max, sum) are merged in a fixed split order (deterministic).
+//  * When |A_i| is small the KV range is split across workgroups; the
+//    partials (O/l in bf16, max, sum) are merged in a fixed split order
+//    (deterministic).
 //  * Workgroup ids are remapped so each XCD runs a contiguous range of
 //    (split, head, query tile): the workgroups sharing an XCD's L2 stream
 //    the same head's K/V at the same time.
@@ -130,7 +131,7 @@ __device__ __forceinline__ void wait_tiles_barrier() {
 
 __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_d128_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-    bf16* __restrict__ o, float* __restrict__ part_o, float* __restrict__ part_ml, int32_t nA,
+    bf16* __restrict__ o, bf16* __restrict__ part_o, float* __restrict__ part_ml, int32_t nA,
     int32_t nkv, int32_t H, float c, int32_t n_qt, int32_t splits, int32_t tiles_per_split) {
   __shared__ __attribute__((aligned(1024))) char smem[2 * NST * TILEB];
   const char* const sK = smem;
@@ -413,40 +414,31 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_d128_kernel(
   }
   if (!q_ok) return;
   // acc_o[db][r] <-> dim db*32 + 8*(r/4) + 4*half + r%4, query l32
-  if (splits == 1) {
-    const float inv = 1.0f / l_tot;
-    bf16* orow = o + (size_t)qi * D + h * DH;
+  // acc_o[db][r] <-> dim db*32 + 8*(r/4) + 4*half + r%4, query l32; the
+  // split partials are stored normalised (O / l, bf16) with their (m, l)
+  const float inv = 1.0f / l_tot;
+  bf16* orow = splits == 1 ? o + (size_t)qi * D + h * DH
+                           : part_o + ((size_t)(sp * H + h) * nA + qi) * DH;
 #pragma unroll
-    for (int db = 0; db < DH / 32; ++db)
+  for (int db = 0; db < DH / 32; ++db)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        bf16x4 w4;
+    for (int j = 0; j < 4; ++j) {
+      bf16x4 w4;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w4[e] = (bf16)(acc_o[db][4 * j + e] * inv);
-        *reinterpret_cast<bf16x4*>(orow + db * 32 + 8 * j + 4 * half) = w4;
-      }
-  } else {
-    const size_t prow = ((size_t)(sp * H + h) * nA + qi);
-    float* po = part_o + prow * DH;
-#pragma unroll
-    for (int db = 0; db < DH / 32; ++db)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        f32x4 w4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) w4[e] = acc_o[db][4 * j + e];
-        *reinterpret_cast<f32x4*>(po + db * 32 + 8 * j + 4 * half) = w4;
-      }
-    if (half == 0) {
-      part_ml[prow * 2 + 0] = m_run;
-      part_ml[prow * 2 + 1] = l_tot;
+      for (int e = 0; e < 4; ++e) w4[e] = (bf16)(acc_o[db][4 * j + e] * inv);
+      *reinterpret_cast<bf16x4*>(orow + db * 32 + 8 * j + 4 * half) = w4;
     }
+  if (splits > 1 && half == 0) {
+    const size_t prow = (size_t)(sp * H + h) * nA + qi;
+    part_ml[prow * 2 + 0] = m_run;
+    part_ml[prow * 2 + 1] = l_tot;
   }
 }
 
-// Merge split partials in split order: O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
+// Merge split partials in split order: with weights w_s = l_s 2^(m_s - M),
+// O = sum_s w_s (O_s / l_s) / sum_s w_s.
 template <int HD>
-__global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict__ part_o,
+__global__ __launch_bounds__(256) void attn_merge_kernel(const bf16* __restrict__ part_o,
                                                          const float* __restrict__ part_ml,
                                                          bf16* __restrict__ o, int32_t nA,
                                                          int32_t H, int32_t splits) {
@@ -462,11 +454,11 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int s = 0; s < splits; ++s) {
     const size_t pr = (size_t)(s * H + h) * nA + qi;
-    const float w = __builtin_amdgcn_exp2f(part_ml[pr * 2] - M);
-    L += w * part_ml[pr * 2 + 1];
-    const f32x4 po = *reinterpret_cast<const f32x4*>(part_o + pr * HD + d4);
+    const float w = __builtin_amdgcn_exp2f(part_ml[pr * 2] - M) * part_ml[pr * 2 + 1];
+    L += w;
+    const bf16x4 po = *reinterpret_cast<const bf16x4*>(part_o + pr * HD + d4);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(w, po[e], acc[e]);
+    for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(w, (float)po[e], acc[e]);
   }
   const float inv = 1.0f / L;
   bf16x4 w4;
@@ -569,7 +561,7 @@ size_t attn_workspace_bytes(int32_t n_active, int32_t n_kv, int32_t H, int32_t D
   const SplitPlan p = plan_split(n_active, n_kv, H);
   if (p.splits <= 1) return 0;
   const size_t rows = (size_t)p.splits * H * n_active;
-  return align_up(rows * Dh * sizeof(float), 256) + rows * 2 * sizeof(float);
+  return align_up(rows * Dh * sizeof(bf16), 256) + rows * 2 * sizeof(float);
 }
 
 hsa_status launch_attention(const void* q, const void* k, const void* v, void* o,
@@ -578,14 +570,14 @@ hsa_status launch_attention(const void* q, const void* k, const void* v, void* o
   if (n_active == 0) return HSA_OK;
   if (use_mfma_path(Dh, dt)) {
     const SplitPlan p = plan_split(n_active, n_kv, H);
-    float* part_o = nullptr;
+    bf16* part_o = nullptr;
     float* part_ml = nullptr;
     if (p.splits > 1) {
       const size_t rows = (size_t)p.splits * H * n_active;
       if (ws == nullptr || ws_bytes < attn_workspace_bytes(n_active, n_kv, H, Dh))
         return HSA_ERR_WORKSPACE;
-      part_o = (float*)ws;
-      part_ml = (float*)((char*)ws + align_up(rows * Dh * sizeof(float), 256));
+      part_o = (bf16*)ws;
+      part_ml = (float*)((char*)ws + align_up(rows * Dh * sizeof(bf16), 256));
     }
     const int32_t total = p.n_qt * H * p.splits;
     attn_bf16_d128_kernel<<<total, kAttnThreads, 0, s>>>(
