@@ -10,6 +10,12 @@ attention over all 32760 cached rows, out-projection, LN, GELU MLP), unembed,
 cached Euler + score.  Inputs (random-init weights, mid-run K/V caches and
 sampler state) are generated on the device before timing.
 
+Also measured in the same run: the attention kernel alone (HIP events on its
+stream), the full T = 40 sampling loop from fresh latents, iteration time
+against the active fraction, the Euler pass on a working set past the
+Infinity Cache, attainable peaks (an MFMA-only probe kernel and a 256 MiB
+device copy) and the CPU oracle on a bounded sample.
+
 Prints one JSON line.  `value` is HSA iterations per second.
 """
 from __future__ import annotations
@@ -41,7 +47,9 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--blocks", type=int, default=30, help="number of blocks (the workload uses 30)")
-    p.add_argument("--attn-reps", type=int, default=20)
+    p.add_argument("--attn-reps", type=int, default=50)
+    p.add_argument("--no-loop", action="store_true", help="skip the full T=40 sampling loop")
+    p.add_argument("--no-peaks", action="store_true", help="skip the attainable-peak probes")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-scaling", action="store_true", help="skip the iteration-time vs active-fraction sweep")
     p.add_argument("--cpu-rows", type=int, default=2048)
@@ -77,6 +85,47 @@ def calibration_copy():
     dst = torch.empty_like(src)
     dst.copy_(src)
     torch.cuda.synchronize()
+
+
+def attainable_peaks(reps: int = 3):
+    """What this GPU delivers under load: an MFMA-only probe kernel (bf16
+    32x32x16, operands in registers, lib/libhsa_probe.so) and a 1 GiB
+    streaming copy kernel (same library; read + write bytes)."""
+    import ctypes as ct
+    lib = ct.CDLL(os.path.join(ROOT, "token_sparse_attention_compact_amd", "lib", "libhsa_probe.so"))
+    n_wg, iters = 1024, 4000
+    out = torch.empty(n_wg * 512, dtype=torch.float32, device="cuda")
+    stream = ct.c_void_p(torch.cuda.current_stream().cuda_stream)
+    call = lambda: lib.hsa_probe_mfma_peak(n_wg, iters, ct.c_void_p(out.data_ptr()), stream)
+    assert call() == 0
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        assert call() == 0
+    e.record()
+    torch.cuda.synchronize()
+    t = s.elapsed_time(e) / 1e3 / reps
+    mfma_tflops = n_wg * 8 * 16 * iters * 32768.0 / t / 1e12
+    src = torch.ones(256 << 20, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    nbytes = src.numel() * 4
+    copy = lambda: lib.hsa_probe_copy(ct.c_void_p(src.data_ptr()), ct.c_void_p(dst.data_ptr()),
+                                      ct.c_int64(nbytes), stream)
+    assert copy() == 0
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(reps):
+        assert copy() == 0
+    e.record()
+    torch.cuda.synchronize()
+    t = s.elapsed_time(e) / 1e3 / reps
+    assert torch.equal(src[:1024], dst[:1024]) and torch.equal(src[-1024:], dst[-1024:])
+    copy_gbs = 2 * src.numel() * 4 / t / 1e9
+    del src, dst, out
+    return {"mfma_bf16_tflops": round(mfma_tflops, 1), "copy_gbs": round(copy_gbs, 1),
+            "probe": "MFMA-only loop, 1024 workgroups x 8 waves x 64000 MFMAs; 1 GiB streaming copy "
+                     "(16-byte non-temporal accesses), read + write bytes"}
 
 
 def time_euler(H, n_tokens: int, C: int = 16, frac: float = 0.25, reps: int = 10):
@@ -151,7 +200,7 @@ def timed_steps(H, model, sched, state, sigma, steps, warmup):
     return time.perf_counter() - t0
 
 
-def time_attention(H, model, c, n_active, reps):
+def time_attention(H, model, c, n_active, reps, warmup: int = 10):
     """Average duration of the attention kernel at the step's launch configuration,
     with HIP events on the stream the kernel runs on.  Layers' caches rotate so
     K/V come from HBM as in the stack."""
@@ -160,18 +209,46 @@ def time_attention(H, model, c, n_active, reps):
     ws = torch.empty(max(1, H.hsa_attn_workspace_size(n_active, c.N, c.H, c.Dh)), dtype=torch.uint8,
                      device="cuda")
     L = len(model.blocks)
-    for l in range(min(L, 3)):
-        b = model.blocks[l]
+    for r in range(warmup):
+        b = model.blocks[r % L]
         H.hsa_attn_active(q, b["k_cache"], b["v_cache"], o, c.H, c.Dh, ws=ws)
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
     for r in range(reps):
-        b = model.blocks[r % L]
+        b = model.blocks[(warmup + r) % L]
         H.hsa_attn_active(q, b["k_cache"], b["v_cache"], o, c.H, c.Dh, ws=ws)
     end.record()
     torch.cuda.synchronize()
     return start.elapsed_time(end) / 1e3 / reps
+
+
+def sampling_loop(H, model, c, sigma):
+    """The whole sampler: iterations 0..T-1 of hsa_step from fresh latents (all
+    groups active at i = 0, regrouping at i = 10, 20, 30), one device
+    synchronisation at the end."""
+    dev = "cuda"
+    g = torch.Generator(device=dev)
+    g.manual_seed(3 * 1000 + 9)
+    x0 = torch.randn((c.N, c.C), generator=g, device=dev)
+    group0 = torch.from_numpy(synth.group0(c)).to(dev)
+    state = H.DeviceState(model.dims, x0, group0)
+    sched = H.make_schedule(c.T, c.budgets, c.counts())
+    regroup_at = set(c.regroup)
+    n_act = [H.hsa_n_active(sched, i) for i in range(c.T)]
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for i in range(c.T):
+        H.hsa_step(model, sched, state, i, float(sigma[i]), float(sigma[i + 1]), i in regroup_at)
+    e.record()
+    torch.cuda.synchronize()
+    t = s.elapsed_time(e) / 1e3
+    ok = bool(torch.isfinite(state.x).all().item())
+    del state
+    return {"iterations": c.T, "s": round(t, 3), "iter_per_s": round(c.T / t, 3),
+            "mean_active_frac": round(sum(n_act) / (c.T * c.N), 4), "regroup_at": sorted(regroup_at),
+            "finite": ok}
 
 
 def step_scaling(H, model, state, c, sigma, reps: int = 5):
@@ -290,8 +367,17 @@ def main():
                      "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "avg_launch_us": round(t_attn * 1e6, 2),
                      "traffic": recorded_traffic()},
     }
+    if not args.no_peaks:
+        peaks = attainable_peaks()
+        out["attainable"] = peaks
+        out["roofline"]["frac_of_attainable"] = round(attn_tflops / peaks["mfma_bf16_tflops"], 4)
+    if not args.no_loop:
+        out["sampling_loop"] = sampling_loop(H, model, c, sigma)
     if args.euler_tokens > 0:
         out["euler_hbm"] = time_euler(H, args.euler_tokens)
+        if "attainable" in out:
+            out["euler_hbm"]["frac_of_attainable_copy"] = round(
+                out["euler_hbm"]["gbs"] / out["attainable"]["copy_gbs"], 4)
     if not args.no_scaling:
         out["scaling_with_active_fraction"] = step_scaling(H, model, state, c, sigma)
     if not args.no_cpu_baseline:

@@ -3,7 +3,9 @@
     python -m token_sparse_attention_compact_amd.build [-v]
 
 Compiles every csrc/*.hip to an object (in parallel) and links
-token_sparse_attention_compact_amd/lib/libhsa.so.  Always rebuilds.
+token_sparse_attention_compact_amd/lib/libhsa.so; probe/*.hip (measurement
+helpers used by the benchmark only) become lib/libhsa_probe.so.  Always
+rebuilds.
 """
 from __future__ import annotations
 
@@ -20,6 +22,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libhsa.so")
+PROBE_DIR = os.path.join(PKG, "probe")
+PROBE_LIB = os.path.join(LIBDIR, "libhsa_probe.so")
 ARCH = "gfx950"
 
 FLAGS = [
@@ -54,27 +58,32 @@ def _compile(cc, src, obj, verbose):
         print(out, flush=True)
 
 
+def _link(cc, objs, lib, verbose):
+    tmp_lib = lib + ".tmp"
+    cmd = [cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp_lib]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}")
+    os.replace(tmp_lib, lib)
+
+
 def build(verbose: bool = False) -> str:
     cc = hipcc()
     os.makedirs(LIBDIR, exist_ok=True)
+    probes = sorted(os.path.join(PROBE_DIR, f) for f in os.listdir(PROBE_DIR) if f.endswith(".hip"))
     with tempfile.TemporaryDirectory(prefix="hsa_build_") as tmp:
-        objs = []
-        jobs = []
+        objs, probe_objs, jobs = [], [], []
         with cf.ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 4)) as ex:
-            for src in sources():
+            for src, dst in [(p, objs) for p in sources()] + [(p, probe_objs) for p in probes]:
                 obj = os.path.join(tmp, os.path.basename(src) + ".o")
-                objs.append(obj)
+                dst.append(obj)
                 jobs.append(ex.submit(_compile, cc, src, obj, verbose))
             for j in jobs:
                 j.result()
-        tmp_lib = LIB + ".tmp"
-        cmd = [cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp_lib]
-        if verbose:
-            print(" ".join(cmd), flush=True)
-        r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
-        if r.returncode != 0:
-            raise RuntimeError(f"link failed:\n{r.stdout}")
-        os.replace(tmp_lib, LIB)
+        _link(cc, objs, LIB, verbose)
+        _link(cc, probe_objs, PROBE_LIB, verbose)
     return LIB
 
 
