@@ -188,10 +188,26 @@ def test_layernorm_embed_unembed(dtype):
     assert rel_l2(host(vn), O.layer_norm(h) @ w_out.T.astype(np.float64)) < 1e-5
 
 
+@pytest.mark.parametrize("D", [128, 256, 1536, 2000, 5120])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_layernorm_widths(D, dtype):
+    """Row held in registers (D a multiple of 256) and the two-pass kernel
+    (other widths), against the oracle's LayerNorm."""
+    rs = np.random.default_rng(D)
+    rows = 37
+    h = (rs.standard_normal((rows, D)) * 3 - 1.5).astype(np.float32)
+    out = torch.empty(rows, D, dtype=dtype, device=DEV)
+    H.hsa_layernorm(dev(h), out)
+    tol = 1e-5 if dtype == torch.float32 else 4e-3
+    assert rel_l2(host(out), O.layer_norm(h)) < tol
+
+
 # ---------------------------------------------------------------- GEMMs
 
 @pytest.mark.parametrize("M,N,K", [(1, 128, 64), (100, 384, 192), (300, 256, 128), (257, 200, 64),
-                                   (1000, 1536, 1536)])
+                                   (1000, 1536, 1536),
+                                   # 256x256-tile path (wide output / long K), ragged in M and N
+                                   (1100, 6148, 128), (1030, 300, 4160)])
 def test_linear_bf16(M, N, K):
     say(f"linear bf16 M={M} N={N} K={K}")
     rs = np.random.default_rng(M * 7 + N + K)

@@ -2,7 +2,9 @@
 // gather + embed of the active latents (the active rows enter the model,
 // section 2.2 item 1) and final LayerNorm + unembed to the velocity.
 // All three are bandwidth-bound; one 64-wide wavefront per row with float4
-// accesses, statistics in float32 from two passes over the row.
+// accesses.  LayerNorm keeps the row in registers when D is a multiple of
+// 256 (one read of the row from memory, statistics in float32 from the
+// registers); otherwise, and in unembed, the statistics take two passes.
 #include "common.h"
 
 namespace hsa {
@@ -60,6 +62,56 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const float* __restrict_
 #pragma unroll
     for (int c = 0; c < 4; ++c) v[c] = (v[c] - mean) * rstd;
     store4<OutT>(orow + 4 * i, v);
+  }
+}
+
+// Row in registers: lane l holds float4 chunks l, l+64, ..., l+64(NV-1).
+template <typename OutT, int NV>
+__global__ __launch_bounds__(256) void layernorm_reg_kernel(const float* __restrict__ h,
+                                                            OutT* __restrict__ out, int32_t rows,
+                                                            int32_t D) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int32_t row = blockIdx.x * kRowsPerBlock + threadIdx.x / kWave;
+  if (row >= rows) return;
+  const f32x4* hr = reinterpret_cast<const f32x4*>(h + (size_t)row * D);
+  f32x4 v[NV];
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    v[i] = hr[lane + kWave * i];
+    s += (v[i][0] + v[i][1]) + (v[i][2] + v[i][3]);
+  }
+  const float mean = wave_sum(s) / (float)D;
+  float q = 0.f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float d = v[i][c] - mean;
+      q += d * d;
+    }
+  const float rstd = 1.0f / sqrtf(wave_sum(q) / (float)D + kLnEps);
+  OutT* orow = out + (size_t)row * D;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    f32x4 o;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) o[c] = (v[i][c] - mean) * rstd;
+    store4<OutT>(orow + 4 * (lane + kWave * i), o);
+  }
+}
+
+template <typename OutT>
+bool launch_layernorm_reg(const float* h, OutT* out, int32_t rows, int32_t D, int blocks,
+                          hipStream_t s) {
+  if (D % (4 * kWave) != 0) return false;
+  switch (D / (4 * kWave)) {
+#define HSA_LN_CASE(nv) \
+    case nv: layernorm_reg_kernel<OutT, nv><<<blocks, 256, 0, s>>>(h, out, rows, D); return true;
+    HSA_LN_CASE(1) HSA_LN_CASE(2) HSA_LN_CASE(3) HSA_LN_CASE(4) HSA_LN_CASE(5) HSA_LN_CASE(6)
+    HSA_LN_CASE(8) HSA_LN_CASE(10) HSA_LN_CASE(12) HSA_LN_CASE(16) HSA_LN_CASE(20) HSA_LN_CASE(24)
+#undef HSA_LN_CASE
+    default: return false;
   }
 }
 
@@ -183,10 +235,13 @@ hsa_status launch_layernorm(const float* h, void* out, int32_t rows, int32_t D, 
                             hipStream_t s) {
   if (rows == 0) return HSA_OK;
   const int blocks = cdiv(rows, kRowsPerBlock);
-  if (dt == HSA_BF16)
-    layernorm_kernel<bf16><<<blocks, 256, 0, s>>>(h, (bf16*)out, rows, D);
-  else
-    layernorm_kernel<float><<<blocks, 256, 0, s>>>(h, (float*)out, rows, D);
+  if (dt == HSA_BF16) {
+    if (!launch_layernorm_reg<bf16>(h, (bf16*)out, rows, D, blocks, s))
+      layernorm_kernel<bf16><<<blocks, 256, 0, s>>>(h, (bf16*)out, rows, D);
+  } else {
+    if (!launch_layernorm_reg<float>(h, (float*)out, rows, D, blocks, s))
+      layernorm_kernel<float><<<blocks, 256, 0, s>>>(h, (float*)out, rows, D);
+  }
   return launch_status();
 }
 
