@@ -278,20 +278,42 @@ __global__ __launch_bounds__(G::THREADS, G::MINB) void gemm_bf16_kernel(
       }
 }
 
-// 128x128 tiles, 8 wavefronts of 32x64, 2 stages (64 KiB LDS, so two
-// workgroups share a CU: four wavefronts per SIMD hide each other's LDS and
-// HBM latency), an XCD's concurrent tiles as 8 row x 8 column blocks.
-// Measured on MI355X against 256x128/256x256 tiles, 4-wave layouts and 3-4
-// stage rings for the QKV and out-projection shapes of the 1.3B-shaped
-// stack; this one was fastest on both.
-typedef GemmCfg<128, 128, 4, 2, 2, 8> CfgMain;
-// 256x256 tiles, 8 wavefronts of 64x128, 2 stages (128 KiB LDS, one
-// workgroup per CU): half the operand traffic per FLOP of the 128x128 tile.
-// Faster by 6-7% on the MLP shapes (N = 8960, or K = 8960) where there are
-// enough tiles or enough K per tile; used for wide outputs and long K.
-typedef GemmCfg<256, 256, 4, 2, 2, 4, 1> CfgWide;
+// Three tile shapes, chosen per GEMM shape (pick_cfg).  Measured on MI355X
+// (interleaved runs, M = 8190 rows) against 256x128, 256x256, 64x192 and
+// 128x64 tiles, 4- and 8-wave layouts and 2-4 stage rings:
+//  * 256x192, 8 waves of 64x96, 2 stages (112 KiB LDS, one workgroup per
+//    CU): out-projection 762, MLP up 986, MLP down 1141, QKV 920 TFLOP/s;
+//    192 divides the stack's output widths (1536, 4608), so the tile count
+//    is a whole number of rounds over the chip;
+//  * 128x192, 8 waves of 32x96 (80 KiB, two workgroups per CU): QKV 944;
+//  * 128x128, 8 waves of 32x64 (64 KiB, two per CU): 671 / 906 / 950 / 896,
+//    but the most tiles when M is small.
+typedef GemmCfg<256, 192, 4, 2, 2, 4, 1> CfgWide;
+typedef GemmCfg<128, 192, 4, 2, 2, 4> CfgMain;
+typedef GemmCfg<128, 128, 4, 2, 2, 8> CfgSmall;
 
-bool use_wide(int32_t M, int32_t N, int32_t K) { return M >= 1024 && (N >= 6144 || K >= 4096); }
+enum { kCfgWide, kCfgMain, kCfgSmall };
+
+// Cost model: a CU works through ceil(tiles / 256) tiles of its shape one
+// after another (two co-resident workgroups share the CU's MFMA rate), so
+// time ~ ceil(tiles / 256) * tile area / relative efficiency.  Ties go to
+// the larger tile.
+int pick_cfg(int32_t M, int32_t N) {
+  constexpr int64_t kCus = 256;
+  const struct { int id; int64_t bm, bn, eff; } c[3] = {
+      {kCfgWide, 256, 192, 1000}, {kCfgMain, 128, 192, 960}, {kCfgSmall, 128, 128, 900}};
+  int best = kCfgWide;
+  int64_t best_cost = -1;
+  for (const auto& x : c) {
+    const int64_t tiles = cdiv((int64_t)M, x.bm) * cdiv((int64_t)N, x.bn);
+    const int64_t cost = cdiv(tiles, kCus) * x.bm * x.bn * 1000 / x.eff;
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best = x.id;
+    }
+  }
+  return best;
+}
 
 // ---------------------------------------------------------------- float32
 constexpr int FT = 64, FK = 16;
@@ -350,10 +372,11 @@ hsa_status run(const void* a, const void* w, int32_t M, int32_t N, int32_t K, hs
                const EpiArgs& ep, hipStream_t s) {
   if (dt == HSA_BF16) {
     if (N % 4 != 0 || (EPI == EPI_QKV_SCATTER && ep.D % 4 != 0)) return HSA_ERR_SHAPE;
-    if (use_wide(M, N, K))
-      launch_bf16<CfgWide, EPI>(a, w, M, N, K, ep, s);
-    else
-      launch_bf16<CfgMain, EPI>(a, w, M, N, K, ep, s);
+    switch (pick_cfg(M, N)) {
+      case kCfgWide: launch_bf16<CfgWide, EPI>(a, w, M, N, K, ep, s); break;
+      case kCfgMain: launch_bf16<CfgMain, EPI>(a, w, M, N, K, ep, s); break;
+      default: launch_bf16<CfgSmall, EPI>(a, w, M, N, K, ep, s); break;
+    }
   } else {
     dim3 grid(cdiv(N, FT), cdiv(M, FT));
     gemm_f32_kernel<EPI><<<grid, 256, 0, s>>>((const float*)a, (const float*)w, M, N, K, ep);
