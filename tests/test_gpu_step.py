@@ -131,7 +131,10 @@ def run_gpu(c, m, sched, state, iters, sigma, field=None):
 
 
 def select_margin(score, counts):
-    """Smallest relative gap between the scores on either side of a group boundary."""
+    """Smallest relative gap between the scores on either side of a group boundary.
+    A boundary between two +inf scores (tokens without a second prediction yet)
+    is an exact tie on both sides, broken by token index: it has no margin to
+    lose and is skipped."""
     s = np.sort(np.asarray(score, np.float64))[::-1]
     gaps = []
     b = 0
@@ -139,14 +142,24 @@ def select_margin(score, counts):
         b += n
         if 0 < b < s.size:
             hi, lo = s[b - 1], s[b]
+            if np.isinf(hi):
+                if hi != lo:
+                    gaps.append(np.inf)   # +inf against a finite score: no rounding can flip it
+                continue
             gaps.append(abs(hi - lo) / max(abs(hi), 1e-30))
     return min(gaps) if gaps else np.inf
 
 
-def test_step_cfg1_full_run_f32():
-    """DiT-lite float32: 8 iterations, budgets {8,4}, regrouping from i = 3 on."""
+@pytest.mark.parametrize("variant", ["cfg1", "empty_active_sets"])
+def test_step_cfg1_full_run_f32(variant):
+    """DiT-lite float32: 8 iterations, budgets {8,4}, regrouping from i = 3 on.
+    Variant with an empty full-budget group (budgets {8,4,2}, shares 0/50/50):
+    every odd iteration has |A_i| = 0 and is the cached Euler step alone."""
     c = synth.CONFIGS[1]
-    say("hsa_step cfg1 fp32 full run")
+    if variant == "empty_active_sets":
+        c = c.with_(budgets=(8, 4, 2), shares=(0.0, 0.5, 0.5))
+        assert c.counts()[0] == 0
+    say(f"hsa_step cfg1 fp32 full run ({variant})")
     om = oracle_model(c)
     m = device_model(c, om)
     sched = H.make_schedule(c.T, c.budgets, c.counts())
@@ -273,3 +286,19 @@ def test_step_full_size_iteration_properties():
     kv = a @ om.blocks[0]["w_qkv"][c.D:].T
     assert rel_l2(host(m.blocks[0]["k_cache"])[idx[rows]], om.store.act(kv[:, :c.D])) < TOL_BF16
     assert rel_l2(host(m.blocks[0]["v_cache"])[idx[rows]], om.store.act(kv[:, c.D:])) < TOL_BF16
+
+
+def test_zero_row_calls_are_no_ops():
+    """|A_i| = 0 reaches every row-wise entry point as zero rows: each returns
+    success and writes nothing."""
+    D = 256
+    sentinel = torch.full((4, D), 7.0, dtype=torch.bfloat16, device=DEV)
+    q = torch.zeros(0, D, dtype=torch.bfloat16, device=DEV)
+    kv = torch.randn(100, D, device=DEV).to(torch.bfloat16)
+    o = sentinel[:0]
+    H.hsa_attn_active(q, kv, kv, o, 2, 128)
+    w = torch.randn(D, D, device=DEV).to(torch.bfloat16)
+    H.hsa_linear(q, w, sentinel[:0])
+    H.hsa_layernorm(torch.zeros(0, D, device=DEV), sentinel[:0])
+    torch.cuda.synchronize()
+    assert torch.all(sentinel == 7.0)

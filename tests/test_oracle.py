@@ -328,6 +328,27 @@ def test_skipped_tokens_advance_with_cached_velocity():
     assert np.all(np.any(st.k_cache[:, a] != before.k_cache[:, a], axis=-1))
 
 
+def test_empty_active_set_iteration():
+    # A schedule whose full-budget group is empty: at odd i no group is active,
+    # |A_i| = 0, and the iteration is the cached Euler step alone.
+    c = _tiny_cfg(budgets=(8, 4, 2), shares=(0.0, 0.5, 0.5), L=1)
+    assert c.counts()[0] == 0
+    m = _model(c)
+    sched = O.Schedule(T=8, budgets=[8, 4, 2], counts=c.counts())
+    assert O.n_active_closed_form(c.counts(), [8, 4, 2], 8, 1) == 0
+    sigma = synth.sigma_schedule(8)
+    st = O.init_state(m.dims, synth.x0(c), synth.group0(c))
+    O.sample(m, sched, st, sigma, iters=[0])
+    before = st.copy()
+    out = O.hsa_iteration(m, sched, st, 1, sigma[1], sigma[2], regroup=False)
+    assert out["active_idx"].size == 0
+    ds = float(np.float32(sigma[2]) - np.float32(sigma[1]))
+    np.testing.assert_array_equal(st.v_hat, before.v_hat)
+    np.testing.assert_array_equal(st.score, before.score)
+    np.testing.assert_array_equal(st.k_cache, before.k_cache)
+    np.testing.assert_allclose(st.x, before.x + ds * before.v_hat, rtol=1e-6)
+
+
 def test_cache_rows_hold_last_active_projection():
     # After each iteration, row n of layer l holds the K/V the token had at its last
     # active iteration; attention at i sees those stale rows for skipped tokens.
