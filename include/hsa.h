@@ -50,7 +50,10 @@ typedef enum {
 typedef enum { HSA_F32 = 0, HSA_BF16 = 1 } hsa_dtype;
 
 /* Model shape.  N tokens, C latent channels, width D = H * Dh, MLP width F,
- * L blocks, n_text text tokens for cross-attention (0: no cross-attention). */
+ * L blocks, n_text text tokens for cross-attention (0: no cross-attention).
+ * bf16 operands are streamed through 32-bit buffer descriptors: every bf16
+ * matrix a kernel reads whole (N x D, N x F, weights) must stay below 4 GiB,
+ * i.e. N * max(D, F) * 2 < 2^32; larger shapes return HSA_ERR_SHAPE. */
 typedef struct {
   int32_t N, C, D, H, Dh, F, L, n_text;
   hsa_dtype dtype;
@@ -149,8 +152,9 @@ hsa_status hsa_euler(float *x, float *v_hat, float *score, const float *v_new,
 /* Active-query attention (section 2.2 items 3-4): for each of n_active query
  * rows and each head h, o = softmax(q_h K_h^T * scale) V_h over all n_kv rows
  * of k and v, no mask.  q, o [n_active][H*Dh]; k, v [n_kv][H*Dh].  Dh is 64
- * or 128.  ws: at least hsa_attn_workspace_size() bytes (may be NULL when
- * that size is 0). */
+ * or 128; bf16 needs n_kv * H * Dh * 2 < 2^32 (HSA_ERR_SHAPE otherwise).
+ * ws: at least hsa_attn_workspace_size() bytes (may be NULL when that size
+ * is 0). */
 hsa_status hsa_attn_active(const void *q, const void *k, const void *v, void *o,
                            int32_t n_active, int32_t n_kv, int32_t H, int32_t Dh, float scale,
                            hsa_dtype dtype, void *ws, size_t ws_bytes, void *stream);
@@ -172,7 +176,9 @@ hsa_status hsa_unembed(const float *h, const void *w_out, float *v_new, int32_t 
                        int32_t D, int32_t C, hsa_dtype dtype, void *stream);
 
 /* Linear map on rows: out = act(a w^T), a [M][K], w [Nout][K], out [M][Nout],
- * all in dtype; act 0 = identity, 1 = GELU (tanh form). */
+ * all in dtype; act 0 = identity, 1 = GELU (tanh form).  bf16: K % 64 == 0,
+ * Nout % 4 == 0, M * K * 2 and Nout * K * 2 below 2^32 (HSA_ERR_SHAPE
+ * otherwise; the same holds for hsa_linear_residual and hsa_qkv_scatter). */
 hsa_status hsa_linear(const void *a, const void *w, void *out, int32_t M, int32_t Nout,
                       int32_t K, int32_t act, hsa_dtype dtype, void *stream);
 

@@ -90,3 +90,23 @@ def test_step_rejects_bad_schedule_before_launch():
     ok = H.make_schedule(8, [8, 4], [128, 128])
     st.workspace_bytes = 16                            # too small
     assert H.load().hsa_step(ct.byref(m), ct.byref(ok), ct.byref(st), 0, 1.0, 0.875, 0, None, None) == -5
+
+
+def test_bf16_operands_past_4gib_are_rejected():
+    """bf16 operands go through 32-bit buffer descriptors: shapes whose
+    operands reach 4 GiB come back as HSA_ERR_SHAPE before any launch."""
+    L = H.load()
+    big = H.make_dims(1 << 20, 16, 2048, 16, 128, 8192, 1)          # N x F x 2 = 16 GiB
+    with pytest.raises(H.HsaError) as e:
+        H.hsa_workspace_size(big)
+    assert e.value.status == -2
+    ok = H.make_dims(75600, 16, 5120, 40, 128, 13824, 40)          # the 14B-shaped stack fits
+    assert H.hsa_workspace_size(ok) > 0
+    null = None
+    # M * K * 2 = 4 GiB exactly
+    assert L.hsa_linear(null, null, null, 1 << 21, 64, 1024, 0, 1, null) == -2
+    assert L.hsa_linear(null, null, null, 0, 1 << 21, 1024, 0, 1, null) == -2     # W too large
+    # n_kv * H * Dh * 2 = 8 GiB
+    assert L.hsa_attn_active(null, null, null, null, 4, 1 << 21, 16, 128, 0.1, 1, null, 0, null) == -2
+    # float32 has no such limit on these entry points (it fails later on the null pointers)
+    assert L.hsa_linear(null, null, null, 1 << 21, 64, 1024, 0, 0, null) == -1

@@ -18,6 +18,10 @@ hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 bool valid_dtype(hsa_dtype t) { return t == HSA_F32 || t == HSA_BF16; }
 
+// bf16 GEMM and attention operands are read through buffer descriptors whose
+// size and offsets are 32-bit: a whole operand must stay below 4 GiB.
+bool fits_buffer(int64_t bytes) { return bytes < ((int64_t)1 << 32); }
+
 hsa_status check_dims(const hsa_dims* d) {
   if (!d) return HSA_ERR_ARG;
   if (!valid_dtype(d->dtype)) return HSA_ERR_DTYPE;
@@ -28,6 +32,8 @@ hsa_status check_dims(const hsa_dims* d) {
   if (d->Dh != 64 && d->Dh != 128) return HSA_ERR_SHAPE;
   if (d->C % 4 != 0) return HSA_ERR_SHAPE;
   if (d->dtype == HSA_BF16 && (d->D % 64 != 0 || d->F % 64 != 0)) return HSA_ERR_SHAPE;
+  if (d->dtype == HSA_BF16 && !fits_buffer((int64_t)d->N * (d->D > d->F ? d->D : d->F) * 2))
+    return HSA_ERR_SHAPE;
   if (d->dtype == HSA_F32 && (d->D % 4 != 0 || d->F % 4 != 0)) return HSA_ERR_SHAPE;
   return HSA_OK;
 }
@@ -188,7 +194,9 @@ hsa_status block_forward_impl(const hsa_model* m, int32_t layer, float* h,
 hsa_status check_gemm_shape(int32_t M, int32_t N, int32_t K, hsa_dtype dt) {
   if (!valid_dtype(dt)) return HSA_ERR_DTYPE;
   if (M < 0 || N <= 0 || K <= 0) return HSA_ERR_SHAPE;
-  if (dt == HSA_BF16 && K % 64 != 0) return HSA_ERR_SHAPE;
+  if (dt == HSA_BF16 && (K % 64 != 0 || N % 4 != 0)) return HSA_ERR_SHAPE;
+  if (dt == HSA_BF16 && (!fits_buffer((int64_t)M * K * 2) || !fits_buffer((int64_t)N * K * 2)))
+    return HSA_ERR_SHAPE;
   if (dt == HSA_F32 && K % 4 != 0) return HSA_ERR_SHAPE;
   return HSA_OK;
 }
@@ -293,6 +301,7 @@ hsa_status hsa_attn_active(const void* q, const void* k, const void* v, void* o,
                            hsa_dtype dtype, void* ws, size_t ws_bytes, void* stream) {
   if (!valid_dtype(dtype)) return HSA_ERR_DTYPE;
   if (n_active < 0 || n_kv <= 0 || H <= 0 || (Dh != 64 && Dh != 128)) return HSA_ERR_SHAPE;
+  if (dtype == HSA_BF16 && !fits_buffer((int64_t)n_kv * H * Dh * 2)) return HSA_ERR_SHAPE;
   if (n_active == 0) return HSA_OK;
   CHECK_PTR(q);
   CHECK_PTR(k);
