@@ -110,3 +110,37 @@ def test_bf16_operands_past_4gib_are_rejected():
     assert L.hsa_attn_active(null, null, null, null, 4, 1 << 21, 16, 128, 0.1, 1, null, 0, null) == -2
     # float32 has no such limit on these entry points (it fails later on the null pointers)
     assert L.hsa_linear(null, null, null, 1 << 21, 64, 1024, 0, 0, null) == -1
+
+
+def test_binding_rejects_mismatched_shapes():
+    """The C ABI sees raw pointers only; the binding checks tensor shapes against
+    the sizes it passes, so a short buffer is an error, not an out-of-bounds
+    access.  These raise before any pointer is taken (host tensors suffice)."""
+    import torch
+    bf = torch.bfloat16
+    q = torch.zeros(10, 256, dtype=bf)
+    kv = torch.zeros(50, 256, dtype=bf)
+    with pytest.raises(ValueError, match="o: expected shape"):
+        H.hsa_attn_active(q, kv, kv, torch.zeros(9, 256, dtype=bf), 2, 128)
+    with pytest.raises(ValueError, match="q: expected shape"):
+        H.hsa_attn_active(q, kv, kv, q, 2, 64)                       # H * Dh != width
+    with pytest.raises(ValueError, match="v: expected shape"):
+        H.hsa_attn_active(q, kv, torch.zeros(49, 256, dtype=bf), q, 2, 128)
+    with pytest.raises(ValueError, match="out: expected shape"):
+        H.hsa_linear(q, torch.zeros(128, 256, dtype=bf), torch.zeros(10, 64, dtype=bf))
+    with pytest.raises(ValueError, match="a: expected shape"):
+        H.hsa_linear(q, torch.zeros(128, 192, dtype=bf), torch.zeros(10, 128, dtype=bf))
+    with pytest.raises(ValueError, match="out: expected shape"):
+        H.hsa_layernorm(torch.zeros(4, 256), torch.zeros(4, 128, dtype=bf))
+    with pytest.raises(ValueError, match="pos: expected shape"):
+        x = torch.zeros(8, 16)
+        H.hsa_euler(x, x.clone(), torch.zeros(8), None, torch.zeros(7, dtype=torch.int32), 0.1, False)
+    d = H.make_dims(64, 16, 256, 2, 128, 512, 1)
+    blk = {"w_qkv": torch.zeros(768, 256, dtype=bf), "w_o": torch.zeros(256, 256, dtype=bf),
+           "w_1": torch.zeros(512, 256, dtype=bf), "w_2": torch.zeros(256, 512, dtype=bf),
+           "k_cache": torch.zeros(64, 256, dtype=bf), "v_cache": torch.zeros(63, 256, dtype=bf)}
+    with pytest.raises(ValueError, match="v_cache: expected shape"):
+        H.DeviceModel(d, torch.zeros(256, 16, dtype=bf), torch.zeros(16, 256, dtype=bf), [blk])
+    blk["v_cache"] = torch.zeros(64, 256, dtype=torch.float32)
+    with pytest.raises(ValueError, match="v_cache: expected"):
+        H.DeviceModel(d, torch.zeros(256, 16, dtype=bf), torch.zeros(16, 256, dtype=bf), [blk])

@@ -3,8 +3,10 @@ the HSA iteration runs in the library's HIP kernels.  torch is used for device
 memory and streams.
 
 Function names mirror include/hsa.h.  Each wrapper takes torch tensors, checks
-dtype/device/contiguity, passes raw pointers and the current HIP stream, and
-raises HsaError on a non-zero status.  If libhsa.so is missing the import
+dtype, device, contiguity and shape (the C ABI sees raw pointers only, so a
+tensor smaller than the sizes passed would be read or written out of
+bounds), passes raw pointers and the current HIP stream, and raises HsaError
+on a non-zero status.  If libhsa.so is missing the import
 fails loudly: there is no fallback path.
 """
 from __future__ import annotations
@@ -147,6 +149,19 @@ def _need(t: torch.Tensor, dtype, name: str):
         raise ValueError(f"{name}: expected {dtype}, got {t.dtype}")
 
 
+def _shape(t: torch.Tensor, shape, name: str):
+    """Exact shape; None in `shape` accepts any size in that dimension."""
+    if t.dim() != len(shape) or any(s is not None and d != s for d, s in zip(t.shape, shape)):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _rows(t: torch.Tensor, rows: int, cols: Optional[int], name: str):
+    """At least `rows` rows (and exactly `cols` columns when given)."""
+    if t.dim() != (1 if cols is None else 2) or t.shape[0] < rows or (cols is not None and t.shape[1] != cols):
+        want = f"[>={rows}]" if cols is None else f"[>={rows}, {cols}]"
+        raise ValueError(f"{name}: expected shape {want}, got {tuple(t.shape)}")
+
+
 # ---------------------------------------------------------------- structs from python
 def make_dims(N, C, D, H, Dh, F, L, n_text=0, dtype=torch.bfloat16) -> Dims:
     return Dims(N, C, D, H, Dh, F, L, n_text, HSA_BF16 if dtype == torch.bfloat16 else HSA_F32)
@@ -191,6 +206,10 @@ def hsa_active_set(group: torch.Tensor, sched: Schedule, it: int, active_idx: to
     _need(group, torch.uint8, "group")
     for t, n in ((active_idx, "active_idx"), (pos, "pos"), (n_active_dev, "n_active_dev")):
         _need(t, torch.int32, n)
+    N = group.numel()
+    _rows(active_idx, N, None, "active_idx")
+    _rows(pos, N, None, "pos")
+    _rows(n_active_dev, 1, None, "n_active_dev")
     _check("hsa_active_set", load().hsa_active_set(_ptr(group), group.numel(), ct.byref(sched), it,
                                                    _ptr(active_idx), _ptr(pos), _ptr(n_active_dev),
                                                    _stream(stream)))
@@ -199,6 +218,7 @@ def hsa_active_set(group: torch.Tensor, sched: Schedule, it: int, active_idx: to
 def hsa_select(score: torch.Tensor, counts: Sequence[int], group_out: torch.Tensor, stream=None):
     _need(score, torch.float32, "score")
     _need(group_out, torch.uint8, "group_out")
+    _shape(group_out, (score.numel(),), "group_out")
     arr = (ct.c_int32 * len(counts))(*counts)
     _check("hsa_select", load().hsa_select(_ptr(score), score.numel(), arr, len(counts),
                                            _ptr(group_out), None, 0, _stream(stream)))
@@ -212,6 +232,11 @@ def hsa_euler(x, v_hat, score, v_new, pos, dsigma: float, update_score: bool, ep
         _need(v_new, torch.float32, "v_new")
     _need(pos, torch.int32, "pos")
     N, C = x.shape
+    _shape(v_hat, (N, C), "v_hat")
+    _shape(score, (N,), "score")
+    _shape(pos, (N,), "pos")
+    if v_new is not None:
+        _shape(v_new, (None, C), "v_new")   # rows: every pos[n] >= 0 must index one
     _check("hsa_euler", load().hsa_euler(_ptr(x), _ptr(v_hat), _ptr(score), _ptr(v_new), _ptr(pos),
                                          N, C, dsigma, eps, int(update_score), _stream(stream)))
 
@@ -222,6 +247,10 @@ def hsa_attn_active(q, k, v, o, H: int, Dh: int, scale: Optional[float] = None,
     for t in (k, v, o):
         _need(t, q.dtype, "k/v/o")
     nA, nkv = q.shape[0], k.shape[0]
+    _shape(q, (nA, H * Dh), "q")
+    _shape(k, (nkv, H * Dh), "k")
+    _shape(v, (nkv, H * Dh), "v")
+    _shape(o, (nA, H * Dh), "o")
     if scale is None:
         scale = Dh ** -0.5
     need = hsa_attn_workspace_size(nA, nkv, H, Dh)
@@ -235,6 +264,7 @@ def hsa_attn_active(q, k, v, o, H: int, Dh: int, scale: Optional[float] = None,
 def hsa_layernorm(h, out, stream=None):
     _need(h, torch.float32, "h")
     rows, D = h.shape
+    _shape(out, (rows, D), "out")
     _check("hsa_layernorm", load().hsa_layernorm(_ptr(h), _ptr(out), rows, D, _dt(out), _stream(stream)))
 
 
@@ -243,6 +273,9 @@ def hsa_embed(x, active_idx, n_active: int, w_in, h, stream=None):
     _need(h, torch.float32, "h")
     _need(active_idx, torch.int32, "active_idx")
     D, C = w_in.shape
+    _shape(x, (None, C), "x")
+    _rows(active_idx, n_active, None, "active_idx")
+    _rows(h, n_active, D, "h")
     _check("hsa_embed", load().hsa_embed(_ptr(x), _ptr(active_idx), _ptr(w_in), _ptr(h), n_active, C, D,
                                          _dt(w_in), _stream(stream)))
 
@@ -251,6 +284,8 @@ def hsa_unembed(h, w_out, v_new, n_active: int, stream=None):
     _need(h, torch.float32, "h")
     _need(v_new, torch.float32, "v_new")
     C, D = w_out.shape
+    _rows(h, n_active, D, "h")
+    _rows(v_new, n_active, C, "v_new")
     _check("hsa_unembed", load().hsa_unembed(_ptr(h), _ptr(w_out), _ptr(v_new), n_active, D, C,
                                              _dt(w_out), _stream(stream)))
 
@@ -258,6 +293,10 @@ def hsa_unembed(h, w_out, v_new, n_active: int, stream=None):
 def hsa_linear(a, w, out, act: int = 0, M: Optional[int] = None, stream=None):
     M = a.shape[0] if M is None else M
     Nout, K = w.shape
+    _need(w, a.dtype, "w")
+    _need(out, a.dtype, "out")
+    _rows(a, M, K, "a")
+    _rows(out, M, Nout, "out")
     _check("hsa_linear", load().hsa_linear(_ptr(a), _ptr(w), _ptr(out), M, Nout, K, act, _dt(a),
                                            _stream(stream)))
 
@@ -266,6 +305,9 @@ def hsa_linear_residual(a, w, h, M: Optional[int] = None, stream=None):
     _need(h, torch.float32, "h")
     M = a.shape[0] if M is None else M
     Nout, K = w.shape
+    _need(w, a.dtype, "w")
+    _rows(a, M, K, "a")
+    _rows(h, M, Nout, "h")
     _check("hsa_linear_residual", load().hsa_linear_residual(_ptr(a), _ptr(w), _ptr(h), M, Nout, K,
                                                              _dt(a), _stream(stream)))
 
@@ -273,6 +315,13 @@ def hsa_linear_residual(a, w, h, M: Optional[int] = None, stream=None):
 def hsa_qkv_scatter(a, active_idx, n_active: int, w_qkv, q_out, k_cache, v_cache, stream=None):
     _need(active_idx, torch.int32, "active_idx")
     N, D = k_cache.shape
+    for t, n in ((w_qkv, "w_qkv"), (q_out, "q_out"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _need(t, a.dtype, n)
+    _shape(v_cache, (N, D), "v_cache")
+    _shape(w_qkv, (3 * D, D), "w_qkv")
+    _rows(a, n_active, D, "a")
+    _rows(q_out, n_active, D, "q_out")
+    _rows(active_idx, n_active, None, "active_idx")
     _check("hsa_qkv_scatter", load().hsa_qkv_scatter(_ptr(a), _ptr(active_idx), _ptr(w_qkv), _ptr(q_out),
                                                      _ptr(k_cache), _ptr(v_cache), n_active, N, D,
                                                      _dt(a), _stream(stream)))
@@ -287,6 +336,23 @@ class DeviceModel:
 
     def __init__(self, dims: Dims, w_in: torch.Tensor, w_out: torch.Tensor, blocks: List[dict]):
         self.dims = dims
+        dt = torch.bfloat16 if dims.dtype == HSA_BF16 else torch.float32
+        N, C, D, F, T = dims.N, dims.C, dims.D, dims.F, dims.n_text
+        if len(blocks) != dims.L:
+            raise ValueError(f"blocks: expected {dims.L}, got {len(blocks)}")
+        shapes = {"w_qkv": (3 * D, D), "w_o": (D, D), "w_1": (F, D), "w_2": (D, F),
+                  "k_cache": (N, D), "v_cache": (N, D)}
+        if T > 0:
+            shapes.update({"w_qx": (D, D), "w_ox": (D, D), "k_text": (T, D), "v_text": (T, D)})
+        for t, shp, n in ((w_in, (D, C), "w_in"), (w_out, (C, D), "w_out")):
+            _need(t, dt, n)
+            _shape(t, shp, n)
+        for l, b in enumerate(blocks):
+            for n, shp in shapes.items():
+                if b.get(n) is None:
+                    raise ValueError(f"block {l}: {n} missing")
+                _need(b[n], dt, f"block {l} {n}")
+                _shape(b[n], shp, f"block {l} {n}")
         self.w_in, self.w_out = w_in.contiguous(), w_out.contiguous()
         self.blocks = [{k: (v.contiguous() if v is not None else None) for k, v in b.items()} for b in blocks]
         arr = (Block * dims.L)()
@@ -306,6 +372,12 @@ class DeviceState:
                  v_hat: Optional[torch.Tensor] = None, score: Optional[torch.Tensor] = None):
         dev = x0.device
         N, C = dims.N, dims.C
+        _shape(x0, (N, C), "x0")
+        _shape(group0, (N,), "group0")
+        if v_hat is not None:
+            _shape(v_hat, (N, C), "v_hat")
+        if score is not None:
+            _shape(score, (N,), "score")
         self.x = x0.to(torch.float32).contiguous().clone()
         self.v_hat = (torch.zeros(N, C, device=dev) if v_hat is None else v_hat.clone().contiguous())
         self.score = (torch.full((N,), float("inf"), device=dev) if score is None
@@ -322,12 +394,18 @@ class DeviceState:
 def hsa_block_forward(model: DeviceModel, layer: int, h, active_idx, n_active: int,
                       ws: torch.Tensor, stream=None):
     _need(h, torch.float32, "h")
+    _need(active_idx, torch.int32, "active_idx")
+    _rows(h, n_active, model.dims.D, "h")
+    _rows(active_idx, n_active, None, "active_idx")
     _check("hsa_block_forward", load().hsa_block_forward(ct.byref(model.c), layer, _ptr(h), _ptr(active_idx),
                                                          n_active, _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def hsa_step(model: DeviceModel, sched: Schedule, state: DeviceState, it: int, sigma_i: float,
              sigma_next: float, regroup: bool, v_field: Optional[torch.Tensor] = None, stream=None):
+    if v_field is not None:
+        _need(v_field, torch.float32, "v_field")
+        _shape(v_field, (model.dims.N, model.dims.C), "v_field")
     _check("hsa_step", load().hsa_step(ct.byref(model.c), ct.byref(sched), ct.byref(state.c), it,
                                        float(sigma_i), float(sigma_next), int(regroup), _ptr(v_field),
                                        _stream(stream)))
