@@ -94,17 +94,19 @@ def test_block_forward_small_bf16(n_text):
     assert rel_l2(host(m.blocks[0]["v_cache"])[idx], vref[idx]) < 5e-3
 
 
-@pytest.mark.parametrize("frac", [0.25])
-def test_block_forward_full_size_sampled_rows(frac):
+@pytest.mark.parametrize("frac,pattern", [(0.25, "random"), (0.25, "blob"), (0.0625, "blob")])
+def test_block_forward_full_size_sampled_rows(frac, pattern):
     """Wan-1.3B-shaped block (D 1536, 12x128 heads, F 8960) over N = 32760 cached
-    rows with 25% active: every active row's K/V goes through the oracle, the
-    block output is checked on 48 sampled active rows."""
+    rows, active rows drawn at random or as contiguous spatial blobs (per frame
+    the tokens nearest a drifting centre): every active row's K/V goes through
+    the oracle, the block output is checked on 48 sampled active rows."""
     c = synth.CONFIGS[2]
     nA = synth.n_active_for_fraction(c.N, frac)
-    say(f"block_forward full-size nA={nA}")
+    say(f"block_forward full-size nA={nA} {pattern}")
     om = oracle_model(c)
     kc, vc = synth.kv_cache(c)
-    idx = synth.active_random(c, nA)
+    idx = synth.active_random(c, nA) if pattern == "random" else synth.active_blob(c, nA)
+    assert idx.size == nA and np.all(np.diff(idx) > 0)
     h = synth.hidden_states(c, nA)
     m = device_model(c, om, kc[None], vc[None])
     ws = torch.empty(H.hsa_workspace_size(m.dims), dtype=torch.uint8, device=DEV)
