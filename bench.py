@@ -11,7 +11,8 @@ cached Euler + score.  Inputs (random-init weights, mid-run K/V caches and
 sampler state) are generated on the device before timing.
 
 Also measured in the same run: the attention kernel alone (HIP events on its
-stream), the full T = 40 sampling loop from fresh latents, iteration time
+stream), also at other active fractions and at the 14B-shaped layer, the full
+T = 40 sampling loop from fresh latents, iteration time
 against the active fraction, the Euler pass on a working set past the
 Infinity Cache, attainable peaks (an MFMA-only probe kernel and a 256 MiB
 device copy) and the CPU oracle on a bounded sample.
@@ -50,6 +51,8 @@ def parse():
     p.add_argument("--attn-reps", type=int, default=50)
     p.add_argument("--no-loop", action="store_true", help="skip the full T=40 sampling loop")
     p.add_argument("--no-peaks", action="store_true", help="skip the attainable-peak probes")
+    p.add_argument("--no-sweep", action="store_true",
+                   help="skip the attention sweep over active fractions and the 14B-shaped layer")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-scaling", action="store_true", help="skip the iteration-time vs active-fraction sweep")
     p.add_argument("--cpu-rows", type=int, default=2048)
@@ -223,6 +226,42 @@ def time_attention(H, model, c, n_active, reps, warmup: int = 10):
     return start.elapsed_time(end) / 1e3 / reps
 
 
+def attention_sweep(H, model, c, fracs=(1.0, 0.5, 0.25, 0.125, 0.0625, 0.05), reps: int = 10):
+    """Attention alone at other active fractions of the same stack (K/V of the
+    stack's layers, rotating), and at the 14B-shaped layer: N = 75600 cached
+    rows, |A| = 18900 (25%), 40 heads x 128."""
+    out = {"N": c.N, "heads": c.H, "frac": list(fracs), "n_active": [], "tflops": []}
+    for f in fracs:
+        nA = synth.n_active_for_fraction(c.N, f)
+        t = time_attention(H, model, c, nA, reps, warmup=3)
+        out["n_active"].append(nA)
+        out["tflops"].append(round(4.0 * nA * c.N * c.D / t / 1e12, 1))
+    c4 = synth.CONFIGS[4]
+    nA = c4.counts()[0]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(4 * 1000 + 5)
+    kc = torch.randn((c4.N, c4.D), generator=g, device="cuda").to(torch.bfloat16)
+    vc = torch.randn((c4.N, c4.D), generator=g, device="cuda").to(torch.bfloat16)
+    q = torch.randn((nA, c4.D), generator=g, device="cuda").to(torch.bfloat16)
+    o = torch.empty_like(q)
+    ws = torch.empty(max(1, H.hsa_attn_workspace_size(nA, c4.N, c4.H, c4.Dh)), dtype=torch.uint8,
+                     device="cuda")
+    for _ in range(2):
+        H.hsa_attn_active(q, kc, vc, o, c4.H, c4.Dh, ws=ws)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(5):
+        H.hsa_attn_active(q, kc, vc, o, c4.H, c4.Dh, ws=ws)
+    e.record()
+    torch.cuda.synchronize()
+    t = s.elapsed_time(e) / 1e3 / 5
+    out["wan14b_shape"] = {"N": c4.N, "n_active": nA, "heads": c4.H, "head_dim": c4.Dh,
+                           "ms": round(t * 1e3, 2), "tflops": round(4.0 * nA * c4.N * c4.D / t / 1e12, 1)}
+    del kc, vc, q, o, ws
+    return out
+
+
 def sampling_loop(H, model, c, sigma):
     """The whole sampler: iterations 0..T-1 of hsa_step from fresh latents (all
     groups active at i = 0, regrouping at i = 10, 20, 30), one device
@@ -371,6 +410,8 @@ def main():
         peaks = attainable_peaks()
         out["attainable"] = peaks
         out["roofline"]["frac_of_attainable"] = round(attn_tflops / peaks["mfma_bf16_tflops"], 4)
+    if not args.no_sweep:
+        out["attention_sweep"] = attention_sweep(H, model, c)
     if not args.no_loop:
         out["sampling_loop"] = sampling_loop(H, model, c, sigma)
     if args.euler_tokens > 0:
