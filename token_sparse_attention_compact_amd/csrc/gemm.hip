@@ -138,7 +138,8 @@ __device__ __forceinline__ void wait_barrier() {
 
 // Tile configuration: BM x BN output tile, WM x WN wavefronts (each owning a
 // (BM/WM) x (BN/WN) block of 32x32 MFMA tiles), NST LDS stages of BK=64,
-// tile groups of GM row blocks, at least MINB workgroups per CU (which caps
+// tile groups of GM row blocks by default (the launch may pass another
+// group size), at least MINB workgroups per CU (which caps
 // the registers per lane: 128 at two 512-thread workgroups, 256 at one).
 template <int BM_, int BN_, int WM_, int WN_, int NST_, int GM_, int MINB_ = 2>
 struct GemmCfg {
@@ -160,7 +161,7 @@ struct GemmCfg {
 template <class G, int EPI>
 __global__ __launch_bounds__(G::THREADS, G::MINB) void gemm_bf16_kernel(
     const bf16* __restrict__ A, const bf16* __restrict__ W, int32_t M, int32_t N, int32_t K,
-    EpiArgs ep) {
+    int32_t gm, EpiArgs ep) {
   constexpr int BM = G::BM, BN = G::BN, NST = G::NST;
   __shared__ __attribute__((aligned(1024))) char smem[NST * G::STAGE];
   static_assert(G::FM >= 1 && G::FN >= 1, "wave tile");
@@ -169,7 +170,7 @@ __global__ __launch_bounds__(G::THREADS, G::MINB) void gemm_bf16_kernel(
   const int32_t tm = (M + BM - 1) / BM;
   const int32_t tn = (N + BN - 1) / BN;
   int32_t mi, ni;
-  tile_coords(blockIdx.x, tm, tn, G::GM, mi, ni);
+  tile_coords(blockIdx.x, tm, tn, gm, mi, ni);
   const int32_t m0 = mi * BM;
   const int32_t n0 = ni * BN;
 
@@ -294,6 +295,14 @@ typedef GemmCfg<128, 128, 4, 2, 2, 8> CfgSmall;
 
 enum { kCfgWide, kCfgMain, kCfgSmall };
 
+// Row blocks per tile group of the 256x192 tiles.  Each layer's weights are
+// read cold from HBM once per iteration: with wide outputs (QKV, MLP up) two
+// row blocks per group keep more of W's column tiles streaming at once
+// (interleaved runs over 8 rotating weight sets: MLP up 863 -> 931, QKV
+// 878 -> 904 TFLOP/s); the narrow, long-K shapes (out-projection, MLP down)
+// do best with four.
+int32_t wide_group_rows(int32_t N) { return N > 2048 ? 2 : CfgWide::GM; }
+
 // Cost model: a CU works through ceil(tiles / 256) tiles of its shape one
 // after another (two co-resident workgroups share the CU's MFMA rate), so
 // time ~ ceil(tiles / 256) * tile area / relative efficiency.  Ties go to
@@ -361,10 +370,10 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 }
 
 template <class G, int EPI>
-void launch_bf16(const void* a, const void* w, int32_t M, int32_t N, int32_t K, const EpiArgs& ep,
-                 hipStream_t s) {
+void launch_bf16(const void* a, const void* w, int32_t M, int32_t N, int32_t K, int32_t gm,
+                 const EpiArgs& ep, hipStream_t s) {
   const int32_t tiles = cdiv(M, G::BM) * cdiv(N, G::BN);
-  gemm_bf16_kernel<G, EPI><<<tiles, G::THREADS, 0, s>>>((const bf16*)a, (const bf16*)w, M, N, K, ep);
+  gemm_bf16_kernel<G, EPI><<<tiles, G::THREADS, 0, s>>>((const bf16*)a, (const bf16*)w, M, N, K, gm, ep);
 }
 
 template <int EPI>
@@ -373,9 +382,11 @@ hsa_status run(const void* a, const void* w, int32_t M, int32_t N, int32_t K, hs
   if (dt == HSA_BF16) {
     if (N % 4 != 0 || (EPI == EPI_QKV_SCATTER && ep.D % 4 != 0)) return HSA_ERR_SHAPE;
     switch (pick_cfg(M, N)) {
-      case kCfgWide: launch_bf16<CfgWide, EPI>(a, w, M, N, K, ep, s); break;
-      case kCfgMain: launch_bf16<CfgMain, EPI>(a, w, M, N, K, ep, s); break;
-      default: launch_bf16<CfgSmall, EPI>(a, w, M, N, K, ep, s); break;
+      case kCfgWide:
+        launch_bf16<CfgWide, EPI>(a, w, M, N, K, wide_group_rows(N), ep, s);
+        break;
+      case kCfgMain: launch_bf16<CfgMain, EPI>(a, w, M, N, K, CfgMain::GM, ep, s); break;
+      default: launch_bf16<CfgSmall, EPI>(a, w, M, N, K, CfgSmall::GM, ep, s); break;
     }
   } else {
     dim3 grid(cdiv(N, FT), cdiv(M, FT));
