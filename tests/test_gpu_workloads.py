@@ -173,3 +173,61 @@ def test_churn_regime_euler_score_select():
             np.testing.assert_array_equal(np.isfinite(host(st.score)), fin)
             if fin.any():
                 assert rel_l2(host(st.score)[fin], ost.score[fin]) < 1e-5
+
+
+def test_churn_regime_whole_sampling_run():
+    """All 40 iterations of the aggressive regime (budgets {40, 10, 5}, churn
+    field replacing v_new).  At each regroup (10, 20, 30) the GPU's grouping
+    must be a valid ranking of its own scores and agree with the oracle on
+    every token clear of a boundary; the oracle then adopts the GPU's groups
+    (ties at a boundary may fall either way), so every other iteration is
+    compared exactly: active sets bit for bit, v_hat exactly, x and scores
+    to float32 rounding."""
+    c = synth.CONFIGS[5]
+    say("churn regime, 40 iterations")
+    field = synth.ChurnField(c)
+    dt = torch.bfloat16
+    io = synth.io_weights(c)
+    w = synth.block_weights(c, 0)
+    blk = {k: dev(w[k], dt) for k in ("w_qkv", "w_o", "w_1", "w_2")}
+    blk.update(k_cache=torch.zeros(c.N, c.D, dtype=dt, device=DEV),
+               v_cache=torch.zeros(c.N, c.D, dtype=dt, device=DEV))
+    m = H.DeviceModel(H.make_dims(c.N, c.C, c.D, c.H, c.Dh, c.F, 1, 0, dt), dev(io["w_in"], dt),
+                      dev(io["w_out"], dt), [blk])
+    sched = H.make_schedule(c.T, c.budgets, c.counts())
+    osched = O.Schedule(c.T, list(c.budgets), c.counts())
+    sigma = synth.sigma_schedule(c.T)
+    x0, g0 = synth.x0(c), synth.group0(c)
+    st = H.DeviceState(m.dims, dev(x0), dev(g0, torch.uint8))
+    ost = O.State(x0.astype(np.float64), np.zeros((c.N, c.C)), np.full(c.N, np.inf), g0.copy(),
+                  np.zeros((0,)), np.zeros((0,)))
+    bounds = np.cumsum(c.counts())[:-1]
+    for i in range(c.T):
+        regroup = i in c.regroup
+        vf = field(i)
+        H.hsa_step(m, sched, st, i, float(sigma[i]), float(sigma[i + 1]), regroup, dev(vf))
+        torch.cuda.synchronize()
+        pre = ost.score.copy()
+        out = O.field_iteration(osched, ost, i, sigma[i], sigma[i + 1], regroup, vf)
+        if regroup:
+            g_gpu = st.group.cpu().numpy()
+            assert np.bincount(g_gpu, minlength=len(c.counts())).tolist() == c.counts()
+            srt = np.sort(pre)[::-1]
+            t = srt[bounds]
+            clear = np.all(np.abs(pre[:, None] - t[None, :]) > 1e-4 * np.abs(t[None, :]), axis=1)
+            np.testing.assert_array_equal(g_gpu[clear], ost.group[clear])
+            # continue from the GPU's grouping: redo the oracle's iteration with it
+            ost.group = g_gpu.copy()
+            ost.x[:] = xs_before
+            ost.v_hat[:] = vh_before
+            ost.score[:] = pre
+            out = O.field_iteration(osched, ost, i, sigma[i], sigma[i + 1], False, vf)
+        nA = out["active_idx"].size
+        np.testing.assert_array_equal(st.active_idx[:nA].cpu().numpy(), out["active_idx"])
+        np.testing.assert_array_equal(host(st.v_hat), ost.v_hat)
+        assert rel_l2(host(st.x), ost.x) < 1e-6
+        fin = np.isfinite(ost.score)
+        np.testing.assert_array_equal(np.isfinite(host(st.score)), fin)
+        if fin.any():
+            assert rel_l2(host(st.score)[fin], ost.score[fin]) < 1e-5
+        xs_before, vh_before = ost.x.copy(), ost.v_hat.copy()
