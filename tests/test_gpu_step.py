@@ -304,3 +304,48 @@ def test_zero_row_calls_are_no_ops():
     H.hsa_layernorm(torch.zeros(0, D, device=DEV), sentinel[:0])
     torch.cuda.synchronize()
     assert torch.all(sentinel == 7.0)
+
+
+def test_step_graph_capture_replays_match_eager():
+    """hsa_step enqueues kernels only (no allocation, copy, memset or
+    synchronisation), so a caller can capture one iteration in a HIP graph.
+    Three replays from the same starting state, with other device work in
+    between, each equal the eager iteration bit for bit (regroup included)."""
+    c = small_bf16()
+    i = 10
+    say("hsa_step graph capture")
+    om = oracle_model(c)
+    s0 = synth.mid_run_state(c)
+    m = device_model(c, om, s0["k_cache"], s0["v_cache"])
+    sched = H.make_schedule(c.T, c.budgets, c.counts())
+    sigma = synth.sigma_schedule(c.T)
+    st = H.DeviceState(m.dims, dev(s0["x"]), dev(s0["group"], torch.uint8), dev(s0["v_hat"]),
+                       dev(s0["score"]))
+    bufs = [st.x, st.v_hat, st.score, st.group] + [b[n] for b in m.blocks for n in ("k_cache", "v_cache")]
+    init = [b.clone() for b in bufs]
+
+    def restore():
+        for b, v in zip(bufs, init):
+            b.copy_(v)
+
+    def step():
+        H.hsa_step(m, sched, st, i, float(sigma[i]), float(sigma[i + 1]), True)
+
+    restore()
+    step()
+    torch.cuda.synchronize()
+    eager = [b.clone() for b in bufs]
+    restore()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    other = torch.randn(512, 512, device=DEV)
+    for rep in range(3):
+        restore()
+        other = other @ other.T / 512.0        # unrelated eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        for b, e in zip(bufs, eager):
+            assert torch.equal(b, e), f"replay {rep} differs from the eager iteration"
