@@ -51,6 +51,7 @@ def parse():
     p.add_argument("--attn-reps", type=int, default=50)
     p.add_argument("--no-loop", action="store_true", help="skip the full T=40 sampling loop")
     p.add_argument("--no-peaks", action="store_true", help="skip the attainable-peak probes")
+    p.add_argument("--no-graph", action="store_true", help="skip the graph-replay timing of the step")
     p.add_argument("--no-sweep", action="store_true",
                    help="skip the attention sweep over active fractions and the 14B-shaped layer")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -201,6 +202,26 @@ def timed_steps(H, model, sched, state, sigma, steps, warmup):
         H.hsa_step(model, sched, state, ITER, float(sigma[ITER]), float(sigma[ITER + 1]), True)
     torch.cuda.synchronize()
     return time.perf_counter() - t0
+
+
+def graph_steps(H, model, sched, state, sigma, steps: int):
+    """The timed step captured once in a HIP graph (torch.cuda.graph over the
+    library's stream-ordered launches) and replayed: iterations/s without
+    per-launch host overhead."""
+    g = torch.cuda.CUDAGraph()
+    H.hsa_step(model, sched, state, ITER, float(sigma[ITER]), float(sigma[ITER + 1]), True)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        H.hsa_step(model, sched, state, ITER, float(sigma[ITER]), float(sigma[ITER + 1]), True)
+    for _ in range(2):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    t = (time.perf_counter() - t0) / steps
+    return {"ms_per_step": round(t * 1e3, 3), "iter_per_s": round(1.0 / t, 4), "steps": steps}
 
 
 def time_attention(H, model, c, n_active, reps, warmup: int = 10):
@@ -406,6 +427,8 @@ def main():
                      "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "avg_launch_us": round(t_attn * 1e6, 2),
                      "traffic": recorded_traffic()},
     }
+    if not args.no_graph:
+        out["graph_replay"] = graph_steps(H, model, sched, state, sigma, args.steps)
     if not args.no_peaks:
         peaks = attainable_peaks()
         out["attainable"] = peaks
