@@ -226,6 +226,40 @@ def test_linear_bf16(M, N, K):
     assert rel_l2(host(th), h0 + ref) < 1e-5
 
 
+def test_linear_bf16_random_shapes():
+    """Seeded random GEMM shapes (ragged M and N, K a multiple of 64) through
+    every tile shape the library may pick, with each fused epilogue."""
+    rs = np.random.default_rng(2024)
+    for case in range(10):
+        M = int(rs.integers(1, 3000))
+        N = 4 * int(rs.integers(1, 1300))
+        K = 64 * int(rs.integers(1, 40))
+        say(f"linear bf16 random M={M} N={N} K={K}")
+        a = bf(rs.standard_normal((M, K)))
+        w = bf(rs.standard_normal((N, K)) / np.sqrt(K))
+        ref = a.astype(np.float64) @ w.T.astype(np.float64)
+        out = torch.empty(M, N, dtype=torch.bfloat16, device=DEV)
+        act = case % 2
+        H.hsa_linear(dev(a, torch.bfloat16), dev(w, torch.bfloat16), out, act=act)
+        assert rel_l2(host(out), O.gelu_tanh(ref) if act else ref) < 5e-3, (M, N, K, act)
+        h0 = rs.standard_normal((M, N)).astype(np.float32)
+        th = dev(h0)
+        H.hsa_linear_residual(dev(a, torch.bfloat16), dev(w, torch.bfloat16), th)
+        assert rel_l2(host(th), h0 + ref) < 1e-5, (M, N, K)
+
+
+def test_attention_random_shapes():
+    """Seeded random attention shapes (query count, cache rows and heads; the
+    split plan and the partial last tile vary with them) against the oracle."""
+    rs = np.random.default_rng(77)
+    for _ in range(8):
+        nA = int(rs.integers(1, 1500))
+        nkv = int(rs.integers(1, 9000))
+        Hh = int(rs.integers(1, 4))
+        say(f"attention random nA={nA} nkv={nkv} H={Hh}")
+        _attn_case(nA, nkv, Hh, 128, torch.bfloat16, TOL_BF16, seed=int(rs.integers(0, 1000)))
+
+
 @pytest.mark.parametrize("M,N,K", [(1, 64, 4), (77, 384, 128), (256, 512, 512), (130, 100, 36)])
 def test_linear_f32(M, N, K):
     rs = np.random.default_rng(M + N + K)
