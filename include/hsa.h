@@ -128,7 +128,12 @@ hsa_status hsa_n_active(const hsa_schedule *sched, int32_t iter, int32_t *n_acti
  * ascending indices of tokens n with iter mod (T/budget[group[n]]) == 0 (or
  * all tokens inside the phase window) into active_idx[0..|A_i|), pos[N] as
  * the inverse map (-1 for skipped tokens) and |A_i| into *n_active_dev
- * (device int32).  Bit-exact; group values must be < sched->K. */
+ * (device int32).  Bit-exact; group values must be < sched->K, and group k
+ * must hold exactly sched->count[k] tokens (select's output always does).
+ * Otherwise *n_active_dev differs from hsa_n_active(): active_idx is still
+ * written up to hsa_n_active() entries (padded with token 0) and tokens past
+ * them are marked skipped, so every later access stays in bounds, but the
+ * iteration's results are meaningless. */
 hsa_status hsa_active_set(const uint8_t *group, int32_t N, const hsa_schedule *sched,
                           int32_t iter, int32_t *active_idx, int32_t *pos,
                           int32_t *n_active_dev, void *stream);

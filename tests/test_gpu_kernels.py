@@ -54,6 +54,38 @@ def test_active_set_bit_exact(N):
         np.testing.assert_array_equal(pos.cpu().numpy(), ref_pos)
 
 
+def test_active_set_groups_inconsistent_with_counts_stay_in_bounds():
+    """Groups that do not hold count[k] tokens (a caller error): the device
+    count reports the real |A_i|, while active_idx is written up to the
+    closed-form |A_i| that sizes the later launches (padded with token 0,
+    surplus tokens marked skipped), so nothing downstream reads an unwritten
+    or out-of-range index."""
+    N, T, budgets = 5000, 40, [40, 20, 10]
+    rs = np.random.default_rng(11)
+    group = rs.integers(0, 3, N).astype(np.uint8)
+    real = np.bincount(group, minlength=3)
+    for delta in (+300, -300):                       # schedule claims more / fewer full-budget tokens
+        counts = [int(real[0] + delta), int(real[1] - delta), int(real[2])]
+        sched = H.make_schedule(T, budgets, counts)
+        idx = torch.full((N,), -7, dtype=torch.int32, device=DEV)
+        pos = torch.full((N,), -7, dtype=torch.int32, device=DEV)
+        nd = torch.zeros(1, dtype=torch.int32, device=DEV)
+        i = 1                                        # only group 0 is active at odd i
+        H.hsa_active_set(dev(group, torch.uint8), sched, i, idx, pos, nd)
+        torch.cuda.synchronize()
+        expected = H.hsa_n_active(sched, i)
+        ref_idx, _ = O.active_set(group, budgets, T, i)
+        assert int(nd.item()) == ref_idx.size == real[0]
+        got = idx[:expected].cpu().numpy()
+        assert np.all((got >= 0) & (got < N))
+        k = min(expected, ref_idx.size)
+        np.testing.assert_array_equal(got[:k], ref_idx[:k])
+        assert np.all(got[k:] == 0)
+        p = pos.cpu().numpy()
+        assert np.all((p >= -1) & (p < expected))
+        np.testing.assert_array_equal(np.flatnonzero(p >= 0), ref_idx[:k])
+
+
 def test_active_set_phase_window():
     N, T = 1000, 40
     rs = np.random.default_rng(5)

@@ -10,6 +10,12 @@
 // and a scan of the 16 wave totals in LDS; a running total carries across
 // chunks.  Output order is ascending token index, so the result is unique and
 // bit-exact.
+//
+// The launches that follow are sized by the host's closed-form |A_i|
+// (`expected`).  Groups that do not hold exactly count[k] tokens (a caller
+// error) must still leave every later access in bounds: entries past the
+// actual count are filled with token 0, and tokens past `expected` are
+// marked skipped.  *n_active receives the actual count.
 #include "common.h"
 
 namespace hsa {
@@ -21,7 +27,7 @@ constexpr int kPerThread = 4;
 constexpr int kChunk = kThreads * kPerThread;
 
 __global__ __launch_bounds__(kThreads) void active_set_kernel(
-    const uint8_t* __restrict__ group, int32_t N, uint32_t active_groups,
+    const uint8_t* __restrict__ group, int32_t N, uint32_t active_groups, int32_t expected,
     int32_t* __restrict__ active_idx, int32_t* __restrict__ pos, int32_t* __restrict__ n_active) {
   __shared__ int32_t wave_tot[kWaves];
   const int tid = threadIdx.x;
@@ -60,27 +66,28 @@ __global__ __launch_bounds__(kThreads) void active_set_kernel(
     for (int j = 0; j < kPerThread; ++j) {
       const int32_t n = t0 + j;
       if (n < N) {
-        if (f[j]) {
+        if (f[j] && p < expected) {
           active_idx[p] = n;
           pos[n] = p;
-          ++p;
         } else {
           pos[n] = -1;
         }
+        p += f[j] ? 1 : 0;
       }
     }
     running += chunk_tot;
     __syncthreads();  // wave_tot is rewritten by the next chunk
   }
+  for (int32_t i = running + tid; i < expected; i += kThreads) active_idx[i] = 0;
   if (tid == 0) *n_active = running;
 }
 
 }  // namespace
 
 hsa_status launch_active_set(const uint8_t* group, int32_t N, uint32_t active_groups,
-                             int32_t* active_idx, int32_t* pos, int32_t* n_active_dev,
-                             hipStream_t s) {
-  active_set_kernel<<<1, kThreads, 0, s>>>(group, N, active_groups, active_idx, pos,
+                             int32_t expected, int32_t* active_idx, int32_t* pos,
+                             int32_t* n_active_dev, hipStream_t s) {
+  active_set_kernel<<<1, kThreads, 0, s>>>(group, N, active_groups, expected, active_idx, pos,
                                            n_active_dev);
   return launch_status();
 }

@@ -261,8 +261,8 @@ hsa_status hsa_active_set(const uint8_t* group, int32_t N, const hsa_schedule* s
   if (iter < 0 || iter >= sched->T) return HSA_ERR_ARG;
   if (!group || !active_idx || !pos || !n_active_dev) return HSA_ERR_ARG;
   if (!aligned16(active_idx) || !aligned16(pos)) return HSA_ERR_ALIGN;
-  return launch_active_set(group, N, active_group_mask(sched, iter), active_idx, pos,
-                           n_active_dev, as_stream(stream));
+  return launch_active_set(group, N, active_group_mask(sched, iter), n_active_of(sched, iter),
+                           active_idx, pos, n_active_dev, as_stream(stream));
 }
 
 hsa_status hsa_select(const float* score, int32_t N, const int32_t* count, int32_t K,
@@ -434,7 +434,7 @@ hsa_status hsa_step(const hsa_model* model, const hsa_schedule* sched, hsa_state
   if (regroup) RETURN_IF(launch_select(st->score, d.N, sched->count, sched->K, st->group, s));
   // 2. active set; its size is known on the host in closed form
   const int32_t nA = n_active_of(sched, iter);
-  RETURN_IF(launch_active_set(st->group, d.N, active_group_mask(sched, iter), st->active_idx,
+  RETURN_IF(launch_active_set(st->group, d.N, active_group_mask(sched, iter), nA, st->active_idx,
                               st->pos, n_dev, s));
   // 3. model on the active rows
   if (nA > 0) {
