@@ -12,7 +12,8 @@ sampler state) are generated on the device before timing.
 
 Also measured in the same run: the attention kernel alone (HIP events on its
 stream), also at other active fractions and at the 14B-shaped layer, the full
-T = 40 sampling loop from fresh latents, iteration time
+T = 40 sampling loop from fresh latents (also under other schedules and
+against dense sampling), iteration time
 against the active fraction, the Euler pass on a working set past the
 Infinity Cache, attainable peaks (an MFMA-only probe kernel and a 256 MiB
 device copy) and the CPU oracle on a bounded sample.
@@ -52,6 +53,8 @@ def parse():
     p.add_argument("--no-loop", action="store_true", help="skip the full T=40 sampling loop")
     p.add_argument("--no-peaks", action="store_true", help="skip the attainable-peak probes")
     p.add_argument("--no-graph", action="store_true", help="skip the graph-replay timing of the step")
+    p.add_argument("--no-presets", action="store_true",
+                   help="skip the sampler under other schedules and the dense reference loop")
     p.add_argument("--no-sweep", action="store_true",
                    help="skip the attention sweep over active fractions and the 14B-shaped layer")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -283,18 +286,22 @@ def attention_sweep(H, model, c, fracs=(1.0, 0.5, 0.25, 0.125, 0.0625, 0.05), re
     return out
 
 
-def sampling_loop(H, model, c, sigma):
-    """The whole sampler: iterations 0..T-1 of hsa_step from fresh latents (all
-    groups active at i = 0, regrouping at i = 10, 20, 30), one device
-    synchronisation at the end."""
+def sampling_loop(H, model, c, sigma, budgets=None, counts=None, regroup_at=None):
+    """The whole sampler: iterations 0..T-1 of hsa_step from fresh latents
+    (every group active at i = 0), regrouping at the start of the iterations in
+    regroup_at, one device synchronisation at the end.  Defaults: the stack's
+    schedule (budgets 40/20/10 at 25/25/50%, regrouping at 10, 20, 30)."""
     dev = "cuda"
+    budgets = c.budgets if budgets is None else budgets
+    counts = c.counts() if counts is None else counts
+    regroup_at = set(c.regroup if regroup_at is None else regroup_at)
     g = torch.Generator(device=dev)
     g.manual_seed(3 * 1000 + 9)
     x0 = torch.randn((c.N, c.C), generator=g, device=dev)
-    group0 = torch.from_numpy(synth.group0(c)).to(dev)
+    group0 = torch.from_numpy(synth.group0(c.with_(budgets=tuple(budgets),
+                                                   shares=tuple(n / c.N for n in counts)))).to(dev)
     state = H.DeviceState(model.dims, x0, group0)
-    sched = H.make_schedule(c.T, c.budgets, c.counts())
-    regroup_at = set(c.regroup)
+    sched = H.make_schedule(c.T, budgets, counts)
     n_act = [H.hsa_n_active(sched, i) for i in range(c.T)]
     torch.cuda.synchronize()
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -308,7 +315,25 @@ def sampling_loop(H, model, c, sigma):
     del state
     return {"iterations": c.T, "s": round(t, 3), "iter_per_s": round(c.T / t, 3),
             "mean_active_frac": round(sum(n_act) / (c.T * c.N), 4), "regroup_at": sorted(regroup_at),
-            "finite": ok}
+            "budgets": list(budgets), "counts": list(counts), "finite": ok}
+
+
+def schedule_presets(H, model, c, sigma, moderate):
+    """The sampler under other schedules, against dense sampling (every token
+    every step): runtime of each relative to the dense 40-step loop."""
+    N = c.N
+    c5 = synth.CONFIGS[5]                      # budgets 40/10/5 at 12.5/37.5/50%
+    assert c5.N == N and c5.T == c.T
+    runs = {
+        "dense": sampling_loop(H, model, c, sigma, (c.T,), [N], ()),
+        "moderate_dynamic": moderate,
+        "moderate_static": sampling_loop(H, model, c, sigma, c.budgets, c.counts(), ()),
+        "aggressive_dynamic": sampling_loop(H, model, c, sigma, c5.budgets, c5.counts(), c5.regroup),
+    }
+    dense = runs["dense"]["s"]
+    for r in runs.values():
+        r["runtime_vs_dense"] = round(r["s"] / dense, 4)
+    return runs
 
 
 def step_scaling(H, model, state, c, sigma, reps: int = 5):
@@ -437,6 +462,8 @@ def main():
         out["attention_sweep"] = attention_sweep(H, model, c)
     if not args.no_loop:
         out["sampling_loop"] = sampling_loop(H, model, c, sigma)
+        if not args.no_presets:
+            out["schedule_presets"] = schedule_presets(H, model, c, sigma, out["sampling_loop"])
     if args.euler_tokens > 0:
         out["euler_hbm"] = time_euler(H, args.euler_tokens)
         if "attainable" in out:
