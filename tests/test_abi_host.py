@@ -144,3 +144,14 @@ def test_binding_rejects_mismatched_shapes():
     blk["v_cache"] = torch.zeros(64, 256, dtype=torch.float32)
     with pytest.raises(ValueError, match="v_cache: expected"):
         H.DeviceModel(d, torch.zeros(256, 16, dtype=bf), torch.zeros(16, 256, dtype=bf), [blk])
+
+
+def test_probe_library_exports():
+    """The benchmark's attainable-peak probes are built beside the library."""
+    from token_sparse_attention_compact_amd import build as B
+    lib = ct.CDLL(B.PROBE_LIB)
+    for name in ("hsa_probe_mfma_peak", "hsa_probe_copy"):
+        assert hasattr(lib, name)
+    lib.hsa_probe_copy.argtypes = [ct.c_void_p, ct.c_void_p, ct.c_int64, ct.c_void_p]
+    assert lib.hsa_probe_copy(None, None, 1024, None) == -1          # rejected before any launch
+    assert lib.hsa_probe_mfma_peak(0, 10, None, None) == -1
