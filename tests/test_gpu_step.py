@@ -152,15 +152,21 @@ def select_margin(score, counts):
     return min(gaps) if gaps else np.inf
 
 
-@pytest.mark.parametrize("variant", ["cfg1", "empty_active_sets"])
+@pytest.mark.parametrize("variant", ["cfg1", "empty_active_sets", "static_groups", "regroup_every_2"])
 def test_step_cfg1_full_run_f32(variant):
     """DiT-lite float32: 8 iterations, budgets {8,4}, regrouping from i = 3 on.
-    Variant with an empty full-budget group (budgets {8,4,2}, shares 0/50/50):
-    every odd iteration has |A_i| = 0 and is the cached Euler step alone."""
+    Variants: an empty full-budget group (budgets {8,4,2}, shares 0/50/50:
+    every odd iteration has |A_i| = 0 and is the cached Euler step alone);
+    static groups (never regrouped); three groups regrouped every 2nd
+    iteration (budgets {8,4,2})."""
     c = synth.CONFIGS[1]
     if variant == "empty_active_sets":
         c = c.with_(budgets=(8, 4, 2), shares=(0.0, 0.5, 0.5))
         assert c.counts()[0] == 0
+    elif variant == "static_groups":
+        c = c.with_(regroup=())
+    elif variant == "regroup_every_2":
+        c = c.with_(budgets=(8, 4, 2), shares=(0.25, 0.25, 0.5), regroup=(2, 4, 6))
     say(f"hsa_step cfg1 fp32 full run ({variant})")
     om = oracle_model(c)
     m = device_model(c, om)
