@@ -28,6 +28,11 @@ STREAM_HIDDEN = 6
 STREAM_ACTIVE = 7
 STREAM_FIELD = 8
 STREAM_STATE = 9
+STREAM_FEATURES = 10
+
+# Optional Wan-style block features a Config may switch on (names, not flags:
+# each side maps them to its own representation).
+FEATURES = ("qk_norm", "rope3d", "adaln", "cfg")
 
 
 def rng(cfg: int, stream: int, sub: int = 0) -> np.random.Generator:
@@ -68,6 +73,8 @@ class Config:
     n_text: int = 0                     # text tokens for cross-attention (0: none)
     text_dim: int = 0                   # text embedding width
     m: int = 0                          # phase window (first/last m iterations full)
+    features: Tuple[str, ...] = ()      # subset of FEATURES
+    cfg_scale: float = 5.0              # guidance scale when "cfg" is on
 
     @property
     def N(self) -> int:
@@ -164,6 +171,54 @@ def text_inputs(c: Config) -> Dict[str, np.ndarray]:
     if c.dtype == "bf16":
         t, w_t = to_bf16_values(t), to_bf16_values(w_t)
     return {"text": t, "w_t": w_t}
+
+
+def text_inputs_uncond(c: Config) -> np.ndarray:
+    """Second set of text tokens [n_text][text_dim] ~ N(0,1): the condition of the
+    unconditional branch under classifier-free guidance (a stand-in for the
+    encoded empty or negative prompt).  Projected by the same w_t."""
+    t = rng(c.cfg, STREAM_TEXT, 1).standard_normal((c.n_text, c.text_dim), dtype=np.float32)
+    return to_bf16_values(t) if c.dtype == "bf16" else t
+
+
+# ----------------------------------------------------------------------------
+# Optional block features.  Gains, modulation tables and the timestep MLP are
+# float32 in both dtypes (they are small vectors, read once per row).
+# ----------------------------------------------------------------------------
+
+def feature_weights(c: Config, layer: int) -> Dict[str, np.ndarray]:
+    """Per-block feature parameters:
+      q_gain, k_gain [D]: RMSNorm gains of q and k, 1 + N(0, 0.1^2);
+      mod [6][D]: learned modulation table (shift, scale, gate of the attention
+        branch, then of the MLP branch), N(0, 0.1^2) with the gate rows
+        centred on 1 so that both residual branches stay alive."""
+    g = rng(c.cfg, STREAM_FEATURES, 1 + layer)
+    D = c.D
+    q_gain = 1.0 + _normal(g, (D,), 0.1)
+    k_gain = 1.0 + _normal(g, (D,), 0.1)
+    mod = _normal(g, (6, D), 0.1)
+    mod[2] += 1.0
+    mod[5] += 1.0
+    return {"q_gain": q_gain.astype(np.float32), "k_gain": k_gain.astype(np.float32),
+            "mod": mod.astype(np.float32)}
+
+
+def time_weights(c: Config, t_freq: int = 256) -> Dict[str, np.ndarray]:
+    """Timestep MLP and output-head modulation, out-major like every linear map:
+      t_w1 [D][t_freq], t_b1 [D]; t_w2 [D][D], t_b2 [D]; t_w3 [6D][D], t_b3 [6D];
+      head_mod [2][D] (shift, scale of the final LayerNorm).
+    Scales keep the projected modulation around 0.1 in magnitude."""
+    g = rng(c.cfg, STREAM_FEATURES, 0)
+    D = c.D
+    return {
+        "t_w1": _normal(g, (D, t_freq), t_freq ** -0.5),
+        "t_b1": _normal(g, (D,), 0.01),
+        "t_w2": _normal(g, (D, D), D ** -0.5),
+        "t_b2": _normal(g, (D,), 0.01),
+        "t_w3": _normal(g, (6 * D, D), 0.3 * D ** -0.5),
+        "t_b3": _normal(g, (6 * D,), 0.01),
+        "head_mod": _normal(g, (2, D), 0.1),
+    }
 
 
 # ----------------------------------------------------------------------------
