@@ -49,14 +49,55 @@ typedef enum {
 
 typedef enum { HSA_F32 = 0, HSA_BF16 = 1 } hsa_dtype;
 
+/* Optional block features, OR-ed into hsa_dims.features (0: none, the plain
+ * block below).  The pages run HSA on Wan-family DiTs (section 4) but define
+ * none of their layers; each feature follows the published general
+ * definition it is named after:
+ *  HSA_FEAT_QK_NORM  q and k rows, after the projection, are divided by
+ *                    sqrt(mean(x^2) + 1e-6) over the whole width D and
+ *                    multiplied by the block's q_gain / k_gain [D].
+ *  HSA_FEAT_ROPE3D   rotary position embedding of q and k (after the
+ *                    RMSNorm), per head: coordinate pair (2j, 2j+1) turns by
+ *                    pos * 10000^(-j'/p).  A head's P = Dh/2 pairs form a
+ *                    frame section of P - 2*floor(P/3) pairs, then a row and
+ *                    a column section of floor(P/3) pairs each; p is the
+ *                    section's pair count, j' the pair's index in it, pos
+ *                    token n's frame, row or column in the latent grid, n =
+ *                    (f * grid_h + y) * grid_w + x.  The K cache holds
+ *                    rotated keys.
+ *  HSA_FEAT_ADALN    timestep modulation.  t = 1000 * sigma_i; sinusoid
+ *                    s = [cos(t w_k), sin(t w_k)], w_k = 10000^(-k/128),
+ *                    k < 128; e = t_w2 silu(t_w1 s + t_b1) + t_b2 [D];
+ *                    e0 = t_w3 silu(e) + t_b3 [6][D].  Block l uses
+ *                    mod_l + e0 = (shift, scale, gate) of the attention
+ *                    branch, then of the MLP branch: the branch reads
+ *                    LN(h) (1 + scale) + shift and its output is multiplied
+ *                    by gate before the residual add.  Cross-attention is
+ *                    neither modulated nor gated.  The final LayerNorm uses
+ *                    (shift, scale) = head_mod + e.
+ *  HSA_FEAT_CFG      classifier-free guidance with batch 2 (needs
+ *                    n_text > 0): the model runs on the active rows once
+ *                    with (k_text, v_text, k_cache, v_cache) and once with
+ *                    the unconditional set (k_text_u, v_text_u, k_cache_u,
+ *                    v_cache_u); the velocity is v_u + cfg_scale (v_c - v_u). */
+#define HSA_FEAT_QK_NORM 1
+#define HSA_FEAT_ROPE3D 2
+#define HSA_FEAT_ADALN 4
+#define HSA_FEAT_CFG 8
+
 /* Model shape.  N tokens, C latent channels, width D = H * Dh, MLP width F,
- * L blocks, n_text text tokens for cross-attention (0: no cross-attention).
- * bf16 operands are streamed through 32-bit buffer descriptors: every bf16
- * matrix a kernel reads whole (N x D, N x F, weights) must stay below 4 GiB,
- * i.e. N * max(D, F) * 2 < 2^32; larger shapes return HSA_ERR_SHAPE. */
+ * L blocks, n_text text tokens for cross-attention (0: no cross-attention),
+ * `features` a subset of HSA_FEAT_*, (grid_f, grid_h, grid_w) the latent
+ * token grid with grid_f * grid_h * grid_w == N (read with HSA_FEAT_ROPE3D
+ * only).  bf16 operands are streamed through 32-bit buffer descriptors:
+ * every bf16 matrix a kernel reads whole (N x D, N x F, weights) must stay
+ * below 4 GiB, i.e. N * max(D, F) * 2 < 2^32; larger shapes return
+ * HSA_ERR_SHAPE. */
 typedef struct {
   int32_t N, C, D, H, Dh, F, L, n_text;
   hsa_dtype dtype;
+  int32_t features;
+  int32_t grid_f, grid_h, grid_w;
 } hsa_dims;
 
 /* Step schedule (section 2.1).  K groups; budget[k] = s_k steps out of T,
@@ -75,20 +116,32 @@ typedef struct {
  *   k_cache, v_cache [N][D]: the per-layer K/V cache of section 2.2, row n =
  *     token n, head h in columns h*Dh .. h*Dh+Dh-1.
  *   Cross-attention (n_text > 0): w_qx, w_ox [D][D]; k_text, v_text
- *     [n_text][D] (projected once per run by the caller).  NULL otherwise. */
+ *     [n_text][D] (projected once per run by the caller).  NULL otherwise.
+ *   Feature parameters, float32, NULL when their feature is off:
+ *     q_gain, k_gain [D] (HSA_FEAT_QK_NORM); mod [6][D] (HSA_FEAT_ADALN);
+ *     k_text_u, v_text_u [n_text][D] and k_cache_u, v_cache_u [N][D] of the
+ *     unconditional branch (HSA_FEAT_CFG, dtype of hsa_dims). */
 typedef struct {
   const void *w_qkv, *w_o, *w_1, *w_2;
   const void *w_qx, *w_ox;
   void *k_cache, *v_cache;
   const void *k_text, *v_text;
+  const float *q_gain, *k_gain, *mod;
+  const void *k_text_u, *v_text_u;
+  void *k_cache_u, *v_cache_u;
 } hsa_block;
 
 /* Model: embed w_in [D][C] (latent -> width), unembed w_out [C][D]; blocks
- * is a HOST array of L hsa_block. */
+ * is a HOST array of L hsa_block.  HSA_FEAT_ADALN: timestep MLP t_w1
+ * [D][256], t_b1 [D], t_w2 [D][D], t_b2 [D], t_w3 [6D][D], t_b3 [6D] and
+ * head_mod [2][D], all float32 (NULL otherwise).  HSA_FEAT_CFG: cfg_scale
+ * is the guidance scale. */
 typedef struct {
   hsa_dims dims;
   const void *w_in, *w_out;
   const hsa_block *blocks;
+  const float *t_w1, *t_b1, *t_w2, *t_b2, *t_w3, *t_b3, *head_mod;
+  float cfg_scale;
 } hsa_model;
 
 /* Sampler state, all float32 except group/active_idx/pos:
@@ -165,9 +218,11 @@ hsa_status hsa_attn_active(const void *q, const void *k, const void *v, void *o,
                            hsa_dtype dtype, void *ws, size_t ws_bytes, void *stream);
 
 /* Row LayerNorm (no affine, eps 1e-6): out[r] = (h[r]-mean)/sqrt(var+eps),
- * h [rows][D] float32 -> out [rows][D] in dtype. */
-hsa_status hsa_layernorm(const float *h, void *out, int32_t rows, int32_t D, hsa_dtype dtype,
-                         void *stream);
+ * h [rows][D] float32 -> out [rows][D] in dtype.  With shift and scale
+ * ([D] float32, both or neither; the HSA_FEAT_ADALN modulation) out[r] =
+ * LN(h[r]) * (1 + scale) + shift. */
+hsa_status hsa_layernorm(const float *h, void *out, int32_t rows, int32_t D, const float *shift,
+                         const float *scale, hsa_dtype dtype, void *stream);
 
 /* Gather + embed (section 2.2 item 1, the active rows enter the model):
  * h[j] = x[active_idx[j]] w_in^T, x [N][C] float32, w_in [D][C] dtype,
@@ -176,9 +231,11 @@ hsa_status hsa_embed(const float *x, const int32_t *active_idx, const void *w_in
                      int32_t n_active, int32_t C, int32_t D, hsa_dtype dtype, void *stream);
 
 /* Final LayerNorm + unembed: v_new[j] = LN(h[j]) w_out^T, h [n_active][D]
- * float32, w_out [C][D] dtype, v_new [n_active][C] float32. */
+ * float32, w_out [C][D] dtype, v_new [n_active][C] float32.  shift, scale
+ * as for hsa_layernorm (NULL: unmodulated). */
 hsa_status hsa_unembed(const float *h, const void *w_out, float *v_new, int32_t n_active,
-                       int32_t D, int32_t C, hsa_dtype dtype, void *stream);
+                       int32_t D, int32_t C, const float *shift, const float *scale,
+                       hsa_dtype dtype, void *stream);
 
 /* Linear map on rows: out = act(a w^T), a [M][K], w [Nout][K], out [M][Nout],
  * all in dtype; act 0 = identity, 1 = GELU (tanh form).  bf16: K % 64 == 0,
@@ -188,9 +245,10 @@ hsa_status hsa_linear(const void *a, const void *w, void *out, int32_t M, int32_
                       int32_t K, int32_t act, hsa_dtype dtype, void *stream);
 
 /* Linear map added to the float32 residual stream: h += a w^T, a [M][K]
- * dtype, w [Nout][K] dtype, h [M][Nout] float32. */
+ * dtype, w [Nout][K] dtype, h [M][Nout] float32.  With gate ([Nout]
+ * float32, the HSA_FEAT_ADALN gate; NULL: none) h[m][n] += gate[n] (a w^T)[m][n]. */
 hsa_status hsa_linear_residual(const void *a, const void *w, float *h, int32_t M, int32_t Nout,
-                               int32_t K, hsa_dtype dtype, void *stream);
+                               int32_t K, const float *gate, hsa_dtype dtype, void *stream);
 
 /* KV-cache synchronisation steps 1-2 (section 2.2): [q | k | v] = a w_qkv^T
  * for the n_active rows of a; q goes to q_out [n_active][D]; k and v rows
@@ -200,18 +258,44 @@ hsa_status hsa_qkv_scatter(const void *a, const int32_t *active_idx, const void 
                            void *q_out, void *k_cache, void *v_cache, int32_t n_active,
                            int32_t N, int32_t D, hsa_dtype dtype, void *stream);
 
+/* qk-RMSNorm and 3D rotary embedding (HSA_FEAT_QK_NORM / HSA_FEAT_ROPE3D,
+ * whichever dims->features holds; neither: nothing to do) in place on q
+ * [n_active][D] (row j is token active_idx[j]) and on rows active_idx[j] of
+ * k_cache [N][D], dtype of dims.  q_gain, k_gain [D] float32, needed with
+ * HSA_FEAT_QK_NORM. */
+hsa_status hsa_qk_norm_rope(void *q, void *k_cache, const int32_t *active_idx, int32_t n_active,
+                            const hsa_dims *dims, const float *q_gain, const float *k_gain,
+                            void *stream);
+
+/* Timestep embedding of HSA_FEAT_ADALN for sigma (float32, t = 1000 sigma):
+ * e [D] and e0 [6][D], float32 device outputs (e0 also serves as scratch
+ * during the call).  Model weights as in hsa_model. */
+hsa_status hsa_time_embed(const hsa_model *model, float sigma, float *e, float *e0, void *stream);
+
+/* Classifier-free guidance combine (HSA_FEAT_CFG): v = v + g (v_cond - v)
+ * elementwise over rows x C float32 values, v holding the unconditional
+ * velocity on entry. */
+hsa_status hsa_guidance(const float *v_cond, float *v, int32_t rows, int32_t C, float g,
+                        void *stream);
+
 /* One transformer block on the active rows (section 2.2): LN, QKV with cache
  * scatter, active-query attention over all N cached rows, out-projection,
- * optional cross-attention, GELU MLP, residual adds.  h [n_active][D] float32
- * in place; caches of block `layer` updated.  ws as for hsa_step. */
+ * optional cross-attention, GELU MLP, residual adds, with the features of
+ * model->dims.  h [n_active][D] float32 in place; caches of block `layer`
+ * updated.  e0 [6][D]: the timestep projection from hsa_time_embed (needed
+ * with HSA_FEAT_ADALN, else ignored).  branch 0 uses the conditional text
+ * set and caches, 1 the unconditional ones (HSA_FEAT_CFG only).  ws as for
+ * hsa_step. */
 hsa_status hsa_block_forward(const hsa_model *model, int32_t layer, float *h,
-                             const int32_t *active_idx, int32_t n_active, void *ws,
-                             size_t ws_bytes, void *stream);
+                             const int32_t *active_idx, int32_t n_active, const float *e0,
+                             int32_t branch, void *ws, size_t ws_bytes, void *stream);
 
 /* One global HSA iteration `iter` (0-based) from sigma_i to sigma_next:
  *  1. if regroup: group = hsa_select(score, count)   (section 2.1)
  *  2. A_i = hsa_active_set(group, iter)               (sections 2.1, 2.4)
- *  3. h = embed(x[A_i]); L blocks (section 2.2); v_new = unembed(h)
+ *  3. h = embed(x[A_i]); L blocks (section 2.2); v_new = unembed(h); with
+ *     HSA_FEAT_ADALN the timestep embedding of sigma_i first; with
+ *     HSA_FEAT_CFG once per branch, then combined by hsa_guidance
  *  4. if v_field != NULL: v_new[j] = v_field[A_i[j]]  ([N][C] float32; a
  *     synthetic velocity replaces the model's in the Euler/score path)
  *  5. hsa_euler with dsigma = sigma_next - sigma_i, eps = 1e-6, score

@@ -74,7 +74,10 @@ def test_entry_points_reject_bad_arguments_without_a_device():
     assert L.hsa_select(null, 7, counts, 3, null, null, 0, null) == -1
     assert L.hsa_step(null, null, null, 0, 1.0, 0.9, 0, null, null) == -1
     # misaligned device pointer
-    assert L.hsa_layernorm(ct.c_void_p(0x1004), ct.c_void_p(0x2000), 4, 64, 1, null) == -4
+    assert L.hsa_layernorm(ct.c_void_p(0x1004), ct.c_void_p(0x2000), 4, 64, null, null, 1, null) == -4
+    # modulation needs both shift and scale
+    assert L.hsa_layernorm(ct.c_void_p(0x1000), ct.c_void_p(0x2000), 4, 64, ct.c_void_p(0x3000), null, 1,
+                           null) == -1
 
 
 def test_step_rejects_bad_schedule_before_launch():
@@ -155,3 +158,67 @@ def test_probe_library_exports():
     lib.hsa_probe_copy.argtypes = [ct.c_void_p, ct.c_void_p, ct.c_int64, ct.c_void_p]
     assert lib.hsa_probe_copy(None, None, 1024, None) == -1          # rejected before any launch
     assert lib.hsa_probe_mfma_peak(0, 10, None, None) == -1
+
+
+def test_feature_flags_are_validated_on_the_host():
+    L = H.load()
+    n = ct.c_size_t()
+    ok = H.make_dims(32760, 16, 1536, 12, 128, 8960, 30, features=("qk_norm", "rope3d", "adaln"),
+                     grid=(21, 30, 52))
+    assert L.hsa_workspace_size(ct.byref(ok), ct.byref(n)) == 0
+    plain = H.make_dims(32760, 16, 1536, 12, 128, 8960, 30)
+    m = ct.c_size_t()
+    assert L.hsa_workspace_size(ct.byref(plain), ct.byref(m)) == 0
+    assert n.value > m.value                               # timestep vectors
+    bad = H.make_dims(32760, 16, 1536, 12, 128, 8960, 30, features=16)
+    assert L.hsa_workspace_size(ct.byref(bad), ct.byref(n)) == -1   # unknown feature bit
+    bad = H.make_dims(32760, 16, 1536, 12, 128, 8960, 30, features=("rope3d",), grid=(21, 30, 51))
+    assert L.hsa_workspace_size(ct.byref(bad), ct.byref(n)) == -2   # grid does not cover N
+    bad = H.make_dims(32760, 16, 1536, 12, 128, 8960, 30, features=("cfg",))
+    assert L.hsa_workspace_size(ct.byref(bad), ct.byref(n)) == -1   # guidance needs text
+    cfg = H.make_dims(32760, 16, 1536, 12, 128, 8960, 30, n_text=512, features=("cfg",))
+    assert L.hsa_workspace_size(ct.byref(cfg), ct.byref(n)) == 0
+    null = None
+    assert L.hsa_guidance(null, null, 4, 6, 1.0, null) == -2        # C % 4
+    assert L.hsa_guidance(null, null, 4, 8, float("nan"), null) == -1
+    assert L.hsa_qk_norm_rope(null, null, null, 4, ct.byref(ok), null, null, null) == -1
+
+
+def test_feature_parameters_are_required_by_the_model():
+    L = H.load()
+    d = H.make_dims(256, 16, 128, 2, 64, 512, 1, dtype=None, features=("qk_norm",))
+    d.dtype = H.HSA_F32
+    blocks = (H.Block * 1)()
+    for n in ("w_qkv", "w_o", "w_1", "w_2", "k_cache", "v_cache"):
+        setattr(blocks[0], n, 0x1000)
+    m = H.Model(d, 0x1000, 0x1000, blocks)
+    st = H.State(0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 1 << 40)
+    sched = H.make_schedule(8, [8, 4], [128, 128])
+    assert L.hsa_step(ct.byref(m), ct.byref(sched), ct.byref(st), 0, 1.0, 0.875, 0, None, None) == -1
+    blocks[0].q_gain = blocks[0].k_gain = 0x1000
+    d.features = H.FEAT_QK_NORM | H.FEAT_ADALN                 # timestep MLP and mod missing
+    m = H.Model(d, 0x1000, 0x1000, blocks)
+    assert L.hsa_step(ct.byref(m), ct.byref(sched), ct.byref(st), 0, 1.0, 0.875, 0, None, None) == -1
+    assert L.hsa_time_embed(ct.byref(m), 0.5, ct.c_void_p(0x1000), ct.c_void_p(0x1000), None) == -1
+    # time embedding needs the adaLN feature
+    d.features = 0
+    m = H.Model(d, 0x1000, 0x1000, blocks)
+    assert L.hsa_time_embed(ct.byref(m), 0.5, ct.c_void_p(0x1000), ct.c_void_p(0x1000), None) == -1
+
+
+def test_binding_checks_feature_tensors():
+    import torch
+    bf = torch.bfloat16
+    d = H.make_dims(64, 16, 256, 2, 128, 512, 1, features=("qk_norm", "adaln"))
+    blk = {"w_qkv": torch.zeros(768, 256, dtype=bf), "w_o": torch.zeros(256, 256, dtype=bf),
+           "w_1": torch.zeros(512, 256, dtype=bf), "w_2": torch.zeros(256, 512, dtype=bf),
+           "k_cache": torch.zeros(64, 256, dtype=bf), "v_cache": torch.zeros(64, 256, dtype=bf),
+           "q_gain": torch.ones(256), "k_gain": torch.ones(256)}
+    with pytest.raises(ValueError, match="mod missing"):
+        H.DeviceModel(d, torch.zeros(256, 16, dtype=bf), torch.zeros(16, 256, dtype=bf), [blk])
+    blk["mod"] = torch.zeros(6, 256, dtype=bf)
+    with pytest.raises(ValueError, match="mod"):
+        H.DeviceModel(d, torch.zeros(256, 16, dtype=bf), torch.zeros(16, 256, dtype=bf), [blk])
+    blk["mod"] = torch.zeros(6, 256)
+    with pytest.raises(ValueError, match="timestep weights missing"):
+        H.DeviceModel(d, torch.zeros(256, 16, dtype=bf), torch.zeros(16, 256, dtype=bf), [blk])

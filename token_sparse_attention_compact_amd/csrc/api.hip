@@ -12,11 +12,14 @@ using namespace hsa;
 
 namespace {
 
-constexpr int32_t kAbiVersion = 1;
+constexpr int32_t kAbiVersion = 2;
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 bool valid_dtype(hsa_dtype t) { return t == HSA_F32 || t == HSA_BF16; }
+
+constexpr int32_t kAllFeatures = HSA_FEAT_QK_NORM | HSA_FEAT_ROPE3D | HSA_FEAT_ADALN | HSA_FEAT_CFG;
+bool has(const hsa_dims& d, int32_t feature) { return (d.features & feature) != 0; }
 
 // bf16 GEMM and attention operands are read through buffer descriptors whose
 // size and offsets are 32-bit: a whole operand must stay below 4 GiB.
@@ -35,6 +38,12 @@ hsa_status check_dims(const hsa_dims* d) {
   if (d->dtype == HSA_BF16 && !fits_buffer((int64_t)d->N * (d->D > d->F ? d->D : d->F) * 2))
     return HSA_ERR_SHAPE;
   if (d->dtype == HSA_F32 && (d->D % 4 != 0 || d->F % 4 != 0)) return HSA_ERR_SHAPE;
+  if (d->features & ~kAllFeatures) return HSA_ERR_ARG;
+  if ((d->features & HSA_FEAT_ROPE3D) &&
+      (d->grid_f <= 0 || d->grid_h <= 0 || d->grid_w <= 0 ||
+       (int64_t)d->grid_f * d->grid_h * d->grid_w != d->N))
+    return HSA_ERR_SHAPE;
+  if ((d->features & HSA_FEAT_CFG) && d->n_text <= 0) return HSA_ERR_ARG;
   return HSA_OK;
 }
 
@@ -88,6 +97,8 @@ int32_t n_active_of(const hsa_schedule* s, int32_t iter) {
 struct Layout {
   size_t h, a, q, o, u, v_new, n_active, attn, total;
   size_t attn_bytes;
+  size_t temb;    // HSA_FEAT_ADALN: e [D] then e0 [6][D], float32
+  size_t v_cond;  // HSA_FEAT_CFG: conditional-branch velocity [N][C], float32
 };
 
 size_t attn_ws_max(int32_t n_rows, int32_t n_kv, int32_t H, int32_t Dh) {
@@ -125,8 +136,21 @@ Layout layout_of(const hsa_dims* d) {
   }
   L.attn_bytes = ab;
   L.attn = take(ab > 0 ? ab : 16);
+  L.temb = has(*d, HSA_FEAT_ADALN) ? take((size_t)7 * d->D * sizeof(float)) : 0;
+  L.v_cond = has(*d, HSA_FEAT_CFG) ? take(N * d->C * sizeof(float)) : 0;
   L.total = off;
   return L;
+}
+
+hsa_status check_time_weights(const hsa_model* m) {
+  CHECK_PTR(m->t_w1);
+  CHECK_PTR(m->t_b1);
+  CHECK_PTR(m->t_w2);
+  CHECK_PTR(m->t_b2);
+  CHECK_PTR(m->t_w3);
+  CHECK_PTR(m->t_b3);
+  CHECK_PTR(m->head_mod);
+  return HSA_OK;
 }
 
 hsa_status check_model(const hsa_model* m) {
@@ -149,13 +173,28 @@ hsa_status check_model(const hsa_model* m) {
       CHECK_PTR(b.k_text);
       CHECK_PTR(b.v_text);
     }
+    if (has(m->dims, HSA_FEAT_QK_NORM)) {
+      CHECK_PTR(b.q_gain);
+      CHECK_PTR(b.k_gain);
+    }
+    if (has(m->dims, HSA_FEAT_ADALN)) CHECK_PTR(b.mod);
+    if (has(m->dims, HSA_FEAT_CFG)) {
+      CHECK_PTR(b.k_text_u);
+      CHECK_PTR(b.v_text_u);
+      CHECK_PTR(b.k_cache_u);
+      CHECK_PTR(b.v_cache_u);
+    }
   }
+  if (has(m->dims, HSA_FEAT_ADALN)) RETURN_IF(check_time_weights(m));
+  if (has(m->dims, HSA_FEAT_CFG) && !isfinite(m->cfg_scale)) return HSA_ERR_ARG;
   return HSA_OK;
 }
 
+// One block on nA active rows.  e0 [6][D]: timestep projection (adaLN only);
+// branch 1: the unconditional text set and caches (guidance only).
 hsa_status block_forward_impl(const hsa_model* m, int32_t layer, float* h,
-                              const int32_t* active_idx, int32_t nA, char* ws, const Layout& L,
-                              hipStream_t s) {
+                              const int32_t* active_idx, int32_t nA, const float* e0,
+                              int32_t branch, char* ws, const Layout& L, hipStream_t s) {
   if (nA == 0) return HSA_OK;
   const hsa_dims& d = m->dims;
   const hsa_block& b = m->blocks[layer];
@@ -166,28 +205,45 @@ hsa_status block_forward_impl(const hsa_model* m, int32_t layer, float* h,
   void* u = ws + L.u;
   void* attn_ws = ws + L.attn;
   const float scale = 1.0f / sqrtf((float)d.Dh);
+  const bool adaln = has(d, HSA_FEAT_ADALN);
+  void* kc = branch ? b.k_cache_u : b.k_cache;
+  void* vc = branch ? b.v_cache_u : b.v_cache;
+  const void* kt = branch ? b.k_text_u : b.k_text;
+  const void* vt = branch ? b.v_text_u : b.v_text;
+  // row k of the block's modulation: mod[k] + e0[k] (absent without adaLN)
+  auto mod = [&](int k) {
+    return adaln ? ModVec{b.mod + (size_t)k * d.D, e0 + (size_t)k * d.D} : ModVec{nullptr, nullptr};
+  };
+  const ModVec none{nullptr, nullptr};
+  const int epi_res = adaln ? EPI_RESID_GATED : EPI_RESID;
 
   // KV-cache synchronisation: QKV on active rows, fresh K/V scattered into the cache
-  RETURN_IF(launch_layernorm(h, a, nA, d.D, dt, s));
-  EpiArgs e_qkv{q, nullptr, b.k_cache, b.v_cache, active_idx, d.D};
+  RETURN_IF(launch_layernorm(h, a, nA, d.D, dt, mod(0), mod(1), s));
+  EpiArgs e_qkv{q, nullptr, kc, vc, active_idx, d.D, none};
   RETURN_IF(launch_gemm(a, b.w_qkv, nA, 3 * d.D, d.D, dt, EPI_QKV_SCATTER, e_qkv, s));
+  // qk-RMSNorm / rotary embedding of the fresh q rows and cache rows
+  const bool norm = has(d, HSA_FEAT_QK_NORM), rope = has(d, HSA_FEAT_ROPE3D);
+  if (norm || rope)
+    RETURN_IF(launch_qk_norm_rope(q, kc, active_idx, nA, d.D, d.Dh, dt, norm, rope, b.q_gain,
+                                  b.k_gain, d.grid_h, d.grid_w, s));
   // active queries over all N cached rows
-  RETURN_IF(launch_attention(q, b.k_cache, b.v_cache, o, nA, d.N, d.H, d.Dh, scale, dt, attn_ws,
-                             L.attn_bytes, s));
-  EpiArgs e_res{nullptr, h, nullptr, nullptr, nullptr, 0};
-  RETURN_IF(launch_gemm(o, b.w_o, nA, d.D, d.D, dt, EPI_RESID, e_res, s));
+  RETURN_IF(launch_attention(q, kc, vc, o, nA, d.N, d.H, d.Dh, scale, dt, attn_ws, L.attn_bytes, s));
+  EpiArgs e_res{nullptr, h, nullptr, nullptr, nullptr, 0, mod(2)};
+  RETURN_IF(launch_gemm(o, b.w_o, nA, d.D, d.D, dt, epi_res, e_res, s));
   if (d.n_text > 0) {
-    RETURN_IF(launch_layernorm(h, a, nA, d.D, dt, s));
-    EpiArgs e_q{q, nullptr, nullptr, nullptr, nullptr, 0};
+    RETURN_IF(launch_layernorm(h, a, nA, d.D, dt, none, none, s));
+    EpiArgs e_q{q, nullptr, nullptr, nullptr, nullptr, 0, none};
     RETURN_IF(launch_gemm(a, b.w_qx, nA, d.D, d.D, dt, EPI_STORE, e_q, s));
-    RETURN_IF(launch_attention(q, b.k_text, b.v_text, o, nA, d.n_text, d.H, d.Dh, scale, dt,
-                               attn_ws, L.attn_bytes, s));
-    RETURN_IF(launch_gemm(o, b.w_ox, nA, d.D, d.D, dt, EPI_RESID, e_res, s));
+    RETURN_IF(launch_attention(q, kt, vt, o, nA, d.n_text, d.H, d.Dh, scale, dt, attn_ws,
+                               L.attn_bytes, s));
+    EpiArgs e_x{nullptr, h, nullptr, nullptr, nullptr, 0, none};
+    RETURN_IF(launch_gemm(o, b.w_ox, nA, d.D, d.D, dt, EPI_RESID, e_x, s));
   }
-  RETURN_IF(launch_layernorm(h, a, nA, d.D, dt, s));
-  EpiArgs e_up{u, nullptr, nullptr, nullptr, nullptr, 0};
+  RETURN_IF(launch_layernorm(h, a, nA, d.D, dt, mod(3), mod(4), s));
+  EpiArgs e_up{u, nullptr, nullptr, nullptr, nullptr, 0, none};
   RETURN_IF(launch_gemm(a, b.w_1, nA, d.F, d.D, dt, EPI_GELU, e_up, s));
-  RETURN_IF(launch_gemm(u, b.w_2, nA, d.D, d.F, dt, EPI_RESID, e_res, s));
+  EpiArgs e_down{nullptr, h, nullptr, nullptr, nullptr, 0, mod(5)};
+  RETURN_IF(launch_gemm(u, b.w_2, nA, d.D, d.F, dt, epi_res, e_down, s));
   return HSA_OK;
 }
 
@@ -317,14 +373,20 @@ hsa_status hsa_attn_active(const void* q, const void* k, const void* v, void* o,
                           as_stream(stream));
 }
 
-hsa_status hsa_layernorm(const float* h, void* out, int32_t rows, int32_t D, hsa_dtype dtype,
-                         void* stream) {
+hsa_status hsa_layernorm(const float* h, void* out, int32_t rows, int32_t D, const float* shift,
+                         const float* scale, hsa_dtype dtype, void* stream) {
   if (!valid_dtype(dtype)) return HSA_ERR_DTYPE;
   if (rows < 0 || D <= 0 || D % 4 != 0) return HSA_ERR_SHAPE;
+  if ((shift == nullptr) != (scale == nullptr)) return HSA_ERR_ARG;
   if (rows == 0) return HSA_OK;
   CHECK_PTR(h);
   CHECK_PTR(out);
-  return launch_layernorm(h, out, rows, D, dtype, as_stream(stream));
+  if (shift) {
+    CHECK_PTR(shift);
+    CHECK_PTR(scale);
+  }
+  return launch_layernorm(h, out, rows, D, dtype, ModVec{shift, nullptr}, ModVec{scale, nullptr},
+                          as_stream(stream));
 }
 
 hsa_status hsa_embed(const float* x, const int32_t* active_idx, const void* w_in, float* h,
@@ -340,14 +402,21 @@ hsa_status hsa_embed(const float* x, const int32_t* active_idx, const void* w_in
 }
 
 hsa_status hsa_unembed(const float* h, const void* w_out, float* v_new, int32_t n_active,
-                       int32_t D, int32_t C, hsa_dtype dtype, void* stream) {
+                       int32_t D, int32_t C, const float* shift, const float* scale,
+                       hsa_dtype dtype, void* stream) {
   if (!valid_dtype(dtype)) return HSA_ERR_DTYPE;
   if (n_active < 0 || C <= 0 || D <= 0 || D % 4 != 0) return HSA_ERR_SHAPE;
+  if ((shift == nullptr) != (scale == nullptr)) return HSA_ERR_ARG;
   if (n_active == 0) return HSA_OK;
   CHECK_PTR(h);
   CHECK_PTR(w_out);
   CHECK_PTR(v_new);
-  return launch_unembed(h, w_out, v_new, n_active, D, C, dtype, as_stream(stream));
+  if (shift) {
+    CHECK_PTR(shift);
+    CHECK_PTR(scale);
+  }
+  return launch_unembed(h, w_out, v_new, n_active, D, C, dtype, ModVec{shift, nullptr},
+                        ModVec{scale, nullptr}, as_stream(stream));
 }
 
 hsa_status hsa_linear(const void* a, const void* w, void* out, int32_t M, int32_t Nout, int32_t K,
@@ -358,19 +427,21 @@ hsa_status hsa_linear(const void* a, const void* w, void* out, int32_t M, int32_
   CHECK_PTR(a);
   CHECK_PTR(w);
   CHECK_PTR(out);
-  EpiArgs e{out, nullptr, nullptr, nullptr, nullptr, 0};
+  EpiArgs e{out, nullptr, nullptr, nullptr, nullptr, 0, ModVec{nullptr, nullptr}};
   return launch_gemm(a, w, M, Nout, K, dtype, act ? EPI_GELU : EPI_STORE, e, as_stream(stream));
 }
 
 hsa_status hsa_linear_residual(const void* a, const void* w, float* h, int32_t M, int32_t Nout,
-                               int32_t K, hsa_dtype dtype, void* stream) {
+                               int32_t K, const float* gate, hsa_dtype dtype, void* stream) {
   RETURN_IF(check_gemm_shape(M, Nout, K, dtype));
   if (M == 0) return HSA_OK;
   CHECK_PTR(a);
   CHECK_PTR(w);
   CHECK_PTR(h);
-  EpiArgs e{nullptr, h, nullptr, nullptr, nullptr, 0};
-  return launch_gemm(a, w, M, Nout, K, dtype, EPI_RESID, e, as_stream(stream));
+  if (gate) CHECK_PTR(gate);
+  EpiArgs e{nullptr, h, nullptr, nullptr, nullptr, 0, ModVec{gate, nullptr}};
+  return launch_gemm(a, w, M, Nout, K, dtype, gate ? EPI_RESID_GATED : EPI_RESID, e,
+                     as_stream(stream));
 }
 
 hsa_status hsa_qkv_scatter(const void* a, const int32_t* active_idx, const void* w_qkv,
@@ -385,23 +456,66 @@ hsa_status hsa_qkv_scatter(const void* a, const int32_t* active_idx, const void*
   CHECK_PTR(q_out);
   CHECK_PTR(k_cache);
   CHECK_PTR(v_cache);
-  EpiArgs e{q_out, nullptr, k_cache, v_cache, active_idx, D};
+  EpiArgs e{q_out, nullptr, k_cache, v_cache, active_idx, D, ModVec{nullptr, nullptr}};
   return launch_gemm(a, w_qkv, n_active, 3 * D, D, dtype, EPI_QKV_SCATTER, e, as_stream(stream));
 }
 
+hsa_status hsa_qk_norm_rope(void* q, void* k_cache, const int32_t* active_idx, int32_t n_active,
+                            const hsa_dims* dims, const float* q_gain, const float* k_gain,
+                            void* stream) {
+  RETURN_IF(check_dims(dims));
+  if (n_active < 0 || n_active > dims->N) return HSA_ERR_SHAPE;
+  const bool norm = has(*dims, HSA_FEAT_QK_NORM), rope = has(*dims, HSA_FEAT_ROPE3D);
+  if (n_active == 0 || (!norm && !rope)) return HSA_OK;
+  CHECK_PTR(q);
+  CHECK_PTR(k_cache);
+  CHECK_PTR(active_idx);
+  if (norm) {
+    CHECK_PTR(q_gain);
+    CHECK_PTR(k_gain);
+  }
+  return launch_qk_norm_rope(q, k_cache, active_idx, n_active, dims->D, dims->Dh, dims->dtype, norm,
+                             rope, q_gain, k_gain, dims->grid_h, dims->grid_w, as_stream(stream));
+}
+
+hsa_status hsa_time_embed(const hsa_model* model, float sigma, float* e, float* e0, void* stream) {
+  if (!model) return HSA_ERR_ARG;
+  RETURN_IF(check_dims(&model->dims));
+  if (!has(model->dims, HSA_FEAT_ADALN)) return HSA_ERR_ARG;
+  if (!isfinite(sigma)) return HSA_ERR_ARG;
+  RETURN_IF(check_time_weights(model));
+  CHECK_PTR(e);
+  CHECK_PTR(e0);
+  return launch_time_embed(sigma, model->t_w1, model->t_b1, model->t_w2, model->t_b2, model->t_w3,
+                           model->t_b3, model->dims.D, e, e0, as_stream(stream));
+}
+
+hsa_status hsa_guidance(const float* v_cond, float* v, int32_t rows, int32_t C, float g,
+                        void* stream) {
+  if (rows < 0 || C <= 0 || C % 4 != 0) return HSA_ERR_SHAPE;
+  if (!isfinite(g)) return HSA_ERR_ARG;
+  if (rows == 0) return HSA_OK;
+  CHECK_PTR(v_cond);
+  CHECK_PTR(v);
+  return launch_guidance(v_cond, v, (int64_t)rows * C, g, as_stream(stream));
+}
+
 hsa_status hsa_block_forward(const hsa_model* model, int32_t layer, float* h,
-                             const int32_t* active_idx, int32_t n_active, void* ws,
-                             size_t ws_bytes, void* stream) {
+                             const int32_t* active_idx, int32_t n_active, const float* e0,
+                             int32_t branch, void* ws, size_t ws_bytes, void* stream) {
   RETURN_IF(check_model(model));
   if (layer < 0 || layer >= model->dims.L) return HSA_ERR_ARG;
   if (n_active < 0 || n_active > model->dims.N) return HSA_ERR_SHAPE;
+  if (branch != 0 && !(branch == 1 && has(model->dims, HSA_FEAT_CFG))) return HSA_ERR_ARG;
   if (n_active == 0) return HSA_OK;
   CHECK_PTR(h);
   CHECK_PTR(active_idx);
   CHECK_PTR(ws);
+  if (has(model->dims, HSA_FEAT_ADALN)) CHECK_PTR(e0);
   const Layout L = layout_of(&model->dims);
   if (ws_bytes < L.total) return HSA_ERR_WORKSPACE;
-  return block_forward_impl(model, layer, h, active_idx, n_active, (char*)ws, L, as_stream(stream));
+  return block_forward_impl(model, layer, h, active_idx, n_active, e0, branch, (char*)ws, L,
+                            as_stream(stream));
 }
 
 hsa_status hsa_step(const hsa_model* model, const hsa_schedule* sched, hsa_state* st,
@@ -436,12 +550,27 @@ hsa_status hsa_step(const hsa_model* model, const hsa_schedule* sched, hsa_state
   const int32_t nA = n_active_of(sched, iter);
   RETURN_IF(launch_active_set(st->group, d.N, active_group_mask(sched, iter), nA, st->active_idx,
                               st->pos, n_dev, s));
-  // 3. model on the active rows
+  // 3. model on the active rows: timestep embedding of sigma_i (adaLN), then
+  //    embed -> blocks -> unembed per guidance branch, then the combine
   if (nA > 0) {
-    RETURN_IF(launch_embed(st->x, st->active_idx, model->w_in, h, nA, d.C, d.D, d.dtype, s));
-    for (int l = 0; l < d.L; ++l)
-      RETURN_IF(block_forward_impl(model, l, h, st->active_idx, nA, ws, L, s));
-    RETURN_IF(launch_unembed(h, model->w_out, v_new, nA, d.D, d.C, d.dtype, s));
+    const bool adaln = has(d, HSA_FEAT_ADALN), cfg = has(d, HSA_FEAT_CFG);
+    float* e = adaln ? (float*)(ws + L.temb) : nullptr;
+    float* e0 = adaln ? e + d.D : nullptr;
+    if (adaln)
+      RETURN_IF(launch_time_embed(sigma_i, model->t_w1, model->t_b1, model->t_w2, model->t_b2,
+                                  model->t_w3, model->t_b3, d.D, e, e0, s));
+    const ModVec head_shift = adaln ? ModVec{model->head_mod, e} : ModVec{nullptr, nullptr};
+    const ModVec head_scale =
+        adaln ? ModVec{model->head_mod + d.D, e} : ModVec{nullptr, nullptr};
+    float* v_cond = cfg ? (float*)(ws + L.v_cond) : nullptr;
+    for (int branch = 0; branch < (cfg ? 2 : 1); ++branch) {
+      RETURN_IF(launch_embed(st->x, st->active_idx, model->w_in, h, nA, d.C, d.D, d.dtype, s));
+      for (int l = 0; l < d.L; ++l)
+        RETURN_IF(block_forward_impl(model, l, h, st->active_idx, nA, e0, branch, ws, L, s));
+      RETURN_IF(launch_unembed(h, model->w_out, (cfg && branch == 0) ? v_cond : v_new, nA, d.D,
+                               d.C, d.dtype, head_shift, head_scale, s));
+    }
+    if (cfg) RETURN_IF(launch_guidance(v_cond, v_new, (int64_t)nA * d.C, model->cfg_scale, s));
     // 4. optional synthetic velocity in place of the model's
     if (v_field) RETURN_IF(launch_gather_rows(v_field, st->active_idx, v_new, nA, d.C, s));
   }

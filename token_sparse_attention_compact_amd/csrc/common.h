@@ -65,12 +65,46 @@ hsa_status launch_euler(float* x, float* v_hat, float* score, const float* v_new
                         int32_t update_score, hipStream_t s);
 hsa_status launch_gather_rows(const float* src, const int32_t* idx, float* dst, int32_t rows,
                               int32_t C, hipStream_t s);
+
+// A float32 vector [n] given as base[i] + add[i] (add may be null), so that a
+// block's modulation table row and the per-iteration timestep projection are
+// combined where they are read.  base == null: the vector is absent.
+struct ModVec {
+  const float* base;
+  const float* add;
+  __host__ __device__ bool present() const { return base != nullptr; }
+};
+__device__ __forceinline__ f32x4 load_mod4(const ModVec& m, int32_t i) {
+  f32x4 v = *reinterpret_cast<const f32x4*>(m.base + i);
+  if (m.add) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(m.add + i);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] += a[e];
+  }
+  return v;
+}
+__device__ __forceinline__ float load_mod(const ModVec& m, int32_t i) {
+  return m.add ? m.base[i] + m.add[i] : m.base[i];
+}
+
+// LayerNorm, optionally modulated: LN(h) (1 + scale) + shift when both are present.
 hsa_status launch_layernorm(const float* h, void* out, int32_t rows, int32_t D, hsa_dtype dt,
-                            hipStream_t s);
+                            ModVec shift, ModVec scale, hipStream_t s);
 hsa_status launch_embed(const float* x, const int32_t* idx, const void* w_in, float* h,
                         int32_t rows, int32_t C, int32_t D, hsa_dtype dt, hipStream_t s);
 hsa_status launch_unembed(const float* h, const void* w_out, float* v_new, int32_t rows,
-                          int32_t D, int32_t C, hsa_dtype dt, hipStream_t s);
+                          int32_t D, int32_t C, hsa_dtype dt, ModVec shift, ModVec scale,
+                          hipStream_t s);
+
+// Optional block features (wanfeat.hip).
+hsa_status launch_qk_norm_rope(void* q, void* kc, const int32_t* idx, int32_t rows, int32_t D,
+                               int32_t Dh, hsa_dtype dt, bool norm, bool rope,
+                               const float* q_gain, const float* k_gain, int32_t grid_h,
+                               int32_t grid_w, hipStream_t s);
+hsa_status launch_time_embed(float sigma, const float* w1, const float* b1, const float* w2,
+                             const float* b2, const float* w3, const float* b3, int32_t D,
+                             float* e, float* e0, hipStream_t s);
+hsa_status launch_guidance(const float* v_cond, float* v, int64_t n, float g, hipStream_t s);
 
 // GEMM epilogues: out = a w^T followed by one of these.
 enum Epilogue : int {
@@ -78,6 +112,7 @@ enum Epilogue : int {
   EPI_GELU = 1,         // out[m][n] = gelu(acc)                (dtype)
   EPI_RESID = 2,        // resid[m][n] += acc                   (float32)
   EPI_QKV_SCATTER = 3,  // n <  D: q[m][n];  n < 2D: kc[idx[m]][n-D];  else vc[idx[m]][n-2D]
+  EPI_RESID_GATED = 4,  // resid[m][n] += gate[n] * acc          (float32)
 };
 struct EpiArgs {
   void* out;            // EPI_STORE / EPI_GELU output, EPI_QKV_SCATTER q output
@@ -86,6 +121,7 @@ struct EpiArgs {
   void* vc;
   const int32_t* idx;   // EPI_QKV_SCATTER row -> cache row
   int32_t D;            // EPI_QKV_SCATTER width of each of q, k, v
+  ModVec gate;          // EPI_RESID_GATED, [N]
 };
 hsa_status launch_gemm(const void* a, const void* w, int32_t M, int32_t N, int32_t K,
                        hsa_dtype dt, int epi, const EpiArgs& ep, hipStream_t s);

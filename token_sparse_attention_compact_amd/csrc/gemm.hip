@@ -11,9 +11,10 @@
 // each 16-byte chunk at an XOR-swizzled position of its 128-byte row so the
 // operand reads hit distinct banks.  The next stage's loads are in flight
 // while the current one feeds the MFMAs.  Epilogues are fused (store / GELU /
-// residual add / QKV scatter) and work on quads of 4 consecutive output
-// columns: the MFMA computes C^T blocks (w rows as MFMA rows), whose
-// accumulator layout gives each lane runs of 4 consecutive columns of a row.
+// residual add, plain or gated per column / QKV scatter) and work on quads of
+// 4 consecutive output columns: the MFMA computes C^T blocks (w rows as MFMA
+// rows), whose accumulator layout gives each lane runs of 4 consecutive
+// columns of a row.
 //
 // float32 path (small float32 workloads): LDS-tiled FMA GEMM, 64x64 tiles.
 #include "common.h"
@@ -31,6 +32,9 @@ __device__ __forceinline__ void epilogue(const EpiArgs& ep, int32_t N, int32_t r
   } else if constexpr (EPI == EPI_RESID) {
     float* p = ep.resid + (size_t)row * N + col;
     *p = *p + v;
+  } else if constexpr (EPI == EPI_RESID_GATED) {
+    float* p = ep.resid + (size_t)row * N + col;
+    *p = *p + load_mod(ep.gate, col) * v;
   } else {  // EPI_QKV_SCATTER
     const int32_t D = ep.D;
     const int32_t which = col / D;
@@ -64,6 +68,13 @@ __device__ __forceinline__ void epilogue4(const EpiArgs& ep, int32_t N, int32_t 
     f32x4 h = *p;
 #pragma unroll
     for (int e = 0; e < 4; ++e) h[e] += v[e];
+    *p = h;
+  } else if constexpr (EPI == EPI_RESID_GATED) {
+    f32x4* p = reinterpret_cast<f32x4*>(ep.resid + (size_t)row * N + col);
+    const f32x4 g = load_mod4(ep.gate, col);
+    f32x4 h = *p;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) h[e] += g[e] * v[e];
     *p = h;
   } else {  // EPI_QKV_SCATTER: D % 4 == 0, so the 4 columns stay in one of q, k, v
     const int32_t D = ep.D;
@@ -405,6 +416,7 @@ hsa_status launch_gemm(const void* a, const void* w, int32_t M, int32_t N, int32
     case EPI_GELU: return run<EPI_GELU>(a, w, M, N, K, dt, ep, s);
     case EPI_RESID: return run<EPI_RESID>(a, w, M, N, K, dt, ep, s);
     case EPI_QKV_SCATTER: return run<EPI_QKV_SCATTER>(a, w, M, N, K, dt, ep, s);
+    case EPI_RESID_GATED: return run<EPI_RESID_GATED>(a, w, M, N, K, dt, ep, s);
     default: return HSA_ERR_ARG;
   }
 }

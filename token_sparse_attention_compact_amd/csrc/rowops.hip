@@ -5,6 +5,9 @@
 // accesses.  LayerNorm keeps the row in registers when D is a multiple of
 // 256 (one read of the row from memory, statistics in float32 from the
 // registers); otherwise, and in unembed, the statistics take two passes.
+// LayerNorm and unembed optionally apply the timestep modulation
+// LN(h) (1 + scale) + shift (MOD template flag; shift and scale are [D]
+// vectors read as float4 from L2, the same for every row).
 #include "common.h"
 
 namespace hsa {
@@ -45,10 +48,23 @@ __device__ __forceinline__ void store4<bf16>(bf16* p, f32x4 v) {
   *reinterpret_cast<bf16x4*>(p) = b;
 }
 
-template <typename OutT>
+// n (1 + scale) + shift on the float4 chunk at column 4*i.
+template <bool MOD>
+__device__ __forceinline__ f32x4 modulate4(f32x4 n, const ModVec& shift, const ModVec& scale,
+                                           int32_t i) {
+  if constexpr (MOD) {
+    const f32x4 sh = load_mod4(shift, 4 * i);
+    const f32x4 sc = load_mod4(scale, 4 * i);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) n[c] = __builtin_fmaf(n[c], 1.0f + sc[c], sh[c]);
+  }
+  return n;
+}
+
+template <typename OutT, bool MOD>
 __global__ __launch_bounds__(256) void layernorm_kernel(const float* __restrict__ h,
                                                         OutT* __restrict__ out, int32_t rows,
-                                                        int32_t D) {
+                                                        int32_t D, ModVec shift, ModVec scale) {
   const int lane = threadIdx.x & (kWave - 1);
   const int32_t row = blockIdx.x * kRowsPerBlock + threadIdx.x / kWave;
   if (row >= rows) return;
@@ -61,15 +77,16 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const float* __restrict_
     f32x4 v = hr[i];
 #pragma unroll
     for (int c = 0; c < 4; ++c) v[c] = (v[c] - mean) * rstd;
-    store4<OutT>(orow + 4 * i, v);
+    store4<OutT>(orow + 4 * i, modulate4<MOD>(v, shift, scale, i));
   }
 }
 
 // Row in registers: lane l holds float4 chunks l, l+64, ..., l+64(NV-1).
-template <typename OutT, int NV>
+template <typename OutT, int NV, bool MOD>
 __global__ __launch_bounds__(256) void layernorm_reg_kernel(const float* __restrict__ h,
                                                             OutT* __restrict__ out, int32_t rows,
-                                                            int32_t D) {
+                                                            int32_t D, ModVec shift,
+                                                            ModVec scale) {
   const int lane = threadIdx.x & (kWave - 1);
   const int32_t row = blockIdx.x * kRowsPerBlock + threadIdx.x / kWave;
   if (row >= rows) return;
@@ -97,17 +114,21 @@ __global__ __launch_bounds__(256) void layernorm_reg_kernel(const float* __restr
     f32x4 o;
 #pragma unroll
     for (int c = 0; c < 4; ++c) o[c] = (v[i][c] - mean) * rstd;
-    store4<OutT>(orow + 4 * (lane + kWave * i), o);
+    const int32_t c4 = lane + kWave * i;
+    store4<OutT>(orow + 4 * c4, modulate4<MOD>(o, shift, scale, c4));
   }
 }
 
-template <typename OutT>
+template <typename OutT, bool MOD>
 bool launch_layernorm_reg(const float* h, OutT* out, int32_t rows, int32_t D, int blocks,
-                          hipStream_t s) {
+                          ModVec shift, ModVec scale, hipStream_t s) {
   if (D % (4 * kWave) != 0) return false;
   switch (D / (4 * kWave)) {
-#define HSA_LN_CASE(nv) \
-    case nv: layernorm_reg_kernel<OutT, nv><<<blocks, 256, 0, s>>>(h, out, rows, D); return true;
+#define HSA_LN_CASE(nv)                                                                  \
+    case nv:                                                                             \
+      layernorm_reg_kernel<OutT, nv, MOD><<<blocks, 256, 0, s>>>(h, out, rows, D, shift, \
+                                                                 scale);                 \
+      return true;
     HSA_LN_CASE(1) HSA_LN_CASE(2) HSA_LN_CASE(3) HSA_LN_CASE(4) HSA_LN_CASE(5) HSA_LN_CASE(6)
     HSA_LN_CASE(8) HSA_LN_CASE(10) HSA_LN_CASE(12) HSA_LN_CASE(16) HSA_LN_CASE(20) HSA_LN_CASE(24)
 #undef HSA_LN_CASE
@@ -167,11 +188,11 @@ __global__ __launch_bounds__(256) void embed_kernel_c16(const float* __restrict_
 }
 
 // v_new[j][c] = sum_d LN(h[j])[d] * w_out[c][d], C == CC known at compile time.
-template <typename WT, int CC>
+template <typename WT, int CC, bool MOD>
 __global__ __launch_bounds__(256) void unembed_kernel(const float* __restrict__ h,
                                                       const WT* __restrict__ w_out,
                                                       float* __restrict__ v_new, int32_t rows,
-                                                      int32_t D) {
+                                                      int32_t D, ModVec shift, ModVec scale) {
   const int lane = threadIdx.x & (kWave - 1);
   const int32_t row = blockIdx.x * kRowsPerBlock + threadIdx.x / kWave;
   if (row >= rows) return;
@@ -186,6 +207,7 @@ __global__ __launch_bounds__(256) void unembed_kernel(const float* __restrict__ 
     f32x4 v = hr[i];
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[e] = (v[e] - mean) * rstd;
+    v = modulate4<MOD>(v, shift, scale, i);
 #pragma unroll
     for (int c = 0; c < CC; ++c) {
       const WT* w = w_out + (size_t)c * D + 4 * i;
@@ -204,11 +226,12 @@ __global__ __launch_bounds__(256) void unembed_kernel(const float* __restrict__ 
 }
 
 // Any C: one wave reduction per output channel.
-template <typename WT>
+template <typename WT, bool MOD>
 __global__ __launch_bounds__(256) void unembed_kernel_any(const float* __restrict__ h,
                                                           const WT* __restrict__ w_out,
                                                           float* __restrict__ v_new, int32_t rows,
-                                                          int32_t D, int32_t C) {
+                                                          int32_t D, int32_t C, ModVec shift,
+                                                          ModVec scale) {
   const int lane = threadIdx.x & (kWave - 1);
   const int32_t row = blockIdx.x * kRowsPerBlock + threadIdx.x / kWave;
   if (row >= rows) return;
@@ -219,29 +242,62 @@ __global__ __launch_bounds__(256) void unembed_kernel_any(const float* __restric
   for (int c = 0; c < C; ++c) {
     float acc = 0.f;
     for (int i = lane; i < nv; i += kWave) {
-      const f32x4 v = hr[i];
+      f32x4 v = hr[i];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = (v[e] - mean) * rstd;
+      v = modulate4<MOD>(v, shift, scale, i);
       const WT* w = w_out + (size_t)c * D + 4 * i;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc = __builtin_fmaf((v[e] - mean) * rstd, to_f32(w[e]), acc);
+      for (int e = 0; e < 4; ++e) acc = __builtin_fmaf(v[e], to_f32(w[e]), acc);
     }
     acc = wave_sum(acc);
     if (lane == 0) v_new[(size_t)row * C + c] = acc;
   }
 }
 
+template <bool MOD>
+void layernorm_dispatch(const float* h, void* out, int32_t rows, int32_t D, hsa_dtype dt,
+                        ModVec shift, ModVec scale, hipStream_t s) {
+  const int blocks = cdiv(rows, kRowsPerBlock);
+  if (dt == HSA_BF16) {
+    if (!launch_layernorm_reg<bf16, MOD>(h, (bf16*)out, rows, D, blocks, shift, scale, s))
+      layernorm_kernel<bf16, MOD><<<blocks, 256, 0, s>>>(h, (bf16*)out, rows, D, shift, scale);
+  } else {
+    if (!launch_layernorm_reg<float, MOD>(h, (float*)out, rows, D, blocks, shift, scale, s))
+      layernorm_kernel<float, MOD><<<blocks, 256, 0, s>>>(h, (float*)out, rows, D, shift, scale);
+  }
+}
+
+template <bool MOD>
+void unembed_dispatch(const float* h, const void* w_out, float* v_new, int32_t rows, int32_t D,
+                      int32_t C, hsa_dtype dt, ModVec shift, ModVec scale, hipStream_t s) {
+  const int blocks = cdiv(rows, kRowsPerBlock);
+  if (C == 16) {
+    if (dt == HSA_BF16)
+      unembed_kernel<bf16, 16, MOD><<<blocks, 256, 0, s>>>(h, (const bf16*)w_out, v_new, rows, D,
+                                                           shift, scale);
+    else
+      unembed_kernel<float, 16, MOD><<<blocks, 256, 0, s>>>(h, (const float*)w_out, v_new, rows,
+                                                            D, shift, scale);
+  } else {
+    if (dt == HSA_BF16)
+      unembed_kernel_any<bf16, MOD><<<blocks, 256, 0, s>>>(h, (const bf16*)w_out, v_new, rows, D,
+                                                           C, shift, scale);
+    else
+      unembed_kernel_any<float, MOD><<<blocks, 256, 0, s>>>(h, (const float*)w_out, v_new, rows,
+                                                            D, C, shift, scale);
+  }
+}
+
 }  // namespace
 
 hsa_status launch_layernorm(const float* h, void* out, int32_t rows, int32_t D, hsa_dtype dt,
-                            hipStream_t s) {
+                            ModVec shift, ModVec scale, hipStream_t s) {
   if (rows == 0) return HSA_OK;
-  const int blocks = cdiv(rows, kRowsPerBlock);
-  if (dt == HSA_BF16) {
-    if (!launch_layernorm_reg<bf16>(h, (bf16*)out, rows, D, blocks, s))
-      layernorm_kernel<bf16><<<blocks, 256, 0, s>>>(h, (bf16*)out, rows, D);
-  } else {
-    if (!launch_layernorm_reg<float>(h, (float*)out, rows, D, blocks, s))
-      layernorm_kernel<float><<<blocks, 256, 0, s>>>(h, (float*)out, rows, D);
-  }
+  if (shift.present() && scale.present())
+    layernorm_dispatch<true>(h, out, rows, D, dt, shift, scale, s);
+  else
+    layernorm_dispatch<false>(h, out, rows, D, dt, shift, scale, s);
   return launch_status();
 }
 
@@ -267,20 +323,13 @@ hsa_status launch_embed(const float* x, const int32_t* idx, const void* w_in, fl
 }
 
 hsa_status launch_unembed(const float* h, const void* w_out, float* v_new, int32_t rows,
-                          int32_t D, int32_t C, hsa_dtype dt, hipStream_t s) {
+                          int32_t D, int32_t C, hsa_dtype dt, ModVec shift, ModVec scale,
+                          hipStream_t s) {
   if (rows == 0) return HSA_OK;
-  const int blocks = cdiv(rows, kRowsPerBlock);
-  if (C == 16) {
-    if (dt == HSA_BF16)
-      unembed_kernel<bf16, 16><<<blocks, 256, 0, s>>>(h, (const bf16*)w_out, v_new, rows, D);
-    else
-      unembed_kernel<float, 16><<<blocks, 256, 0, s>>>(h, (const float*)w_out, v_new, rows, D);
-  } else {
-    if (dt == HSA_BF16)
-      unembed_kernel_any<bf16><<<blocks, 256, 0, s>>>(h, (const bf16*)w_out, v_new, rows, D, C);
-    else
-      unembed_kernel_any<float><<<blocks, 256, 0, s>>>(h, (const float*)w_out, v_new, rows, D, C);
-  }
+  if (shift.present() && scale.present())
+    unembed_dispatch<true>(h, w_out, v_new, rows, D, C, dt, shift, scale, s);
+  else
+    unembed_dispatch<false>(h, w_out, v_new, rows, D, C, dt, shift, scale, s);
   return launch_status();
 }
 

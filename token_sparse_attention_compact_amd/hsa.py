@@ -21,11 +21,17 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "lib
 
 HSA_F32, HSA_BF16 = 0, 1
 MAX_GROUPS = 8
+ABI_VERSION = 2
+# optional block features (hsa_dims.features)
+FEAT_QK_NORM, FEAT_ROPE3D, FEAT_ADALN, FEAT_CFG = 1, 2, 4, 8
+FEATURE_BITS = {"qk_norm": FEAT_QK_NORM, "rope3d": FEAT_ROPE3D, "adaln": FEAT_ADALN, "cfg": FEAT_CFG}
+T_FREQ = 256   # width of the timestep sinusoid (t_w1 is [D][256])
 EXPORTED = [
     "hsa_status_str", "hsa_abi_version", "hsa_workspace_size", "hsa_attn_workspace_size",
     "hsa_select_workspace_size", "hsa_n_active", "hsa_active_set", "hsa_select", "hsa_euler",
     "hsa_attn_active", "hsa_layernorm", "hsa_embed", "hsa_unembed", "hsa_linear",
-    "hsa_linear_residual", "hsa_qkv_scatter", "hsa_block_forward", "hsa_step",
+    "hsa_linear_residual", "hsa_qkv_scatter", "hsa_qk_norm_rope", "hsa_time_embed", "hsa_guidance",
+    "hsa_block_forward", "hsa_step",
 ]
 
 
@@ -39,7 +45,8 @@ class HsaError(RuntimeError):
 class Dims(ct.Structure):
     _fields_ = [("N", ct.c_int32), ("C", ct.c_int32), ("D", ct.c_int32), ("H", ct.c_int32),
                 ("Dh", ct.c_int32), ("F", ct.c_int32), ("L", ct.c_int32), ("n_text", ct.c_int32),
-                ("dtype", ct.c_int)]
+                ("dtype", ct.c_int), ("features", ct.c_int32), ("grid_f", ct.c_int32),
+                ("grid_h", ct.c_int32), ("grid_w", ct.c_int32)]
 
 
 class Schedule(ct.Structure):
@@ -47,14 +54,19 @@ class Schedule(ct.Structure):
                 ("budget", ct.c_int32 * MAX_GROUPS), ("count", ct.c_int32 * MAX_GROUPS)]
 
 
+BLOCK_FIELDS = ("w_qkv", "w_o", "w_1", "w_2", "w_qx", "w_ox", "k_cache", "v_cache", "k_text",
+                "v_text", "q_gain", "k_gain", "mod", "k_text_u", "v_text_u", "k_cache_u", "v_cache_u")
+TIME_FIELDS = ("t_w1", "t_b1", "t_w2", "t_b2", "t_w3", "t_b3", "head_mod")
+
+
 class Block(ct.Structure):
-    _fields_ = [(n, ct.c_void_p) for n in ("w_qkv", "w_o", "w_1", "w_2", "w_qx", "w_ox",
-                                           "k_cache", "v_cache", "k_text", "v_text")]
+    _fields_ = [(n, ct.c_void_p) for n in BLOCK_FIELDS]
 
 
 class Model(ct.Structure):
-    _fields_ = [("dims", Dims), ("w_in", ct.c_void_p), ("w_out", ct.c_void_p),
-                ("blocks", ct.POINTER(Block))]
+    _fields_ = ([("dims", Dims), ("w_in", ct.c_void_p), ("w_out", ct.c_void_p),
+                 ("blocks", ct.POINTER(Block))] + [(n, ct.c_void_p) for n in TIME_FIELDS]
+                + [("cfg_scale", ct.c_float)])
 
 
 class State(ct.Structure):
@@ -94,19 +106,25 @@ def load() -> ct.CDLL:
         "hsa_select": ([P, I, PI, I, P, P, S, P], I),
         "hsa_euler": ([P, P, P, P, P, I, I, F, F, I, P], I),
         "hsa_attn_active": ([P, P, P, P, I, I, I, I, F, ct.c_int, P, S, P], I),
-        "hsa_layernorm": ([P, P, I, I, ct.c_int, P], I),
+        "hsa_layernorm": ([P, P, I, I, P, P, ct.c_int, P], I),
         "hsa_embed": ([P, P, P, P, I, I, I, ct.c_int, P], I),
-        "hsa_unembed": ([P, P, P, I, I, I, ct.c_int, P], I),
+        "hsa_unembed": ([P, P, P, I, I, I, P, P, ct.c_int, P], I),
         "hsa_linear": ([P, P, P, I, I, I, I, ct.c_int, P], I),
-        "hsa_linear_residual": ([P, P, P, I, I, I, ct.c_int, P], I),
+        "hsa_linear_residual": ([P, P, P, I, I, I, P, ct.c_int, P], I),
         "hsa_qkv_scatter": ([P, P, P, P, P, P, I, I, I, ct.c_int, P], I),
-        "hsa_block_forward": ([ct.POINTER(Model), I, P, P, I, P, S, P], I),
+        "hsa_qk_norm_rope": ([P, P, P, I, ct.POINTER(Dims), P, P, P], I),
+        "hsa_time_embed": ([ct.POINTER(Model), F, P, P, P], I),
+        "hsa_guidance": ([P, P, I, I, F, P], I),
+        "hsa_block_forward": ([ct.POINTER(Model), I, P, P, I, P, I, P, S, P], I),
         "hsa_step": ([ct.POINTER(Model), ct.POINTER(Schedule), ct.POINTER(State), I, F, F, I, P, P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
         fn.argtypes = args
         fn.restype = res
+    if L.hsa_abi_version() != ABI_VERSION:
+        raise ImportError(f"libhsa.so ABI version {L.hsa_abi_version()}, binding expects "
+                          f"{ABI_VERSION}: rebuild with `python -m token_sparse_attention_compact_amd.build`")
     _lib = L
     return L
 
@@ -163,8 +181,13 @@ def _rows(t: torch.Tensor, rows: int, cols: Optional[int], name: str):
 
 
 # ---------------------------------------------------------------- structs from python
-def make_dims(N, C, D, H, Dh, F, L, n_text=0, dtype=torch.bfloat16) -> Dims:
-    return Dims(N, C, D, H, Dh, F, L, n_text, HSA_BF16 if dtype == torch.bfloat16 else HSA_F32)
+def make_dims(N, C, D, H, Dh, F, L, n_text=0, dtype=torch.bfloat16, features=0,
+              grid=(0, 0, 0)) -> Dims:
+    """`features`: OR of FEAT_* bits, or an iterable of feature names."""
+    if not isinstance(features, int):
+        features = sum(FEATURE_BITS[f] for f in set(features))
+    return Dims(N, C, D, H, Dh, F, L, n_text, HSA_BF16 if dtype == torch.bfloat16 else HSA_F32,
+                features, *grid)
 
 
 def make_schedule(T: int, budgets: Sequence[int], counts: Sequence[int], m: int = 0) -> Schedule:
@@ -261,11 +284,22 @@ def hsa_attn_active(q, k, v, o, H: int, Dh: int, scale: Optional[float] = None,
                                                      scale, dt, _ptr(ws), wsb, _stream(stream)))
 
 
-def hsa_layernorm(h, out, stream=None):
+def _mod_pair(shift, scale, D: int, name: str):
+    if (shift is None) != (scale is None):
+        raise ValueError(f"{name}: shift and scale go together")
+    for t, n in ((shift, "shift"), (scale, "scale")):
+        if t is not None:
+            _need(t, torch.float32, n)
+            _shape(t, (D,), n)
+
+
+def hsa_layernorm(h, out, shift=None, scale=None, stream=None):
     _need(h, torch.float32, "h")
     rows, D = h.shape
     _shape(out, (rows, D), "out")
-    _check("hsa_layernorm", load().hsa_layernorm(_ptr(h), _ptr(out), rows, D, _dt(out), _stream(stream)))
+    _mod_pair(shift, scale, D, "hsa_layernorm")
+    _check("hsa_layernorm", load().hsa_layernorm(_ptr(h), _ptr(out), rows, D, _ptr(shift), _ptr(scale),
+                                                 _dt(out), _stream(stream)))
 
 
 def hsa_embed(x, active_idx, n_active: int, w_in, h, stream=None):
@@ -280,14 +314,15 @@ def hsa_embed(x, active_idx, n_active: int, w_in, h, stream=None):
                                          _dt(w_in), _stream(stream)))
 
 
-def hsa_unembed(h, w_out, v_new, n_active: int, stream=None):
+def hsa_unembed(h, w_out, v_new, n_active: int, shift=None, scale=None, stream=None):
     _need(h, torch.float32, "h")
     _need(v_new, torch.float32, "v_new")
     C, D = w_out.shape
     _rows(h, n_active, D, "h")
     _rows(v_new, n_active, C, "v_new")
+    _mod_pair(shift, scale, D, "hsa_unembed")
     _check("hsa_unembed", load().hsa_unembed(_ptr(h), _ptr(w_out), _ptr(v_new), n_active, D, C,
-                                             _dt(w_out), _stream(stream)))
+                                             _ptr(shift), _ptr(scale), _dt(w_out), _stream(stream)))
 
 
 def hsa_linear(a, w, out, act: int = 0, M: Optional[int] = None, stream=None):
@@ -301,15 +336,18 @@ def hsa_linear(a, w, out, act: int = 0, M: Optional[int] = None, stream=None):
                                            _stream(stream)))
 
 
-def hsa_linear_residual(a, w, h, M: Optional[int] = None, stream=None):
+def hsa_linear_residual(a, w, h, M: Optional[int] = None, gate=None, stream=None):
     _need(h, torch.float32, "h")
     M = a.shape[0] if M is None else M
     Nout, K = w.shape
     _need(w, a.dtype, "w")
     _rows(a, M, K, "a")
     _rows(h, M, Nout, "h")
+    if gate is not None:
+        _need(gate, torch.float32, "gate")
+        _shape(gate, (Nout,), "gate")
     _check("hsa_linear_residual", load().hsa_linear_residual(_ptr(a), _ptr(w), _ptr(h), M, Nout, K,
-                                                             _dt(a), _stream(stream)))
+                                                             _ptr(gate), _dt(a), _stream(stream)))
 
 
 def hsa_qkv_scatter(a, active_idx, n_active: int, w_qkv, q_out, k_cache, v_cache, stream=None):
@@ -327,42 +365,97 @@ def hsa_qkv_scatter(a, active_idx, n_active: int, w_qkv, q_out, k_cache, v_cache
                                                      _dt(a), _stream(stream)))
 
 
+def hsa_qk_norm_rope(q, k_cache, active_idx, n_active: int, dims: Dims, q_gain=None, k_gain=None,
+                     stream=None):
+    dt = torch.bfloat16 if dims.dtype == HSA_BF16 else torch.float32
+    _need(q, dt, "q")
+    _need(k_cache, dt, "k_cache")
+    _need(active_idx, torch.int32, "active_idx")
+    _rows(q, n_active, dims.D, "q")
+    _shape(k_cache, (dims.N, dims.D), "k_cache")
+    _rows(active_idx, n_active, None, "active_idx")
+    for t, n in ((q_gain, "q_gain"), (k_gain, "k_gain")):
+        if t is not None:
+            _need(t, torch.float32, n)
+            _shape(t, (dims.D,), n)
+    _check("hsa_qk_norm_rope", load().hsa_qk_norm_rope(_ptr(q), _ptr(k_cache), _ptr(active_idx), n_active,
+                                                       ct.byref(dims), _ptr(q_gain), _ptr(k_gain),
+                                                       _stream(stream)))
+
+
+def hsa_guidance(v_cond, v, rows: Optional[int] = None, g: float = 1.0, stream=None):
+    _need(v_cond, torch.float32, "v_cond")
+    _need(v, torch.float32, "v")
+    C = v.shape[1]
+    rows = v.shape[0] if rows is None else rows
+    _rows(v, rows, C, "v")
+    _rows(v_cond, rows, C, "v_cond")
+    _check("hsa_guidance", load().hsa_guidance(_ptr(v_cond), _ptr(v), rows, C, float(g), _stream(stream)))
+
+
 # ---------------------------------------------------------------- owning helpers
 class DeviceModel:
     """Device weights + per-layer K/V caches, and the hsa_model struct over them.
 
-    Weight layouts are those of include/hsa.h (out-major [out][in]).  Tensors are
-    kept referenced here so the raw pointers in the struct stay valid."""
+    Weight layouts are those of include/hsa.h (out-major [out][in]).  Feature
+    parameters are float32: per block q_gain, k_gain [D] (qk_norm), mod [6][D]
+    (adaln); the unconditional branch's k_text_u, v_text_u, k_cache_u,
+    v_cache_u in the model dtype (cfg); `time` holds t_w1 .. head_mod (adaln).
+    Tensors are kept referenced here so the raw pointers in the struct stay
+    valid."""
 
-    def __init__(self, dims: Dims, w_in: torch.Tensor, w_out: torch.Tensor, blocks: List[dict]):
+    def __init__(self, dims: Dims, w_in: torch.Tensor, w_out: torch.Tensor, blocks: List[dict],
+                 time: Optional[dict] = None, cfg_scale: float = 1.0):
         self.dims = dims
         dt = torch.bfloat16 if dims.dtype == HSA_BF16 else torch.float32
+        f32 = torch.float32
         N, C, D, F, T = dims.N, dims.C, dims.D, dims.F, dims.n_text
+        feat = dims.features
         if len(blocks) != dims.L:
             raise ValueError(f"blocks: expected {dims.L}, got {len(blocks)}")
-        shapes = {"w_qkv": (3 * D, D), "w_o": (D, D), "w_1": (F, D), "w_2": (D, F),
-                  "k_cache": (N, D), "v_cache": (N, D)}
+        shapes = {"w_qkv": ((3 * D, D), dt), "w_o": ((D, D), dt), "w_1": ((F, D), dt),
+                  "w_2": ((D, F), dt), "k_cache": ((N, D), dt), "v_cache": ((N, D), dt)}
         if T > 0:
-            shapes.update({"w_qx": (D, D), "w_ox": (D, D), "k_text": (T, D), "v_text": (T, D)})
+            shapes.update({"w_qx": ((D, D), dt), "w_ox": ((D, D), dt), "k_text": ((T, D), dt),
+                           "v_text": ((T, D), dt)})
+        if feat & FEAT_QK_NORM:
+            shapes.update({"q_gain": ((D,), f32), "k_gain": ((D,), f32)})
+        if feat & FEAT_ADALN:
+            shapes["mod"] = ((6, D), f32)
+        if feat & FEAT_CFG:
+            shapes.update({"k_text_u": ((T, D), dt), "v_text_u": ((T, D), dt),
+                           "k_cache_u": ((N, D), dt), "v_cache_u": ((N, D), dt)})
         for t, shp, n in ((w_in, (D, C), "w_in"), (w_out, (C, D), "w_out")):
             _need(t, dt, n)
             _shape(t, shp, n)
         for l, b in enumerate(blocks):
-            for n, shp in shapes.items():
+            for n, (shp, tdt) in shapes.items():
                 if b.get(n) is None:
                     raise ValueError(f"block {l}: {n} missing")
-                _need(b[n], dt, f"block {l} {n}")
+                _need(b[n], tdt, f"block {l} {n}")
                 _shape(b[n], shp, f"block {l} {n}")
+        tshapes = {"t_w1": (D, T_FREQ), "t_b1": (D,), "t_w2": (D, D), "t_b2": (D,),
+                   "t_w3": (6 * D, D), "t_b3": (6 * D,), "head_mod": (2, D)}
+        self.time = None
+        if feat & FEAT_ADALN:
+            if time is None:
+                raise ValueError("adaln: timestep weights missing")
+            for n, shp in tshapes.items():
+                if time.get(n) is None:
+                    raise ValueError(f"time: {n} missing")
+                _need(time[n], f32, f"time {n}")
+                _shape(time[n], shp, f"time {n}")
+            self.time = {n: time[n].contiguous() for n in tshapes}
         self.w_in, self.w_out = w_in.contiguous(), w_out.contiguous()
         self.blocks = [{k: (v.contiguous() if v is not None else None) for k, v in b.items()} for b in blocks]
         arr = (Block * dims.L)()
         for l, b in enumerate(self.blocks):
-            for name in ("w_qkv", "w_o", "w_1", "w_2", "w_qx", "w_ox", "k_cache", "v_cache",
-                         "k_text", "v_text"):
-                t = b.get(name)
+            for name in BLOCK_FIELDS:
+                t = b.get(name) if name in shapes else None
                 setattr(arr[l], name, None if t is None else _ptr(t))
         self._arr = arr
-        self.c = Model(dims, _ptr(self.w_in), _ptr(self.w_out), arr)
+        tp = [None if self.time is None else _ptr(self.time[n]) for n in TIME_FIELDS]
+        self.c = Model(dims, _ptr(self.w_in), _ptr(self.w_out), arr, *tp, float(cfg_scale))
 
 
 class DeviceState:
@@ -391,14 +484,27 @@ class DeviceState:
                        _ptr(self.active_idx), _ptr(self.pos), _ptr(self.workspace), nbytes)
 
 
+def hsa_time_embed(model: DeviceModel, sigma: float, e, e0, stream=None):
+    D = model.dims.D
+    for t, shp, n in ((e, (D,), "e"), (e0, (6, D), "e0")):
+        _need(t, torch.float32, n)
+        _shape(t, shp, n)
+    _check("hsa_time_embed", load().hsa_time_embed(ct.byref(model.c), float(sigma), _ptr(e), _ptr(e0),
+                                                   _stream(stream)))
+
+
 def hsa_block_forward(model: DeviceModel, layer: int, h, active_idx, n_active: int,
-                      ws: torch.Tensor, stream=None):
+                      ws: torch.Tensor, e0=None, branch: int = 0, stream=None):
     _need(h, torch.float32, "h")
     _need(active_idx, torch.int32, "active_idx")
     _rows(h, n_active, model.dims.D, "h")
     _rows(active_idx, n_active, None, "active_idx")
+    if e0 is not None:
+        _need(e0, torch.float32, "e0")
+        _shape(e0, (6, model.dims.D), "e0")
     _check("hsa_block_forward", load().hsa_block_forward(ct.byref(model.c), layer, _ptr(h), _ptr(active_idx),
-                                                         n_active, _ptr(ws), ws.numel(), _stream(stream)))
+                                                         n_active, _ptr(e0), branch, _ptr(ws), ws.numel(),
+                                                         _stream(stream)))
 
 
 def hsa_step(model: DeviceModel, sched: Schedule, state: DeviceState, it: int, sigma_i: float,
