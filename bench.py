@@ -15,8 +15,9 @@ stream), also at other active fractions and at the 14B-shaped layer, the full
 T = 40 sampling loop from fresh latents (also under other schedules and
 against dense sampling), iteration time
 against the active fraction, the Euler pass on a working set past the
-Infinity Cache, attainable peaks (an MFMA-only probe kernel and a 256 MiB
-device copy) and the CPU oracle on a bounded sample.
+Infinity Cache, the iteration with the Wan-style block features on (and with
+cross-attention and guidance batch 2), attainable peaks (an MFMA-only probe
+kernel and a 256 MiB device copy) and the CPU oracle on a bounded sample.
 
 Prints one JSON line.  `value` is HSA iterations per second.
 """
@@ -58,6 +59,8 @@ def parse():
     p.add_argument("--no-sweep", action="store_true",
                    help="skip the attention sweep over active fractions and the 14B-shaped layer")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-features", action="store_true",
+                   help="skip the iteration with the Wan-style block features switched on")
     p.add_argument("--no-scaling", action="store_true", help="skip the iteration-time vs active-fraction sweep")
     p.add_argument("--cpu-rows", type=int, default=2048)
     p.add_argument("--euler-tokens", type=int, default=1 << 24,
@@ -366,6 +369,88 @@ def step_scaling(H, model, state, c, sigma, reps: int = 5):
             "fit_max_rel_residual": round(float(np.max(np.abs(pred - ms) / np.array(ms))), 4)}
 
 
+def featured_model(H, model, c, features, n_text: int = 0, seed: int = 77):
+    """The bench stack with Wan-style block features switched on, sharing its
+    weights and caches: float32 gains 1 + N(0, 0.1^2), modulation tables
+    N(0, 0.1^2) with unit-centred gates, a timestep MLP, and with guidance
+    (needs n_text text rows) random cross-attention weights, text K/V for
+    both branches and a copy of every cache for the unconditional branch."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    D, N = c.D, c.N
+    bf = torch.bfloat16
+
+    def randn(shape, std, dtype=torch.float32):
+        return (torch.randn(shape, generator=g, device="cuda") * std).to(dtype)
+
+    blocks = []
+    for b in model.blocks:
+        nb = dict(b)
+        nb["q_gain"], nb["k_gain"] = 1 + randn((D,), 0.1), 1 + randn((D,), 0.1)
+        mod = randn((6, D), 0.1)
+        mod[2] += 1
+        mod[5] += 1
+        nb["mod"] = mod
+        if n_text:
+            for k in ("w_qx", "w_ox"):
+                nb[k] = randn((D, D), D ** -0.5, bf)
+            for k in ("k_text", "v_text", "k_text_u", "v_text_u"):
+                nb[k] = randn((n_text, D), 1.0, bf)
+        if "cfg" in features:
+            nb["k_cache_u"], nb["v_cache_u"] = b["k_cache"].clone(), b["v_cache"].clone()
+        blocks.append(nb)
+    time_w = {"t_w1": randn((D, H.T_FREQ), H.T_FREQ ** -0.5), "t_b1": randn((D,), 0.01),
+              "t_w2": randn((D, D), D ** -0.5), "t_b2": randn((D,), 0.01),
+              "t_w3": randn((6 * D, D), 0.3 * D ** -0.5), "t_b3": randn((6 * D,), 0.01),
+              "head_mod": randn((2, D), 0.1)}
+    dims = H.make_dims(N, c.C, D, c.H, c.Dh, c.F, c.L, n_text, bf, features=features, grid=c.grid)
+    return H.DeviceModel(dims, model.w_in, model.w_out, blocks, time_w, cfg_scale=5.0)
+
+
+def wan_features(H, model, state, c, sigma, plain_ms: float, steps: int = 5, reps: int = 20):
+    """The timed iteration with the Wan-style block features on: (a) qk-RMSNorm
+    + 3D rotary embedding + adaLN timestep modulation on the bench stack; (b)
+    additionally 512-token cross-attention and classifier-free guidance with
+    batch 2 (two block stacks per iteration on the same active rows).  Plus
+    the fused qk-norm + rotation pass alone (HIP events on its stream) against
+    HBM peak: it reads and writes the |A| fresh q rows and |A| K-cache rows,
+    8 |A| D bytes per launch in bf16."""
+    out = {"plain_ms": round(plain_ms, 3)}
+    sched = H.make_schedule(c.T, c.budgets, c.counts())
+    for name, feats, n_text in (("qk_rope_adaln", ("qk_norm", "rope3d", "adaln"), 0),
+                                ("qk_rope_adaln_xattn512_cfg", ("qk_norm", "rope3d", "adaln", "cfg"), 512)):
+        fm = featured_model(H, model, c, feats, n_text)
+        fs = H.DeviceState(fm.dims, state.x, state.group, state.v_hat, state.score)
+        t = timed_steps(H, fm, sched, fs, sigma, steps, 2) / steps * 1e3
+        out[name + "_ms"] = round(t, 3)
+        out[name + "_vs_plain"] = round(t / plain_ms, 4)
+        del fm, fs
+        torch.cuda.empty_cache()
+    # the fused qk-norm + rotation pass alone, at the step's |A_i|
+    nA = H.hsa_n_active(sched, ITER)
+    idx = torch.from_numpy(synth.active_random(c, nA)).to("cuda")
+    q = torch.randn((nA, c.D), device="cuda").to(torch.bfloat16)
+    kc = torch.randn((c.N, c.D), device="cuda").to(torch.bfloat16)
+    gq, gk = torch.ones(c.D, device="cuda"), torch.ones(c.D, device="cuda")
+    dims = H.make_dims(c.N, c.C, c.D, c.H, c.Dh, c.F, 1, 0, torch.bfloat16,
+                       features=("qk_norm", "rope3d"), grid=c.grid)
+    for _ in range(3):
+        H.hsa_qk_norm_rope(q, kc, idx, nA, dims, gq, gk)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(reps):
+        H.hsa_qk_norm_rope(q, kc, idx, nA, dims, gq, gk)
+    end.record()
+    torch.cuda.synchronize()
+    t = start.elapsed_time(end) / 1e3 / reps
+    nbytes = 8.0 * nA * c.D
+    out["qk_norm_rope"] = {"n_active": nA, "avg_launch_us": round(t * 1e6, 2),
+                           "bytes_per_launch": int(nbytes), "gbs": round(nbytes / t / 1e9, 1),
+                           "frac_of_hbm_peak": round(nbytes / t / 1e9 / PEAK_HBM_GBS, 4)}
+    return out
+
+
 def cpu_baseline(c, rows: int):
     """The oracle on a bounded sample of the same iteration: one block with `rows`
     active tokens over all N cached rows (its cost is linear in the number of
@@ -471,6 +556,11 @@ def main():
                 out["euler_hbm"]["gbs"] / out["attainable"]["copy_gbs"], 4)
     if not args.no_scaling:
         out["scaling_with_active_fraction"] = step_scaling(H, model, state, c, sigma)
+    if not args.no_features:
+        out["wan_features"] = wan_features(H, model, state, c, sigma, ms)
+        if "attainable" in out:
+            out["wan_features"]["qk_norm_rope"]["frac_of_attainable_copy"] = round(
+                out["wan_features"]["qk_norm_rope"]["gbs"] / out["attainable"]["copy_gbs"], 4)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(c, args.cpu_rows)
     print(json.dumps(out), flush=True)

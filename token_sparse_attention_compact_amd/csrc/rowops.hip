@@ -82,11 +82,21 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const float* __restrict_
 }
 
 // Row in registers: lane l holds float4 chunks l, l+64, ..., l+64(NV-1).
+// With MOD the block first combines shift and scale (base + add) once into
+// LDS, so the four rows of the block read them from there.
 template <typename OutT, int NV, bool MOD>
 __global__ __launch_bounds__(256) void layernorm_reg_kernel(const float* __restrict__ h,
                                                             OutT* __restrict__ out, int32_t rows,
                                                             int32_t D, ModVec shift,
                                                             ModVec scale) {
+  __shared__ f32x4 s_mod[MOD ? 2 * NV * kWave : 1];   // shift chunks, then scale chunks
+  if constexpr (MOD) {
+    for (int i = threadIdx.x; i < NV * kWave; i += kRowsPerBlock * kWave) {
+      s_mod[i] = load_mod4(shift, 4 * i);
+      s_mod[NV * kWave + i] = load_mod4(scale, 4 * i);
+    }
+    __syncthreads();
+  }
   const int lane = threadIdx.x & (kWave - 1);
   const int32_t row = blockIdx.x * kRowsPerBlock + threadIdx.x / kWave;
   if (row >= rows) return;
@@ -115,7 +125,12 @@ __global__ __launch_bounds__(256) void layernorm_reg_kernel(const float* __restr
 #pragma unroll
     for (int c = 0; c < 4; ++c) o[c] = (v[i][c] - mean) * rstd;
     const int32_t c4 = lane + kWave * i;
-    store4<OutT>(orow + 4 * c4, modulate4<MOD>(o, shift, scale, c4));
+    if constexpr (MOD) {
+      const f32x4 sh = s_mod[c4], sc = s_mod[NV * kWave + c4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) o[c] = __builtin_fmaf(o[c], 1.0f + sc[c], sh[c]);
+    }
+    store4<OutT>(orow + 4 * c4, o);
   }
 }
 

@@ -33,50 +33,17 @@ template <> struct Chunk<bf16> {
   typedef bf16x8 V;
 };
 
-// Rows 0..rows-1 are q rows (row j = token idx[j]); rows rows..2*rows-1 are
-// the K-cache rows idx[j].  Each row: x / sqrt(mean(x^2) + eps) * gain over D
-// (NORM), then pair (2i, 2i+1) of every head rotated by pos * freq (ROPE).
-// A 16-byte chunk never straddles two heads (Dh % 8 == 0).
+// Normalise (NORM) and rotate (ROPE) one row in place: x / sqrt(mean(x^2) +
+// eps) * gain over D, then pair (2i, 2i+1) of every head turned by the angle
+// whose (cos, sin) the wave's table cs holds for pair i of a head.  A 16-byte
+// chunk never straddles two heads (Dh % 8 == 0).
 template <typename T, bool NORM, bool ROPE>
-__global__ __launch_bounds__(256) void qk_norm_rope_kernel(
-    T* __restrict__ q, T* __restrict__ kc, const int32_t* __restrict__ idx, int32_t rows,
-    int32_t D, int32_t Dh, const float* __restrict__ q_gain, const float* __restrict__ k_gain,
-    int32_t grid_h, int32_t grid_w) {
-  // rotation frequency and axis (0 frame, 1 row, 2 column) of each pair of a head
-  __shared__ float s_freq[64];
-  __shared__ int32_t s_axis[64];
-  const int tid = threadIdx.x;
-  if constexpr (ROPE) {
-    const int P = Dh / 2;
-    if (tid < P) {
-      const int p_hw = P / 3;
-      const int p_f = P - 2 * p_hw;
-      int axis, j, p;
-      if (tid < p_f) {
-        axis = 0, j = tid, p = p_f;
-      } else if (tid < p_f + p_hw) {
-        axis = 1, j = tid - p_f, p = p_hw;
-      } else {
-        axis = 2, j = tid - p_f - p_hw, p = p_hw;
-      }
-      // 10000^(-j/p) in double precision, rounded once to float32
-      s_freq[tid] = (float)exp(-(double)j / (double)p * kLn10000);
-      s_axis[tid] = axis;
-    }
-    __syncthreads();
-  }
-  const int lane = tid & (kWave - 1);
-  const int32_t r = blockIdx.x * kRows + tid / kWave;
-  if (r >= 2 * rows) return;
-  const bool is_q = r < rows;
-  const int32_t j = is_q ? r : r - rows;
-  const int32_t tok = idx[j];
-  T* row = is_q ? q + (size_t)j * D : kc + (size_t)tok * D;
-  const float* gain = is_q ? q_gain : k_gain;
+__device__ __forceinline__ void norm_rotate_row(T* __restrict__ row, const float* __restrict__ gain,
+                                                const float2* __restrict__ cs, int32_t D,
+                                                int32_t Dh, int lane) {
   constexpr int CN = Chunk<T>::N;
   typedef typename Chunk<T>::V V;
   const int nch = D / CN;
-
   float rs = 1.0f;
   if constexpr (NORM) {
     float ss = 0.f;
@@ -89,13 +56,6 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(
       }
     }
     rs = 1.0f / sqrtf(wave_sum(ss) / (float)D + kRmsEps);
-  }
-  float pf = 0.f, py = 0.f, px = 0.f;
-  if constexpr (ROPE) {
-    const int32_t plane = grid_h * grid_w;
-    pf = (float)(tok / plane);
-    py = (float)((tok / grid_w) % grid_h);
-    px = (float)(tok % grid_w);
   }
   for (int c = lane; c < nch; c += kWave) {
     V v = reinterpret_cast<const V*>(row)[c];
@@ -114,20 +74,60 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(
       const int pair0 = ((c * CN) % Dh) / 2;
 #pragma unroll
       for (int pr = 0; pr < CN / 2; ++pr) {
-        const int jj = pair0 + pr;
-        const int ax = s_axis[jj];
-        const float pos = ax == 0 ? pf : (ax == 1 ? py : px);
-        float sn, cs;
-        sincosf(pos * s_freq[jj], &sn, &cs);
+        const float2 t = cs[pair0 + pr];
         const float a = x[2 * pr], b = x[2 * pr + 1];
-        x[2 * pr] = a * cs - b * sn;
-        x[2 * pr + 1] = a * sn + b * cs;
+        x[2 * pr] = a * t.x - b * t.y;
+        x[2 * pr + 1] = a * t.y + b * t.x;
       }
     }
 #pragma unroll
     for (int e = 0; e < CN; ++e) v[e] = from_f32<T>(x[e]);
     reinterpret_cast<V*>(row)[c] = v;
   }
+}
+
+// One wavefront per active token j: its q row j and its K-cache row idx[j].
+// The token's rotation (cos, sin) per pair of a head is evaluated once into
+// the wave's LDS table (one pair per lane, precise sincosf) and shared by all
+// heads of both rows.
+template <typename T, bool NORM, bool ROPE>
+__global__ __launch_bounds__(256) void qk_norm_rope_kernel(
+    T* __restrict__ q, T* __restrict__ kc, const int32_t* __restrict__ idx, int32_t rows,
+    int32_t D, int32_t Dh, const float* __restrict__ q_gain, const float* __restrict__ k_gain,
+    int32_t grid_h, int32_t grid_w) {
+  __shared__ float2 s_cs[kRows][64];
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wid = tid / kWave;
+  const int32_t j = blockIdx.x * kRows + wid;
+  const bool valid = j < rows;
+  const int32_t tok = valid ? idx[j] : 0;
+  if constexpr (ROPE) {
+    // pair `lane` of a head: its axis (frame, row, column section) and
+    // frequency 10000^(-j'/p), evaluated in double and rounded once
+    const int P = Dh / 2;
+    if (lane < P) {
+      const int p_hw = P / 3;
+      const int p_f = P - 2 * p_hw;
+      int32_t pos;
+      int jp, p;
+      if (lane < p_f) {
+        pos = tok / (grid_h * grid_w), jp = lane, p = p_f;
+      } else if (lane < p_f + p_hw) {
+        pos = (tok / grid_w) % grid_h, jp = lane - p_f, p = p_hw;
+      } else {
+        pos = tok % grid_w, jp = lane - p_f - p_hw, p = p_hw;
+      }
+      const float freq = (float)exp(-(double)jp / (double)p * kLn10000);
+      float sn, cs;
+      sincosf((float)pos * freq, &sn, &cs);
+      s_cs[wid][lane] = make_float2(cs, sn);
+    }
+    __syncthreads();
+  }
+  if (!valid) return;
+  norm_rotate_row<T, NORM, ROPE>(q + (size_t)j * D, q_gain, s_cs[wid], D, Dh, lane);
+  norm_rotate_row<T, NORM, ROPE>(kc + (size_t)tok * D, k_gain, s_cs[wid], D, Dh, lane);
 }
 
 __device__ __forceinline__ float silu(float x) { return x / (1.0f + expf(-x)); }
@@ -202,7 +202,7 @@ template <typename T>
 void qk_dispatch(T* q, T* kc, const int32_t* idx, int32_t rows, int32_t D, int32_t Dh, bool norm,
                  bool rope, const float* qg, const float* kg, int32_t gh, int32_t gw,
                  hipStream_t s) {
-  const int blocks = cdiv(2 * (int64_t)rows, kRows);
+  const int blocks = cdiv(rows, kRows);
   if (norm && rope)
     qk_norm_rope_kernel<T, true, true>
         <<<blocks, 256, 0, s>>>(q, kc, idx, rows, D, Dh, qg, kg, gh, gw);
