@@ -300,12 +300,17 @@ def select_margin(score, counts):
     return min(gaps) if gaps else np.inf
 
 
-@pytest.mark.parametrize("features,n_text", [(ALL, 0), (ALL + ("cfg",), 8)])
-def test_featured_step_full_run_f32(features, n_text):
+@pytest.mark.parametrize("features,n_text,empty", [(ALL, 0, False), (ALL + ("cfg",), 8, False),
+                                                   (ALL + ("cfg",), 8, True)])
+def test_featured_step_full_run_f32(features, n_text, empty):
     """DiT-lite float32 on the 4x8x8 grid with the features on: all 8
     iterations (regrouping from i = 3 on) against the oracle, every state
-    array after every iteration, both branches' caches under guidance."""
+    array after every iteration, both branches' caches under guidance.
+    `empty`: budgets {8, 4, 2} with an empty full-budget group, so every odd
+    iteration has no active token (the cached Euler step alone)."""
     c = synth.CONFIGS[1].with_(features=features, n_text=n_text, text_dim=32 if n_text else 0)
+    if empty:
+        c = c.with_(budgets=(8, 4, 2), shares=(0.0, 0.5, 0.5))
     say(f"featured hsa_step fp32 full run {features}")
     om = oracle_model(c)
     m = device_model(c)
@@ -369,3 +374,52 @@ def test_featured_step_mid_run_bf16():
             kg = host(m.blocks[l]["k_cache" + sfx])
             np.testing.assert_array_equal(kg[skipped], s0["k_cache"][l][skipped])
             assert rel_l2(kg[out["active_idx"]], ref[l][out["active_idx"]]) < TOL_BF16
+
+
+def test_featured_step_14b_shape_properties():
+    """The 14B-shaped block (N = 75600 on the 21x45x80 grid, D 5120, 40x128
+    heads, F 13824, 512 text tokens) with every feature and guidance, one
+    25%-active iteration from a synthetic mid-run state: properties that hold
+    at any size, plus the layer-0 fresh K/V of sampled active rows against
+    the oracle (they depend only on the row itself)."""
+    c = synth.CONFIGS[4].with_(L=1, features=ALL + ("cfg",))
+    say("featured hsa_step 14B-shaped properties")
+    i = 11
+    om = oracle_model(c)
+    s0 = synth.mid_run_state(c)
+    m = device_model(c, s0["k_cache"], s0["v_cache"])
+    sched = H.make_schedule(c.T, c.budgets, c.counts())
+    sigma = synth.sigma_schedule(c.T)
+    st = H.DeviceState(m.dims, dev(s0["x"]), dev(s0["group"], torch.uint8), dev(s0["v_hat"]),
+                       dev(s0["score"]))
+    H.hsa_step(m, sched, st, i, float(sigma[i]), float(sigma[i + 1]), False)
+    torch.cuda.synchronize()
+    idx, pos = O.active_set(s0["group"], c.budgets, c.T, i)
+    assert idx.size == 18900
+    np.testing.assert_array_equal(st.active_idx[:idx.size].cpu().numpy(), idx)
+    np.testing.assert_array_equal(st.pos.cpu().numpy(), pos)
+    skipped = np.setdiff1d(np.arange(c.N), idx)
+    ds = np.float32(np.float32(sigma[i + 1]) - np.float32(sigma[i]))
+    xs = (s0["x"][skipped].astype(np.float64) + np.float64(ds) * s0["v_hat"][skipped]).astype(np.float32)
+    np.testing.assert_array_equal(host(st.x)[skipped].astype(np.float32), xs)
+    np.testing.assert_array_equal(host(st.v_hat)[skipped], s0["v_hat"][skipped])
+    assert np.all(np.isfinite(host(st.v_hat)[idx]))
+    kc, kcu = host(m.blocks[0]["k_cache"]), host(m.blocks[0]["k_cache_u"])
+    vc, vcu = host(m.blocks[0]["v_cache"]), host(m.blocks[0]["v_cache_u"])
+    for a in (kc, kcu):
+        np.testing.assert_array_equal(a[skipped], s0["k_cache"][0][skipped])
+    for a in (vc, vcu):
+        np.testing.assert_array_equal(a[skipped], s0["v_cache"][0][skipped])
+    # text enters after self-attention: layer-0 fresh K/V are the same in both branches
+    np.testing.assert_array_equal(kcu[idx], kc[idx])
+    np.testing.assert_array_equal(vcu[idx], vc[idx])
+    rows = np.sort(np.random.default_rng(3).choice(idx.size, 16, replace=False))
+    tok = idx[rows]
+    _, e0 = O.time_embedding(om, sigma[i])
+    mod = O.block_modulation(om, 0, e0)
+    stq = om.store
+    a = stq.act(O.modulated_layer_norm(O.embed(om, s0["x"], tok), mod[0], mod[1]))
+    kv = a @ om.blocks[0]["w_qkv"][c.D:].T
+    k_ref = stq.act(O.qk_transform(om.dims, stq.act(kv[:, :c.D]), tok, om.blocks[0]["k_gain"]))
+    assert rel_l2(kc[tok], k_ref) < TOL_BF16
+    assert rel_l2(vc[tok], stq.act(kv[:, c.D:])) < TOL_BF16
