@@ -160,7 +160,9 @@ typedef struct {
 /* Status code as text (static string, never NULL). */
 const char *hsa_status_str(int32_t status);
 
-/* Library ABI version (increments when a signature changes). */
+/* Library ABI version (increments when a signature or struct changes); a
+ * library built from this header returns HSA_ABI_VERSION. */
+#define HSA_ABI_VERSION 2
 int32_t hsa_abi_version(void);
 
 /* Workspace needed by hsa_step / hsa_block_forward for these dims (host out). */

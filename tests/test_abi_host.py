@@ -28,6 +28,15 @@ def test_every_declared_symbol_is_exported():
     assert set(H.EXPORTED) == set(names), "binding list and header disagree"
 
 
+def test_abi_version_matches_header_and_binding():
+    text = open(HEADER).read()
+    v = int(re.search(r"#define HSA_ABI_VERSION (\d+)", text).group(1))
+    assert H.load().hsa_abi_version() == v == H.ABI_VERSION
+    # struct sizes the binding marshals agree with the header's field lists
+    assert [f for f, _ in H.Dims._fields_][-4:] == ["features", "grid_f", "grid_h", "grid_w"]
+    assert len(H.Block._fields_) == 17 and H.Model._fields_[-1][0] == "cfg_scale"
+
+
 def test_status_strings():
     for code in (0, -1, -2, -3, -4, -5, -6, -7, 99):
         assert H.status_str(code)
