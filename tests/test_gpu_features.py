@@ -423,3 +423,50 @@ def test_featured_step_14b_shape_properties():
     k_ref = stq.act(O.qk_transform(om.dims, stq.act(kv[:, :c.D]), tok, om.blocks[0]["k_gain"]))
     assert rel_l2(kc[tok], k_ref) < TOL_BF16
     assert rel_l2(vc[tok], stq.act(kv[:, c.D:])) < TOL_BF16
+
+
+def test_featured_step_graph_capture_replays_match_eager():
+    """The featured iteration (timestep MLP, modulated LayerNorms, gated
+    residuals, qk-norm + rotation pass, two guidance branches and the
+    combine) enqueues kernels only, so it captures in a HIP graph: three
+    replays from the same state, with other device work in between, each
+    equal the eager iteration bit for bit."""
+    c = tiny(ALL + ("cfg",), "bf16", Dh=128, H_=2, grid=(2, 20, 16), n_text=16, text_dim=64, L=2,
+             T=40, budgets=(40, 20, 10), shares=(0.25, 0.25, 0.5), regroup=(10, 20, 30))
+    say("featured hsa_step graph capture")
+    i = 10
+    s0 = synth.mid_run_state(c)
+    m = device_model(c, s0["k_cache"], s0["v_cache"])
+    sched = H.make_schedule(c.T, c.budgets, c.counts())
+    sigma = synth.sigma_schedule(c.T)
+    st = H.DeviceState(m.dims, dev(s0["x"]), dev(s0["group"], torch.uint8), dev(s0["v_hat"]),
+                       dev(s0["score"]))
+    bufs = [st.x, st.v_hat, st.score, st.group] + [
+        b[n] for b in m.blocks for n in ("k_cache", "v_cache", "k_cache_u", "v_cache_u")]
+    init = [b.clone() for b in bufs]
+
+    def restore():
+        for b, v in zip(bufs, init):
+            b.copy_(v)
+
+    def step():
+        H.hsa_step(m, sched, st, i, float(sigma[i]), float(sigma[i + 1]), True)
+
+    restore()
+    step()
+    torch.cuda.synchronize()
+    eager = [b.clone() for b in bufs]
+    restore()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    other = torch.randn(512, 512, device=DEV)
+    for rep in range(3):
+        restore()
+        other = other @ other.T / 512.0
+        g.replay()
+        torch.cuda.synchronize()
+        for b, e in zip(bufs, eager):
+            assert torch.equal(b, e), f"replay {rep} differs from the eager iteration"
