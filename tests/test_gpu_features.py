@@ -300,32 +300,33 @@ def select_margin(score, counts):
     return min(gaps) if gaps else np.inf
 
 
-@pytest.mark.parametrize("features,n_text,empty", [(ALL, 0, False), (ALL + ("cfg",), 8, False),
-                                                   (ALL + ("cfg",), 8, True)])
-def test_featured_step_full_run_f32(features, n_text, empty):
+@pytest.mark.parametrize("features,n_text,empty,m", [(ALL, 0, False, 0), (ALL + ("cfg",), 8, False, 0),
+                                                     (ALL + ("cfg",), 8, True, 0), (ALL + ("cfg",), 8, True, 2)])
+def test_featured_step_full_run_f32(features, n_text, empty, m):
     """DiT-lite float32 on the 4x8x8 grid with the features on: all 8
     iterations (regrouping from i = 3 on) against the oracle, every state
     array after every iteration, both branches' caches under guidance.
     `empty`: budgets {8, 4, 2} with an empty full-budget group, so every odd
-    iteration has no active token (the cached Euler step alone)."""
-    c = synth.CONFIGS[1].with_(features=features, n_text=n_text, text_dim=32 if n_text else 0)
+    iteration has no active token (the cached Euler step alone); `m`: phase
+    window, the first and last m iterations run every token."""
+    c = synth.CONFIGS[1].with_(features=features, n_text=n_text, text_dim=32 if n_text else 0, m=m)
     if empty:
         c = c.with_(budgets=(8, 4, 2), shares=(0.0, 0.5, 0.5))
     say(f"featured hsa_step fp32 full run {features}")
     om = oracle_model(c)
-    m = device_model(c)
-    sched = H.make_schedule(c.T, c.budgets, c.counts())
-    osched = O.Schedule(c.T, list(c.budgets), c.counts(), regroup=c.regroup)
+    dm = device_model(c)
+    sched = H.make_schedule(c.T, c.budgets, c.counts(), m=c.m)
+    osched = O.Schedule(c.T, list(c.budgets), c.counts(), m=c.m, regroup=c.regroup)
     sigma = synth.sigma_schedule(c.T)
     x0, g0 = synth.x0(c), synth.group0(c)
-    st = H.DeviceState(m.dims, dev(x0), dev(g0, torch.uint8))
+    st = H.DeviceState(dm.dims, dev(x0), dev(g0, torch.uint8))
     ost = O.init_state(om.dims, x0, g0)
     for i in range(c.T):
         if i in c.regroup:
             fin = np.isfinite(ost.score)
             dev_rel = np.max(np.abs(host(st.score)[fin] - ost.score[fin]) / np.abs(ost.score[fin]))
             assert select_margin(ost.score, c.counts()) > 10 * dev_rel
-        H.hsa_step(m, sched, st, i, float(sigma[i]), float(sigma[i + 1]), i in c.regroup)
+        H.hsa_step(dm, sched, st, i, float(sigma[i]), float(sigma[i + 1]), i in c.regroup)
         torch.cuda.synchronize()
         O.sample(om, osched, ost, sigma, iters=[i])
         np.testing.assert_array_equal(st.group.cpu().numpy(), ost.group)
@@ -335,10 +336,10 @@ def test_featured_step_full_run_f32(features, n_text, empty):
         np.testing.assert_array_equal(np.isfinite(host(st.score)), fin)
         if fin.any():
             assert rel_l2(host(st.score)[fin], ost.score[fin]) < TOL_F32
-        assert rel_l2(host(m.blocks[0]["k_cache"]), ost.k_cache[0]) < TOL_F32
+        assert rel_l2(host(dm.blocks[0]["k_cache"]), ost.k_cache[0]) < TOL_F32
         if "cfg" in features:
-            assert rel_l2(host(m.blocks[0]["k_cache_u"]), ost.k_cache_u[0]) < TOL_F32
-            assert rel_l2(host(m.blocks[0]["v_cache_u"]), ost.v_cache_u[0]) < TOL_F32
+            assert rel_l2(host(dm.blocks[0]["k_cache_u"]), ost.k_cache_u[0]) < TOL_F32
+            assert rel_l2(host(dm.blocks[0]["v_cache_u"]), ost.v_cache_u[0]) < TOL_F32
 
 
 def test_featured_step_mid_run_bf16():
