@@ -61,6 +61,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-features", action="store_true",
                    help="skip the iteration with the Wan-style block features switched on")
+    p.add_argument("--wan14b", action="store_true",
+                   help="also time the whole 14B-shaped iteration (40 blocks, N=75600; ~155 GB of HBM)")
     p.add_argument("--no-scaling", action="store_true", help="skip the iteration-time vs active-fraction sweep")
     p.add_argument("--cpu-rows", type=int, default=2048)
     p.add_argument("--euler-tokens", type=int, default=1 << 24,
@@ -451,6 +453,29 @@ def wan_features(H, model, state, c, sigma, plain_ms: float, steps: int = 5, rep
     return out
 
 
+def wan14b_iteration(H, steps: int = 2):
+    """The whole 14B-shaped iteration (opt-in, --wan14b): 40 blocks, N = 75600
+    (21 x 45 x 80), D 5120, 40 x 128 heads, F 13824, 512-token cross-attention,
+    iteration 11 of the {40, 20, 10} schedule (|A| = 18900, 25%), regroup on;
+    (a) the plain block with cross-attention, (b) with qk-RMSNorm, 3D RoPE,
+    adaLN modulation and guidance batch 2 (a second cache set: ~155 GB of HBM
+    in all)."""
+    c = synth.CONFIGS[4]
+    sched = H.make_schedule(c.T, c.budgets, c.counts())
+    sigma = synth.sigma_schedule(c.T)
+    base, state = device_inputs(c, H, seed_base=5)
+    out = {"workload": "wan14b-shaped 40-block stack, N=75600 (21x45x80), 25% active, 512 text tokens",
+           "n_active": H.hsa_n_active(sched, ITER)}
+    for name, feats in (("xattn", ()), ("xattn_qk_rope_adaln_cfg", ("qk_norm", "rope3d", "adaln", "cfg"))):
+        fm = featured_model(H, base, c, feats, c.n_text)
+        fs = H.DeviceState(fm.dims, state.x, state.group, state.v_hat, state.score)
+        t = timed_steps(H, fm, sched, fs, sigma, steps, 1) / steps
+        out[name + "_s_per_iter"] = round(t, 3)
+        del fm, fs
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(c, rows: int):
     """The oracle on a bounded sample of the same iteration: one block with `rows`
     active tokens over all N cached rows (its cost is linear in the number of
@@ -561,6 +586,10 @@ def main():
         if "attainable" in out:
             out["wan_features"]["qk_norm_rope"]["frac_of_attainable_copy"] = round(
                 out["wan_features"]["qk_norm_rope"]["gbs"] / out["attainable"]["copy_gbs"], 4)
+    if args.wan14b:
+        del model, state
+        torch.cuda.empty_cache()
+        out["wan14b_iteration"] = wan14b_iteration(H)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(c, args.cpu_rows)
     print(json.dumps(out), flush=True)
