@@ -162,7 +162,7 @@ const char *hsa_status_str(int32_t status);
 
 /* Library ABI version (increments when a signature or struct changes); a
  * library built from this header returns HSA_ABI_VERSION. */
-#define HSA_ABI_VERSION 2
+#define HSA_ABI_VERSION 3
 int32_t hsa_abi_version(void);
 
 /* Workspace needed by hsa_step / hsa_block_forward for these dims (host out). */
@@ -252,13 +252,16 @@ hsa_status hsa_linear(const void *a, const void *w, void *out, int32_t M, int32_
 hsa_status hsa_linear_residual(const void *a, const void *w, float *h, int32_t M, int32_t Nout,
                                int32_t K, const float *gate, hsa_dtype dtype, void *stream);
 
-/* KV-cache synchronisation steps 1-2 (section 2.2): [q | k | v] = a w_qkv^T
- * for the n_active rows of a; q goes to q_out [n_active][D]; k and v rows
+/* KV-cache synchronisation steps 1-2 (section 2.2): [q | k | v] = a_j w_qkv^T
+ * for the n_active active rows; q goes to q_out [n_active][D]; k and v rows
  * overwrite k_cache[active_idx[j]] and v_cache[active_idx[j]] ([N][D]).
- * Rows of the cache not in active_idx are not touched. */
-hsa_status hsa_qkv_scatter(const void *a, const int32_t *active_idx, const void *w_qkv,
-                           void *q_out, void *k_cache, void *v_cache, int32_t n_active,
-                           int32_t N, int32_t D, hsa_dtype dtype, void *stream);
+ * Rows of the cache not in active_idx are not touched.  gather 0: a_j is row
+ * j of a [n_active][D]; gather 1: a_j = a[active_idx[j]] of a [N][D] (the
+ * active rows read straight from a per-token hidden state; bf16 needs
+ * N * D * 2 < 2^32). */
+hsa_status hsa_qkv_scatter(const void *a, const int32_t *active_idx, int32_t gather,
+                           const void *w_qkv, void *q_out, void *k_cache, void *v_cache,
+                           int32_t n_active, int32_t N, int32_t D, hsa_dtype dtype, void *stream);
 
 /* qk-RMSNorm and 3D rotary embedding (HSA_FEAT_QK_NORM / HSA_FEAT_ROPE3D,
  * whichever dims->features holds; neither: nothing to do) in place on q

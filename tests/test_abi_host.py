@@ -35,6 +35,8 @@ def test_abi_version_matches_header_and_binding():
     # struct sizes the binding marshals agree with the header's field lists
     assert [f for f, _ in H.Dims._fields_][-4:] == ["features", "grid_f", "grid_h", "grid_w"]
     assert len(H.Block._fields_) == 17 and H.Model._fields_[-1][0] == "cfg_scale"
+    # gather flag of the QKV projection is validated
+    assert H.load().hsa_qkv_scatter(None, None, 2, None, None, None, None, 4, 8, 64, 1, None) == -1
 
 
 def test_status_strings():

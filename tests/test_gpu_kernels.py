@@ -331,6 +331,41 @@ def test_qkv_scatter_positions(dtype):
     assert rel_l2(v_h[idx], ref[:, 2 * D:]) < tol
 
 
+@pytest.mark.parametrize("dtype,N,D,nA", [(torch.bfloat16, 700, 256, 233), (torch.float32, 700, 256, 233),
+                                           (torch.bfloat16, 32760, 1536, 8190)])
+def test_qkv_scatter_gather_mode(dtype, N, D, nA):
+    """gather=1 reads the active rows a[active_idx[j]] straight from the [N][D]
+    per-token matrix: bit-identical to the compact call on those rows
+    (ragged 233-row case and the Wan-1.3B stage shape), and against the oracle
+    on sampled rows."""
+    say(f"qkv gather {dtype} N={N} D={D} nA={nA}")
+    rs = np.random.default_rng(22)
+    w = (rs.standard_normal((3 * D, D)) / np.sqrt(D)).astype(np.float32)
+    if dtype == torch.bfloat16:
+        w = bf(w)
+    idx = np.sort(rs.choice(N, nA, replace=False)).astype(np.int32)
+    ta = torch.randn(N, D, device=DEV).to(dtype)            # the per-token matrix
+    ti, tw = dev(idx, torch.int32), dev(w, dtype)
+    out = []
+    for gather in (False, True):
+        kc = torch.zeros(N, D, dtype=dtype, device=DEV)
+        vc = torch.zeros(N, D, dtype=dtype, device=DEV)
+        q = torch.empty(nA, D, dtype=dtype, device=DEV)
+        a = ta if gather else ta[ti.long()].contiguous()
+        H.hsa_qkv_scatter(a, ti, nA, tw, q, kc, vc, gather=gather)
+        torch.cuda.synchronize()
+        out.append((q, kc, vc))
+    for x, y in zip(out[0], out[1]):
+        assert torch.equal(x, y), "gathered rows differ from the compact call"
+    rows = np.sort(rs.choice(nA, min(nA, 64), replace=False))
+    ref = host(ta)[idx[rows]] @ w.astype(np.float64).T
+    tol = 5e-3 if dtype == torch.bfloat16 else 1e-6
+    q, kc, vc = out[1]
+    assert rel_l2(host(q)[rows], ref[:, :D]) < tol
+    assert rel_l2(host(kc)[idx[rows]], ref[:, D:2 * D]) < tol
+    assert rel_l2(host(vc)[idx[rows]], ref[:, 2 * D:]) < tol
+
+
 # ---------------------------------------------------------------- attention
 
 def _attn_case(nA, nkv, Hh, Dh, dtype, tol, seed=0):

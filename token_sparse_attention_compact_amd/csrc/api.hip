@@ -444,11 +444,13 @@ hsa_status hsa_linear_residual(const void* a, const void* w, float* h, int32_t M
                      as_stream(stream));
 }
 
-hsa_status hsa_qkv_scatter(const void* a, const int32_t* active_idx, const void* w_qkv,
-                           void* q_out, void* k_cache, void* v_cache, int32_t n_active, int32_t N,
-                           int32_t D, hsa_dtype dtype, void* stream) {
+hsa_status hsa_qkv_scatter(const void* a, const int32_t* active_idx, int32_t gather,
+                           const void* w_qkv, void* q_out, void* k_cache, void* v_cache,
+                           int32_t n_active, int32_t N, int32_t D, hsa_dtype dtype, void* stream) {
   RETURN_IF(check_gemm_shape(n_active, 3 * D, D, dtype));
   if (n_active > N || N <= 0) return HSA_ERR_SHAPE;
+  if (gather != 0 && gather != 1) return HSA_ERR_ARG;
+  if (gather && dtype == HSA_BF16 && !fits_buffer((int64_t)N * D * 2)) return HSA_ERR_SHAPE;
   if (n_active == 0) return HSA_OK;
   CHECK_PTR(a);
   CHECK_PTR(active_idx);
@@ -456,7 +458,7 @@ hsa_status hsa_qkv_scatter(const void* a, const int32_t* active_idx, const void*
   CHECK_PTR(q_out);
   CHECK_PTR(k_cache);
   CHECK_PTR(v_cache);
-  EpiArgs e{q_out, nullptr, k_cache, v_cache, active_idx, D, ModVec{nullptr, nullptr}};
+  EpiArgs e{q_out, nullptr, k_cache, v_cache, active_idx, D, ModVec{nullptr, nullptr}, gather ? N : 0};
   return launch_gemm(a, w_qkv, n_active, 3 * D, D, dtype, EPI_QKV_SCATTER, e, as_stream(stream));
 }
 

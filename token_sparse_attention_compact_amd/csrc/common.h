@@ -122,6 +122,8 @@ struct EpiArgs {
   const int32_t* idx;   // EPI_QKV_SCATTER row -> cache row
   int32_t D;            // EPI_QKV_SCATTER width of each of q, k, v
   ModVec gate;          // EPI_RESID_GATED, [N]
+  int32_t gather_rows;  // EPI_QKV_SCATTER only: > 0 when row m of a is a[idx[m]] of an
+                        // a with gather_rows rows; 0 when a is [M][K]
 };
 hsa_status launch_gemm(const void* a, const void* w, int32_t M, int32_t N, int32_t K,
                        hsa_dtype dt, int epi, const EpiArgs& ep, hipStream_t s);

@@ -17,6 +17,8 @@
 // columns of a row.
 //
 // float32 path (small float32 workloads): LDS-tiled FMA GEMM, 64x64 tiles.
+// The QKV projection can read its rows gathered, a[idx[m]], from a larger
+// matrix (the per-token hidden state), on both paths.
 #include "common.h"
 
 namespace hsa {
@@ -192,12 +194,17 @@ __global__ __launch_bounds__(G::THREADS, G::MINB) void gemm_bf16_kernel(
 
   // DMA source offsets (bytes from the tile's k-slice base), fixed over k.
   // Load j of wave w fills 16-byte slots (j*WAVES + w)*64 + lane of a tile.
+  // QKV may read its rows gathered from a larger matrix: row m of the tile is
+  // a[idx[m]] (rows past M repeat the last active row; they are not stored).
+  const bool gather = EPI == EPI_QKV_SCATTER && ep.gather_rows > 0;
   uint32_t voff_a[G::LOADS_A], voff_b[G::LOADS_B];
 #pragma unroll
   for (int j = 0; j < G::LOADS_A; ++j) {
     const int sl = (j * G::WAVES + wave) * 64 + lane;
     const int r = sl >> 3, p = sl & 7;
-    voff_a[j] = (uint32_t)(r * K * 2 + gpos(r, p) * 16);   // gpos(r, .) is an involution
+    const uint32_t row_off = gather ? (uint32_t)ep.idx[min(m0 + r, M - 1)] * (uint32_t)K * 2u
+                                    : (uint32_t)(r * K * 2);
+    voff_a[j] = row_off + (uint32_t)(gpos(r, p) * 16);   // gpos(r, .) is an involution
   }
 #pragma unroll
   for (int j = 0; j < G::LOADS_B; ++j) {
@@ -205,9 +212,10 @@ __global__ __launch_bounds__(G::THREADS, G::MINB) void gemm_bf16_kernel(
     const int r = sl >> 3, p = sl & 7;
     voff_b[j] = (uint32_t)(r * K * 2 + gpos(r, p) * 16);
   }
-  const uint32_t bytes_a = (uint32_t)(M - m0) * (uint32_t)K * 2u;
+  const uint32_t bytes_a = gather ? (uint32_t)ep.gather_rows * (uint32_t)K * 2u
+                                  : (uint32_t)(M - m0) * (uint32_t)K * 2u;
   const uint32_t bytes_b = (uint32_t)(min(N, n0 + BN) - n0) * (uint32_t)K * 2u;
-  const char* a_base = reinterpret_cast<const char*>(A) + (size_t)m0 * K * 2;
+  const char* a_base = reinterpret_cast<const char*>(A) + (gather ? 0 : (size_t)m0 * K * 2);
   const char* b_base = reinterpret_cast<const char*>(W) + (size_t)n0 * K * 2;
 
   auto issue = [&](int kt, int stage) {
@@ -348,11 +356,13 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
   const int tid = threadIdx.x;
   const int lr = tid >> 2, lk = (tid & 3) * 4;
   const int ty = tid >> 4, tx = tid & 15;
+  const bool gather = EPI == EPI_QKV_SCATTER && ep.gather_rows > 0;
+  const int32_t arow = (m0 + lr < M && gather) ? ep.idx[m0 + lr] : m0 + lr;   // row of a
   float acc[4][4] = {};
   for (int32_t k0 = 0; k0 < K; k0 += FK) {
     const int32_t gk = k0 + lk;
     f32x4 va = {0.f, 0.f, 0.f, 0.f}, vb = {0.f, 0.f, 0.f, 0.f};
-    if (m0 + lr < M && gk < K) va = *reinterpret_cast<const f32x4*>(A + (size_t)(m0 + lr) * K + gk);
+    if (m0 + lr < M && gk < K) va = *reinterpret_cast<const f32x4*>(A + (size_t)arow * K + gk);
     if (n0 + lr < N && gk < K) vb = *reinterpret_cast<const f32x4*>(W + (size_t)(n0 + lr) * K + gk);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {

@@ -21,7 +21,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "lib
 
 HSA_F32, HSA_BF16 = 0, 1
 MAX_GROUPS = 8
-ABI_VERSION = 2
+ABI_VERSION = 3
 # optional block features (hsa_dims.features)
 FEAT_QK_NORM, FEAT_ROPE3D, FEAT_ADALN, FEAT_CFG = 1, 2, 4, 8
 FEATURE_BITS = {"qk_norm": FEAT_QK_NORM, "rope3d": FEAT_ROPE3D, "adaln": FEAT_ADALN, "cfg": FEAT_CFG}
@@ -111,7 +111,7 @@ def load() -> ct.CDLL:
         "hsa_unembed": ([P, P, P, I, I, I, P, P, ct.c_int, P], I),
         "hsa_linear": ([P, P, P, I, I, I, I, ct.c_int, P], I),
         "hsa_linear_residual": ([P, P, P, I, I, I, P, ct.c_int, P], I),
-        "hsa_qkv_scatter": ([P, P, P, P, P, P, I, I, I, ct.c_int, P], I),
+        "hsa_qkv_scatter": ([P, P, I, P, P, P, P, I, I, I, ct.c_int, P], I),
         "hsa_qk_norm_rope": ([P, P, P, I, ct.POINTER(Dims), P, P, P], I),
         "hsa_time_embed": ([ct.POINTER(Model), F, P, P, P], I),
         "hsa_guidance": ([P, P, I, I, F, P], I),
@@ -350,18 +350,24 @@ def hsa_linear_residual(a, w, h, M: Optional[int] = None, gate=None, stream=None
                                                              _ptr(gate), _dt(a), _stream(stream)))
 
 
-def hsa_qkv_scatter(a, active_idx, n_active: int, w_qkv, q_out, k_cache, v_cache, stream=None):
+def hsa_qkv_scatter(a, active_idx, n_active: int, w_qkv, q_out, k_cache, v_cache, gather: bool = False,
+                    stream=None):
+    """gather=False: row j of a ([>= n_active][D]) is active row j; gather=True:
+    a is the [N][D] per-token matrix and active row j is a[active_idx[j]]."""
     _need(active_idx, torch.int32, "active_idx")
     N, D = k_cache.shape
     for t, n in ((w_qkv, "w_qkv"), (q_out, "q_out"), (k_cache, "k_cache"), (v_cache, "v_cache")):
         _need(t, a.dtype, n)
     _shape(v_cache, (N, D), "v_cache")
     _shape(w_qkv, (3 * D, D), "w_qkv")
-    _rows(a, n_active, D, "a")
+    if gather:
+        _shape(a, (N, D), "a")
+    else:
+        _rows(a, n_active, D, "a")
     _rows(q_out, n_active, D, "q_out")
     _rows(active_idx, n_active, None, "active_idx")
-    _check("hsa_qkv_scatter", load().hsa_qkv_scatter(_ptr(a), _ptr(active_idx), _ptr(w_qkv), _ptr(q_out),
-                                                     _ptr(k_cache), _ptr(v_cache), n_active, N, D,
+    _check("hsa_qkv_scatter", load().hsa_qkv_scatter(_ptr(a), _ptr(active_idx), int(bool(gather)), _ptr(w_qkv),
+                                                     _ptr(q_out), _ptr(k_cache), _ptr(v_cache), n_active, N, D,
                                                      _dt(a), _stream(stream)))
 
 
