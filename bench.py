@@ -15,7 +15,9 @@ stream), also at other active fractions and at the 14B-shaped layer, the full
 T = 40 sampling loop from fresh latents (also under other schedules and
 against dense sampling), iteration time
 against the active fraction, the Euler pass on a working set past the
-Infinity Cache, the iteration with the Wan-style block features on (and with
+Infinity Cache, one block's stages (gathered QKV + scatter, attention,
+out-projection) at four active fractions and two active-set patterns, the
+iteration with the Wan-style block features on (and with
 cross-attention and guidance batch 2), attainable peaks (an MFMA-only probe
 kernel and a 256 MiB device copy) and the CPU oracle on a bounded sample.
 
@@ -61,6 +63,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-features", action="store_true",
                    help="skip the iteration with the Wan-style block features switched on")
+    p.add_argument("--no-stages", action="store_true",
+                   help="skip the per-stage timing of one block at four active fractions")
     p.add_argument("--wan14b", action="store_true",
                    help="also time the whole 14B-shaped iteration (40 blocks, N=75600; ~155 GB of HBM)")
     p.add_argument("--no-scaling", action="store_true", help="skip the iteration-time vs active-fraction sweep")
@@ -453,6 +457,61 @@ def wan_features(H, model, state, c, sigma, plain_ms: float, steps: int = 5, rep
     return out
 
 
+def _event_time(fn, reps: int, warmup: int = 2) -> float:
+    """Mean seconds per call of fn() under HIP events on the current stream."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / 1e3 / reps
+
+
+def stage_bench(H, model, c, reps: int = 10):
+    """One Wan-1.3B-shaped block's stages (the single-block workload: D 1536,
+    12 x 128 heads, N = 32760 cached rows) at |A| in {32760, 16380, 8190,
+    2048}, active rows uniform random or contiguous spatial blobs: QKV with
+    the K/V scatter reading the active rows straight from the [N][D]
+    per-token LayerNorm output (gather mode) and from a compact copy,
+    attention over all N cached rows, out-projection with the residual add.
+    Layer 0's weights, fresh caches; HIP events, mean over reps."""
+    b = model.blocks[0]
+    N, D = c.N, c.D
+    bf = torch.bfloat16
+    hidden = torch.randn(N, D, device="cuda").to(bf)
+    kc = torch.randn(N, D, device="cuda").to(bf)
+    vc = torch.randn(N, D, device="cuda").to(bf)
+    rows = []
+    for nA in (32760, 16380, 8190, 2048):
+        for pattern in ("random", "blob"):
+            idx_np = synth.active_random(c, nA) if pattern == "random" else synth.active_blob(c, nA)
+            idx = torch.from_numpy(idx_np).to("cuda")
+            q = torch.empty(nA, D, dtype=bf, device="cuda")
+            o = torch.empty(nA, D, dtype=bf, device="cuda")
+            hres = torch.zeros(nA, D, device="cuda")
+            compact = hidden[idx.long()].contiguous()
+            ws = torch.empty(max(1, H.hsa_attn_workspace_size(nA, N, c.H, c.Dh)), dtype=torch.uint8,
+                             device="cuda")
+            t_g = _event_time(lambda: H.hsa_qkv_scatter(hidden, idx, nA, b["w_qkv"], q, kc, vc, gather=True), reps)
+            t_c = _event_time(lambda: H.hsa_qkv_scatter(compact, idx, nA, b["w_qkv"], q, kc, vc), reps)
+            t_a = _event_time(lambda: H.hsa_attn_active(q, kc, vc, o, c.H, c.Dh, ws=ws), reps)
+            t_o = _event_time(lambda: H.hsa_linear_residual(o, b["w_o"], hres), reps)
+            qkv_f, attn_f, out_f = 2.0 * nA * D * 3 * D, 4.0 * nA * N * D, 2.0 * nA * D * D
+            rows.append({"n_active": nA, "pattern": pattern,
+                         "qkv_scatter_gather_us": round(t_g * 1e6, 1),
+                         "qkv_scatter_gather_tflops": round(qkv_f / t_g / 1e12, 1),
+                         "qkv_scatter_compact_us": round(t_c * 1e6, 1),
+                         "attention_us": round(t_a * 1e6, 1), "attention_tflops": round(attn_f / t_a / 1e12, 1),
+                         "out_proj_us": round(t_o * 1e6, 1), "out_proj_tflops": round(out_f / t_o / 1e12, 1)})
+    del hidden, kc, vc
+    torch.cuda.empty_cache()
+    return rows
+
+
 def wan14b_iteration(H, steps: int = 2):
     """The whole 14B-shaped iteration (opt-in, --wan14b): 40 blocks, N = 75600
     (21 x 45 x 80), D 5120, 40 x 128 heads, F 13824, 512-token cross-attention,
@@ -509,7 +568,35 @@ def cpu_baseline(c, rows: int):
             "sample": f"1 block with {rows} of {n_active} active rows over N={cs.N} cached rows "
                       f"({t_block:.2f} s), scaled x{n_active / rows:.1f} rows x {c.L} blocks, "
                       f"+ select/active-set/Euler over all N ({t_tail:.2f} s); projected "
-                      f"{t_iter:.1f} s per iteration"}
+                      f"{t_iter:.1f} s per iteration",
+            "dit_lite_full_run": oracle_dit_lite_run()}
+
+
+def oracle_dit_lite_run():
+    """The oracle's whole 8-iteration float32 DiT-lite run (N = 256 on the 4x8x8
+    grid, budgets {8, 4}, regrouping from i = 3 on), with the BLAS thread pool
+    as it is and with one thread."""
+    from oracle import hsa_oracle as O
+    c = synth.CONFIGS[1]
+    dims = O.Dims(N=c.N, C=c.C, D=c.D, H=c.H, Dh=c.Dh, F=c.F, L=c.L, bf16=False)
+    om = O.make_model(dims, synth.io_weights(c), [synth.block_weights(c, l) for l in range(c.L)])
+    sched = O.Schedule(c.T, list(c.budgets), c.counts(), regroup=c.regroup)
+    sigma = synth.sigma_schedule(c.T)
+
+    def run():
+        st = O.init_state(dims, synth.x0(c), synth.group0(c))
+        t0 = time.perf_counter()
+        O.sample(om, sched, st, sigma)
+        return time.perf_counter() - t0
+
+    out = {"iterations": c.T, "s": round(run(), 4)}
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            out["s_single_thread"] = round(run(), 4)
+    except Exception:  # pragma: no cover
+        pass
+    return out
 
 
 def main():
@@ -581,6 +668,8 @@ def main():
                 out["euler_hbm"]["gbs"] / out["attainable"]["copy_gbs"], 4)
     if not args.no_scaling:
         out["scaling_with_active_fraction"] = step_scaling(H, model, state, c, sigma)
+    if not args.no_stages:
+        out["stage_bench"] = stage_bench(H, model, c)
     if not args.no_features:
         out["wan_features"] = wan_features(H, model, state, c, sigma, ms)
         if "attainable" in out:
