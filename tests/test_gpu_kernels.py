@@ -383,11 +383,14 @@ def _attn_case(nA, nkv, Hh, Dh, dtype, tol, seed=0):
     return err
 
 
+@pytest.mark.parametrize("Dh", [128, 64])
 @pytest.mark.parametrize("nA,nkv", [(1, 1), (37, 63), (128, 64), (129, 65), (300, 1000), (64, 4097),
                                     (2, 20000), (700, 5000)])
-def test_attention_bf16_d128(nA, nkv):
-    say(f"attention bf16 nA={nA} nkv={nkv}")
-    err = _attn_case(nA, nkv, 2, 128, torch.bfloat16, TOL_BF16)
+def test_attention_bf16(nA, nkv, Dh):
+    """The MFMA path at both head widths: ragged query and key counts, tails
+    of one key, KV splits (long key ranges, few queries)."""
+    say(f"attention bf16 Dh={Dh} nA={nA} nkv={nkv}")
+    err = _attn_case(nA, nkv, 2 if Dh == 128 else 3, Dh, torch.bfloat16, TOL_BF16)
     assert err < 1e-2
 
 
@@ -396,13 +399,10 @@ def test_attention_f32(nA, nkv, Dh):
     _attn_case(nA, nkv, 2, Dh, torch.float32, 1e-5)
 
 
-def test_attention_bf16_d64_plain():
-    _attn_case(99, 500, 2, 64, torch.bfloat16, TOL_BF16)
-
-
-def test_attention_closed_forms_bf16():
+@pytest.mark.parametrize("Dh", [128, 64])
+def test_attention_closed_forms_bf16(Dh):
     # q = 0 -> mean of V rows; all V rows equal -> that row
-    nkv, Hh, Dh = 3000, 2, 128
+    nkv, Hh = 3000, 2
     rs = np.random.default_rng(9)
     k = bf(rs.standard_normal((nkv, Hh * Dh)))
     v = bf(rs.standard_normal((nkv, Hh * Dh)))
@@ -443,14 +443,15 @@ def _softmax_range_case(pattern, nA, nkv, Hh=2, Dh=128, seed=5):
     return bf(q), bf(k), bf(v)
 
 
+@pytest.mark.parametrize("Dh", [128, 64])
 @pytest.mark.parametrize("pattern", ["spike", "ramp", "negative"])
 @pytest.mark.parametrize("nA,nkv", [(70, 5000), (300, 2113), (1, 9000)])
-def test_attention_softmax_reference_moves(pattern, nA, nkv):
+def test_attention_softmax_reference_moves(pattern, nA, nkv, Dh):
     """The running max is taken from the first keys and raised only when a
     later tile's probabilities grow far above 1: spikes, ramps and uniformly
     very negative scores against the oracle (several KV splits included)."""
-    say(f"attention softmax range {pattern} nA={nA} nkv={nkv}")
-    Hh, Dh = 2, 128
+    say(f"attention softmax range Dh={Dh} {pattern} nA={nA} nkv={nkv}")
+    Hh = 2
     q, k, v = _softmax_range_case(pattern, nA, nkv, Hh, Dh)
     o = torch.empty(nA, Hh * Dh, dtype=torch.bfloat16, device=DEV)
     H.hsa_attn_active(dev(q, torch.bfloat16), dev(k, torch.bfloat16), dev(v, torch.bfloat16), o, Hh, Dh)
@@ -468,6 +469,25 @@ def test_attention_full_size_sampled_rows(frac):
     say(f"attention full-size nA={nA}")
     kc, vc = synth.kv_cache(c)
     rs = np.random.default_rng(77)
+    q = bf(rs.standard_normal((nA, c.D)))
+    o = torch.empty(nA, c.D, dtype=torch.bfloat16, device=DEV)
+    H.hsa_attn_active(dev(q, torch.bfloat16), dev(kc, torch.bfloat16), dev(vc, torch.bfloat16), o,
+                      c.H, c.Dh)
+    rows = np.sort(rs.choice(nA, 64, replace=False))
+    ref = O.attention(q[rows], kc, vc, c.H, c.Dh)
+    assert rel_l2(host(o)[rows], ref) < TOL_BF16
+
+
+@pytest.mark.parametrize("frac", [0.25, 0.0625])
+def test_attention_full_size_64_wide_heads(frac):
+    """64-wide heads at the full token count: N = 32760 cached rows, 32 heads x
+    64 (D = 2048, the head layout of LTX-style DiTs); 64 sampled query rows
+    against the oracle."""
+    c = synth.CONFIGS[2].with_(D=2048, H=32, Dh=64)
+    nA = synth.n_active_for_fraction(c.N, frac)
+    say(f"attention full-size Dh=64 nA={nA}")
+    kc, vc = synth.kv_cache(c)
+    rs = np.random.default_rng(78)
     q = bf(rs.standard_normal((nA, c.D)))
     o = torch.empty(nA, c.D, dtype=torch.bfloat16, device=DEV)
     H.hsa_attn_active(dev(q, torch.bfloat16), dev(kc, torch.bfloat16), dev(vc, torch.bfloat16), o,

@@ -69,10 +69,10 @@ def small_bf16(**kw):
 
 # ---------------------------------------------------------------- one block
 
-@pytest.mark.parametrize("n_text", [0, 16])
-def test_block_forward_small_bf16(n_text):
-    c = small_bf16(L=1, n_text=n_text, text_dim=64 if n_text else 0)
-    say(f"block_forward small bf16 n_text={n_text}")
+@pytest.mark.parametrize("n_text,Dh", [(0, 128), (16, 128), (0, 64), (16, 64)])
+def test_block_forward_small_bf16(n_text, Dh):
+    c = small_bf16(L=1, n_text=n_text, text_dim=64 if n_text else 0, H=256 // Dh, Dh=Dh)
+    say(f"block_forward small bf16 n_text={n_text} Dh={Dh}")
     om = oracle_model(c)
     kc, vc = synth.kv_cache(c)
     rs = np.random.default_rng(1)

@@ -365,7 +365,7 @@ hsa_status hsa_attn_active(const void* q, const void* k, const void* v, void* o,
   CHECK_PTR(o);
   if (!(scale > 0.f) || !isfinite(scale)) return HSA_ERR_ARG;
   const size_t need = attn_workspace_bytes(n_active, n_kv, H, Dh);
-  if (dtype == HSA_BF16 && Dh == 128 && need > 0) {
+  if (dtype == HSA_BF16 && need > 0) {
     if (!ws || ws_bytes < need) return HSA_ERR_WORKSPACE;
     if (!aligned16(ws)) return HSA_ERR_ALIGN;
   }

@@ -3,14 +3,16 @@
 // rows of active tokens and stale rows of skipped ones), so the work is
 // O(|A_i| * N) instead of O(N^2).  No mask.
 //
-// bf16, Dh = 128: flash-style online softmax on v_mfma_f32_32x32x16_bf16.
+// bf16, Dh = 128 or 64: flash-style online softmax on
+// v_mfma_f32_32x32x16_bf16 (one kernel body, templated on the head width).
 //  * One workgroup = one head x 256 queries (8 wavefronts x 32, two per SIMD
 //    so one wave's softmax overlaps the other's MFMAs).  It streams the
-//    head's K/V in tiles of 64 rows through a 4-stage LDS ring.
+//    head's K/V in tiles of 64 rows through a 4-stage LDS ring (128 KiB at
+//    Dh = 128, 64 KiB at Dh = 64).
 //  * Tiles move HBM -> LDS with buffer_load ... lds (no register staging, no
 //    per-load VALU work; rows past the end read as zero).  Each 16-byte chunk
 //    lands at an XOR-swizzled position of its 256-byte row, so the operand
-//    reads below hit distinct banks.
+//    reads below hit distinct banks (256-byte rows at Dh = 128, 128-byte at 64).
 //  * Each wavefront computes S^T = K Q^T (keys as MFMA rows, its 32 queries
 //    as columns): a lane holds one query's scores, so the row max and row
 //    sum are in-lane except one exchange between the lane halves
@@ -22,9 +24,9 @@
 //    16-dim block and gives lane i dim i of those 4 keys.
 //  * Inside each wavefront the loop is software-pipelined over 32-key
 //    sub-tiles (two per LDS tile): one step issues the S^T MFMAs of sub-tile
-//    u+1 and the PV MFMAs of sub-tile u-1 alternately, with the softmax of
-//    sub-tile u spread between them, so the MFMA unit always has independent
-//    work while the VALU turns scores into probabilities.  One 32x32 score
+//    u+1 and the PV MFMAs of sub-tile u-1 alternately (Dh/16 of each), with
+//    the softmax of sub-tile u spread between them, so the MFMA unit always
+//    has independent work while the VALU turns scores into probabilities.  One 32x32 score
 //    block per sub-tile keeps the live registers within the 256 a wave may
 //    hold at two waves per SIMD.
 //  * Softmax in log2 units with little VALU work per score: Q is pre-scaled
@@ -42,7 +44,7 @@
 //  * Workgroup ids are remapped so each XCD runs a contiguous range of
 //    (split, head, query tile): the workgroups sharing an XCD's L2 stream
 //    the same head's K/V at the same time.
-// Other head sizes / float32: a plain LDS-tiled kernel (float32 arithmetic).
+// float32: a plain LDS-tiled kernel (float32 arithmetic).
 #include "common.h"
 
 namespace hsa {
@@ -54,14 +56,23 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int NW = 8;                      // wavefronts per workgroup
 constexpr int kAttnThreads = NW * 64;
-constexpr int DH = 128;
 constexpr int BKV = 64;                    // keys per tile (LDS stage)
 constexpr int SUB = 32;                    // keys per sub-tile (one S^T MFMA block)
 constexpr int BQ = NW * 32;                // queries per workgroup
 constexpr int NST = 4;                     // LDS stages
-constexpr int ROWB = DH * 2;               // bytes per K/V row of one head (256)
-constexpr int TILEB = BKV * ROWB;          // 16 KiB per K or V tile
-constexpr int LOADS = TILEB / 16 / kAttnThreads;   // 16-byte loads per lane per tile and operand (2)
+
+// Head-width constants of the MFMA path (Dh = 128 or 64).
+template <int DH_>
+struct AttnShape {
+  static constexpr int DH = DH_;
+  static constexpr int ROWB = DH * 2;                        // bytes per K/V row of one head
+  static constexpr int TILEB = BKV * ROWB;                   // bytes per K or V tile
+  static constexpr int LOADS = TILEB / 16 / kAttnThreads;    // 16-byte loads per lane per tile
+  static constexpr int NS = DH / 16;      // S^T MFMAs per sub-tile (16 dims each) = PV MFMAs
+  static constexpr int NDB = DH / 32;     // 32-dim blocks of O^T
+  static constexpr int EPS = 16 / NS;     // score elements a lane exponentiates per MFMA pair
+  static_assert(LOADS * 16 * kAttnThreads == TILEB, "tile load split");
+};
 // Largest row-sum partial (32 probabilities of one query in one lane) a tile may
 // reach before the running max is raised: it bounds every probability by 2^32.
 constexpr float kRaiseSum = 4294967296.0f;
@@ -74,9 +85,23 @@ __device__ __forceinline__ int32_t xcd_remap(int32_t bid, int32_t total) {
   return (bid % kXcd) * per + bid / kXcd;
 }
 
-// Position of 16-byte chunk c (0..15) within row r of a K / V tile in LDS.
-__device__ __forceinline__ int k_pos(int r, int c) { return c ^ (r & 15); }
-__device__ __forceinline__ int v_pos(int r, int c) { return c ^ ((r & 3) << 2); }
+// Position of 16-byte chunk c within row r of a K / V tile in LDS (XOR
+// swizzles, involutions in c).  Dh = 128 (16 chunks, 256-byte rows): K reads
+// of 16 consecutive rows at one chunk, and the transposing V reads, hit
+// distinct banks.  Dh = 64 (8 chunks, 128-byte rows): the K swizzle spreads 8
+// or 16 consecutive rows at one chunk over distinct banks; the V swizzle swaps
+// the halves of rows 2, 3 (mod 4) so the 4-key x 32-dim blocks of a
+// transposing read cover all 64 banks.
+template <int DH>
+__device__ __forceinline__ int k_pos(int r, int c) {
+  if constexpr (DH == 128) return c ^ (r & 15);
+  else return c ^ (((r >> 1) ^ (r << 2)) & 7);
+}
+template <int DH>
+__device__ __forceinline__ int v_pos(int r, int c) {
+  if constexpr (DH == 128) return c ^ ((r & 3) << 2);
+  else return c ^ (((r >> 1) & 1) << 2);
+}
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
@@ -103,12 +128,14 @@ __device__ __forceinline__ void dma16(uint32_t lds_addr, uint32_t voff, i32x4 rs
 #pragma clang diagnostic pop
 
 // Issue the loads of one K and one V tile (rows row0.. of head h) into LDS.
+template <int DH>
 __device__ __forceinline__ void issue_tile(const bf16* k, const bf16* v, int32_t row0, int32_t nkv,
                                            int32_t ldk, int32_t h, uint32_t sk, uint32_t sv,
                                            const uint32_t* voff_k, const uint32_t* voff_v,
                                            int wave) {
   const int32_t rows_left = nkv - row0;
   const uint32_t nbytes = rows_left > 0 ? (uint32_t)rows_left * (uint32_t)ldk * 2u : 0u;
+  constexpr int LOADS = AttnShape<DH>::LOADS;
   const size_t off = ((size_t)row0 * ldk + (size_t)h * DH) * 2;
   const i32x4 rk = buffer_rsrc(reinterpret_cast<const char*>(k) + off, nbytes);
   const i32x4 rv = buffer_rsrc(reinterpret_cast<const char*>(v) + off, nbytes);
@@ -124,16 +151,20 @@ __device__ __forceinline__ void issue_tile(const bf16* k, const bf16* v, int32_t
 // Wait until at most OUT tiles' loads of this wave are in flight, then
 // synchronise the workgroup.  No memory fence: the only LDS writes are the
 // tile loads, whose completion vmcnt reports.
-template <int OUT>
+template <int DH, int OUT>
 __device__ __forceinline__ void wait_tiles_barrier() {
-  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"(OUT * 2 * LOADS) : "memory");
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"(OUT * 2 * AttnShape<DH>::LOADS) : "memory");
 }
 
-__global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_d128_kernel(
+template <int DH_>
+__device__ __forceinline__ void attn_bf16_body(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     bf16* __restrict__ o, bf16* __restrict__ part_o, float* __restrict__ part_ml, int32_t nA,
-    int32_t nkv, int32_t H, float c, int32_t n_qt, int32_t splits, int32_t tiles_per_split) {
-  __shared__ __attribute__((aligned(1024))) char smem[2 * NST * TILEB];
+    int32_t nkv, int32_t H, float c, int32_t n_qt, int32_t splits, int32_t tiles_per_split,
+    char* smem) {
+  typedef AttnShape<DH_> S;
+  constexpr int DH = S::DH, ROWB = S::ROWB, TILEB = S::TILEB, LOADS = S::LOADS;
+  constexpr int NS = S::NS, NDB = S::NDB, EPS = S::EPS;
   const char* const sK = smem;
   const char* const sV = smem + NST * TILEB;
   const uint32_t sK_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
@@ -161,9 +192,9 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_d128_kernel(
 #pragma unroll
   for (int j = 0; j < LOADS; ++j) {
     const int s = (j * NW + wave) * 64 + lane;   // 16-byte slot in the tile
-    const int r = s >> 4, p = s & 15;
-    voff_k[j] = (uint32_t)(r * D * 2 + k_pos(r, p) * 16);   // k_pos is an involution
-    voff_v[j] = (uint32_t)(r * D * 2 + v_pos(r, p) * 16);
+    const int r = s / (ROWB / 16), p = s % (ROWB / 16);   // row, chunk
+    voff_k[j] = (uint32_t)(r * D * 2 + k_pos<DH>(r, p) * 16);   // k_pos is an involution
+    voff_v[j] = (uint32_t)(r * D * 2 + v_pos<DH>(r, p) * 16);
   }
 
   // ---- Q^T fragments (B operand): lane = query column, 8 consecutive dims
@@ -185,7 +216,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_d128_kernel(
   // K (A operand of S^T): row kb*32 + l32, chunk 2*dk + half
   uint32_t koff[DH / 16];
 #pragma unroll
-  for (int dk = 0; dk < DH / 16; ++dk) koff[dk] = (uint32_t)(l32 * ROWB + k_pos(l32, 2 * dk + half) * 16);
+  for (int dk = 0; dk < DH / 16; ++dk) koff[dk] = (uint32_t)(l32 * ROWB + k_pos<DH>(l32, 2 * dk + half) * 16);
   // V (transposing reads): 16-lane group g points at keys kbase + i/4, dims d0 + 4*(i%4)
   const int grp = lane >> 4, gi = lane & 15;
   const int vrow = 4 * (grp >> 1) + (gi >> 2);   // key within a 8-key step (plus 16*jp + 8*second + 32*kb)
@@ -193,7 +224,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_d128_kernel(
 #pragma unroll
   for (int db = 0; db < DH / 32; ++db) {
     const int chunk = 4 * db + 2 * (grp & 1) + ((gi & 3) >> 1);
-    voffr[db] = (uint32_t)(vrow * ROWB + v_pos(vrow, chunk) * 16 + 8 * (gi & 1));
+    voffr[db] = (uint32_t)(vrow * ROWB + v_pos<DH>(vrow, chunk) * 16 + 8 * (gi & 1));
   }
 
   f32x16 acc_o[DH / 32];
@@ -270,8 +301,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_d128_kernel(
     return l2[0] + l2[1];
   };
   // O^T += V^T P^T over the sub-tile: k-step jp covers keys 16*jp + 4*half + {0..3, 8..11}
-  auto vfrag = [&](const char* vt, int j) {   // j: k-step jp = j/4, dims block db = j%4
-    const int jp = j >> 2, db = j & 3;
+  auto vfrag = [&](const char* vt, int j) {   // j: k-step jp = j/NDB, dims block db = j%NDB
+    const int jp = j / NDB, db = j % NDB;
     const char* vk = vt + 16 * jp * ROWB;
     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vk + voffr[db]));
     const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vk + 8 * ROWB + voffr[db]));
@@ -283,10 +314,10 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_d128_kernel(
     bf16x8 vf[2];
     vf[0] = vfrag(vt, 0);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (j + 1 < 8) vf[(j + 1) & 1] = vfrag(vt, j + 1);
-      acc_o[j & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[j & 1], __builtin_bit_cast(bf16x8, pw[j >> 2]),
-                                                             acc_o[j & 3], 0, 0, 0);
+    for (int j = 0; j < NS; ++j) {
+      if (j + 1 < NS) vf[(j + 1) & 1] = vfrag(vt, j + 1);
+      acc_o[j % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          vf[j & 1], __builtin_bit_cast(bf16x8, pw[j / NDB]), acc_o[j % NDB], 0, 0, 0);
     }
   };
   // LDS addresses of sub-tile u's K and V rows
@@ -299,7 +330,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_d128_kernel(
 #pragma unroll
   for (int st = 0; st < NST - 1; ++st)
     if (st < ntiles)
-      issue_tile(k, v, kv_begin + st * BKV, nkv, D, h, sK_lds + st * TILEB, sV_lds + st * TILEB,
+      issue_tile<DH>(k, v, kv_begin + st * BKV, nkv, D, h, sK_lds + st * TILEB, sV_lds + st * TILEB,
                  voff_k, voff_v, wave);
 
   // Software pipeline inside each wavefront over 32-key sub-tiles: step u
@@ -314,11 +345,11 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_d128_kernel(
                   bool pv) {
     if (u & 1) {
       const int it = u >> 1;   // stage of sub-tile u; sub-tile u+1 opens stage it+1
-      if (it + 2 < ntiles) wait_tiles_barrier<1>();
-      else wait_tiles_barrier<0>();
+      if (it + 2 < ntiles) wait_tiles_barrier<DH, 1>();
+      else wait_tiles_barrier<DH, 0>();
       if (it + NST - 1 < ntiles) {
         const int ns = (it + NST - 1) % NST;
-        issue_tile(k, v, kv_begin + (it + NST - 1) * BKV, nkv, D, h, sK_lds + ns * TILEB,
+        issue_tile<DH>(k, v, kv_begin + (it + NST - 1) * BKV, nkv, D, h, sK_lds + ns * TILEB,
                    sV_lds + ns * TILEB, voff_k, voff_v, wave);
       }
     }
@@ -328,26 +359,29 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_d128_kernel(
     kf[0] = kfrag(kt, 0);
     if (pv) vf[0] = vfrag(vt, 0);
     float l2[2] = {0.f, 0.f};
-    float p_even = 0.f;
+    // slot j: S^T MFMA j of sub-tile u+1, the first EPS/2 exponentials of the
+    // slot's score elements of sub-tile u, PV MFMA j of sub-tile u-1, the rest
+    // of them with their bf16 packing and the row-sum adds
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (j + 1 < 8) kf[(j + 1) & 1] = kfrag(kt, j + 1);
+    for (int j = 0; j < NS; ++j) {
+      if (j + 1 < NS) kf[(j + 1) & 1] = kfrag(kt, j + 1);
       s_nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[j & 1], qf[j], j == 0 ? negm : s_nxt, 0, 0, 0);
-      {
-        const int r = 2 * j;   // score element r of sub-tile u
-        p_even = __builtin_amdgcn_exp2f(s_cur[r]);
-      }
+      float p[EPS];
+#pragma unroll
+      for (int e = 0; e < EPS / 2; ++e) p[e] = __builtin_amdgcn_exp2f(s_cur[EPS * j + e]);
       if (pv) {
-        if (j + 1 < 8) vf[(j + 1) & 1] = vfrag(vt, j + 1);
-        acc_o[j & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[j & 1], __builtin_bit_cast(bf16x8, pw_prev[j >> 2]),
-                                                               acc_o[j & 3], 0, 0, 0);
+        if (j + 1 < NS) vf[(j + 1) & 1] = vfrag(vt, j + 1);
+        acc_o[j % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            vf[j & 1], __builtin_bit_cast(bf16x8, pw_prev[j / NDB]), acc_o[j % NDB], 0, 0, 0);
       }
-      {
-        const int r = 2 * j + 1;
-        const float p_odd = __builtin_amdgcn_exp2f(s_cur[r]);
-        const bf16x2 pr = {(bf16)p_even, (bf16)p_odd};
-        pw_cur[r >> 3][(r & 7) >> 1] = __builtin_bit_cast(uint32_t, pr);
-        l2[j & 1] += p_even + p_odd;
+#pragma unroll
+      for (int e = EPS / 2; e < EPS; ++e) p[e] = __builtin_amdgcn_exp2f(s_cur[EPS * j + e]);
+#pragma unroll
+      for (int pr = 0; pr < EPS / 2; ++pr) {
+        const int r = EPS * j + 2 * pr;   // score elements r, r+1 of sub-tile u
+        const bf16x2 pk = {(bf16)p[2 * pr], (bf16)p[2 * pr + 1]};
+        pw_cur[r >> 3][(r & 7) >> 1] = __builtin_bit_cast(uint32_t, pk);
+        l2[(j * (EPS / 2) + pr) & 1] += p[2 * pr] + p[2 * pr + 1];
       }
     }
     float lt = l2[0] + l2[1];
@@ -360,9 +394,9 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_d128_kernel(
 
   f32x16 sa, sb;
   u32x4 pwa[2], pwb[2];   // P^T fragments (packed bf16 pairs) of two consecutive sub-tiles
-  if (min(NST - 2, ntiles - 1) >= 2) wait_tiles_barrier<2>();
-  else if (ntiles - 1 >= 1) wait_tiles_barrier<1>();
-  else wait_tiles_barrier<0>();
+  if (min(NST - 2, ntiles - 1) >= 2) wait_tiles_barrier<DH, 2>();
+  else if (ntiles - 1 >= 1) wait_tiles_barrier<DH, 1>();
+  else wait_tiles_barrier<DH, 0>();
   // first sub-tile: unshifted scores, whose max is the initial reference
   {
     const char* kt = k_sub(0);
@@ -434,6 +468,22 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_d128_kernel(
     part_ml[prow * 2 + 1] = l_tot;
   }
 }
+
+#define HSA_ATTN_ARGS                                                                        \
+  const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,        \
+      bf16 *__restrict__ o, bf16 *__restrict__ part_o, float *__restrict__ part_ml, int32_t nA, \
+      int32_t nkv, int32_t H, float c, int32_t n_qt, int32_t splits, int32_t tiles_per_split
+
+__global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_d128_kernel(HSA_ATTN_ARGS) {
+  __shared__ __attribute__((aligned(1024))) char smem[2 * NST * AttnShape<128>::TILEB];
+  attn_bf16_body<128>(q, k, v, o, part_o, part_ml, nA, nkv, H, c, n_qt, splits, tiles_per_split, smem);
+}
+
+__global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_d64_kernel(HSA_ATTN_ARGS) {
+  __shared__ __attribute__((aligned(1024))) char smem[2 * NST * AttnShape<64>::TILEB];
+  attn_bf16_body<64>(q, k, v, o, part_o, part_ml, nA, nkv, H, c, n_qt, splits, tiles_per_split, smem);
+}
+#undef HSA_ATTN_ARGS
 
 // Merge split partials in split order: with weights w_s = l_s 2^(m_s - M),
 // O = sum_s w_s (O_s / l_s) / sum_s w_s.
@@ -552,7 +602,7 @@ SplitPlan plan_split(int32_t nA, int32_t nkv, int32_t H) {
   return p;
 }
 
-bool use_mfma_path(int32_t Dh, hsa_dtype dt) { return dt == HSA_BF16 && Dh == 128; }
+bool use_mfma_path(int32_t Dh, hsa_dtype dt) { return dt == HSA_BF16 && (Dh == 128 || Dh == 64); }
 
 }  // namespace
 
@@ -580,23 +630,27 @@ hsa_status launch_attention(const void* q, const void* k, const void* v, void* o
       part_ml = (float*)((char*)ws + align_up(rows * Dh * sizeof(bf16), 256));
     }
     const int32_t total = p.n_qt * H * p.splits;
-    attn_bf16_d128_kernel<<<total, kAttnThreads, 0, s>>>(
-        (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, part_o, part_ml, n_active, n_kv,
-        H, scale * kLog2e, p.n_qt, p.splits, p.tiles_per_split);
+    if (Dh == 128)
+      attn_bf16_d128_kernel<<<total, kAttnThreads, 0, s>>>(
+          (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, part_o, part_ml, n_active,
+          n_kv, H, scale * kLog2e, p.n_qt, p.splits, p.tiles_per_split);
+    else
+      attn_bf16_d64_kernel<<<total, kAttnThreads, 0, s>>>(
+          (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, part_o, part_ml, n_active,
+          n_kv, H, scale * kLog2e, p.n_qt, p.splits, p.tiles_per_split);
     if (p.splits > 1) {
-      const int64_t threads = (int64_t)n_active * H * (DH / 4);
-      attn_merge_kernel<DH><<<(unsigned)((threads + 255) / 256), 256, 0, s>>>(
-          part_o, part_ml, (bf16*)o, n_active, H, p.splits);
+      const int64_t threads = (int64_t)n_active * H * (Dh / 4);
+      const unsigned blocks = (unsigned)((threads + 255) / 256);
+      if (Dh == 128)
+        attn_merge_kernel<128><<<blocks, 256, 0, s>>>(part_o, part_ml, (bf16*)o, n_active, H, p.splits);
+      else
+        attn_merge_kernel<64><<<blocks, 256, 0, s>>>(part_o, part_ml, (bf16*)o, n_active, H, p.splits);
     }
     return launch_status();
   }
   dim3 grid(cdiv(n_active, 64), H);
   if (dt == HSA_BF16) {
-    if (Dh == 64)
-      attn_plain_kernel<bf16, 64><<<grid, 256, 0, s>>>((const bf16*)q, (const bf16*)k, (const bf16*)v,
-                                                       (bf16*)o, n_active, n_kv, H, scale);
-    else
-      return HSA_ERR_SHAPE;
+    return HSA_ERR_SHAPE;   // bf16 takes the MFMA path for every supported head width
   } else {
     if (Dh == 64)
       attn_plain_kernel<float, 64><<<grid, 256, 0, s>>>((const float*)q, (const float*)k,
