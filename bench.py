@@ -261,8 +261,9 @@ def time_attention(H, model, c, n_active, reps, warmup: int = 10):
 
 def attention_sweep(H, model, c, fracs=(1.0, 0.5, 0.25, 0.125, 0.0625, 0.05), reps: int = 10):
     """Attention alone at other active fractions of the same stack (K/V of the
-    stack's layers, rotating), and at the 14B-shaped layer: N = 75600 cached
-    rows, |A| = 18900 (25%), 40 heads x 128."""
+    stack's layers, rotating), at the 14B-shaped layer: N = 75600 cached
+    rows, |A| = 18900 (25%), 40 heads x 128, and with 64-wide heads: N =
+    32760, 32 heads x 64, |A| = 8190 and 2048."""
     out = {"N": c.N, "heads": c.H, "frac": list(fracs), "n_active": [], "tflops": []}
     for f in fracs:
         nA = synth.n_active_for_fraction(c.N, f)
@@ -292,6 +293,21 @@ def attention_sweep(H, model, c, fracs=(1.0, 0.5, 0.25, 0.125, 0.0625, 0.05), re
     out["wan14b_shape"] = {"N": c4.N, "n_active": nA, "heads": c4.H, "head_dim": c4.Dh,
                            "ms": round(t * 1e3, 2), "tflops": round(4.0 * nA * c4.N * c4.D / t / 1e12, 1)}
     del kc, vc, q, o, ws
+    # 64-wide heads (the LTX-style head layout): N = 32760, 32 x 64, 25% and 1/16 active
+    Hh, Dh = 32, 64
+    D = Hh * Dh
+    kc = torch.randn((c.N, D), generator=g, device="cuda").to(torch.bfloat16)
+    vc = torch.randn((c.N, D), generator=g, device="cuda").to(torch.bfloat16)
+    rows = []
+    for nA in (8190, 2048):
+        q = torch.randn((nA, D), generator=g, device="cuda").to(torch.bfloat16)
+        o = torch.empty_like(q)
+        ws = torch.empty(max(1, H.hsa_attn_workspace_size(nA, c.N, Hh, Dh)), dtype=torch.uint8,
+                         device="cuda")
+        t = _event_time(lambda: H.hsa_attn_active(q, kc, vc, o, Hh, Dh, ws=ws), 5)
+        rows.append({"n_active": nA, "ms": round(t * 1e3, 3), "tflops": round(4.0 * nA * c.N * D / t / 1e12, 1)})
+    out["heads_64_wide"] = {"N": c.N, "heads": Hh, "head_dim": Dh, "runs": rows}
+    del kc, vc
     return out
 
 
