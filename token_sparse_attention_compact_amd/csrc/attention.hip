@@ -486,7 +486,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_d64_kernel(HSA_ATTN
 #undef HSA_ATTN_ARGS
 
 // Merge split partials in split order: with weights w_s = l_s 2^(m_s - M),
-// O = sum_s w_s (O_s / l_s) / sum_s w_s.
+// O = sum_s w_s (O_s / l_s) / sum_s w_s.  One thread per 8 dims of a
+// (query, head) row: 16-byte partial reads and output writes.
 template <int HD>
 __global__ __launch_bounds__(256) void attn_merge_kernel(const bf16* __restrict__ part_o,
                                                          const float* __restrict__ part_ml,
@@ -494,27 +495,27 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const bf16* __restrict_
                                                          int32_t H, int32_t splits) {
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t rows = (int64_t)nA * H;
-  const int64_t row = t / (HD / 4);
-  const int d4 = (int)(t % (HD / 4)) * 4;
+  const int64_t row = t / (HD / 8);
+  const int d8 = (int)(t % (HD / 8)) * 8;
   if (row >= rows) return;
   const int32_t qi = (int32_t)(row / H), h = (int32_t)(row % H);
   float M = -INFINITY;
   for (int s = 0; s < splits; ++s) M = fmaxf(M, part_ml[((size_t)(s * H + h) * nA + qi) * 2]);
   float L = 0.f;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int s = 0; s < splits; ++s) {
     const size_t pr = (size_t)(s * H + h) * nA + qi;
     const float w = __builtin_amdgcn_exp2f(part_ml[pr * 2] - M) * part_ml[pr * 2 + 1];
     L += w;
-    const bf16x4 po = *reinterpret_cast<const bf16x4*>(part_o + pr * HD + d4);
+    const bf16x8 po = *reinterpret_cast<const bf16x8*>(part_o + pr * HD + d8);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(w, (float)po[e], acc[e]);
+    for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(w, (float)po[e], acc[e]);
   }
   const float inv = 1.0f / L;
-  bf16x4 w4;
+  bf16x8 w8;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) w4[e] = (bf16)(acc[e] * inv);
-  *reinterpret_cast<bf16x4*>(o + (size_t)qi * H * HD + h * HD + d4) = w4;
+  for (int e = 0; e < 8; ++e) w8[e] = (bf16)(acc[e] * inv);
+  *reinterpret_cast<bf16x8*>(o + (size_t)qi * H * HD + h * HD + d8) = w8;
 }
 
 // ---------------------------------------------------------------- plain path
@@ -639,7 +640,7 @@ hsa_status launch_attention(const void* q, const void* k, const void* v, void* o
           (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, part_o, part_ml, n_active,
           n_kv, H, scale * kLog2e, p.n_qt, p.splits, p.tiles_per_split);
     if (p.splits > 1) {
-      const int64_t threads = (int64_t)n_active * H * (Dh / 4);
+      const int64_t threads = (int64_t)n_active * H * (Dh / 8);
       const unsigned blocks = (unsigned)((threads + 255) / 256);
       if (Dh == 128)
         attn_merge_kernel<128><<<blocks, 256, 0, s>>>(part_o, part_ml, (bf16*)o, n_active, H, p.splits);
