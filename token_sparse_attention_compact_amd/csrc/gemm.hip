@@ -4,21 +4,23 @@
 // the QKV projection (with the fresh K/V rows scattered into the per-layer
 // cache, item 2), the attention out-projection, and the MLP.
 //
-// bf16 path: v_mfma_f32_32x32x16_bf16 on 128x128 output tiles, eight
-// wavefronts each owning a 32x64 block as 1x2 MFMA tiles.  K advances in
-// steps of 64 through a 2-stage ring of LDS filled straight from HBM with
-// buffer_load ... lds (no register staging; rows past M or N read as zero),
-// each 16-byte chunk at an XOR-swizzled position of its 128-byte row so the
-// operand reads hit distinct banks.  The next stage's loads are in flight
-// while the current one feeds the MFMAs.  Epilogues are fused (store / GELU /
-// residual add, plain or gated per column / QKV scatter) and work on quads of
-// 4 consecutive output columns: the MFMA computes C^T blocks (w rows as MFMA
-// rows), whose accumulator layout gives each lane runs of 4 consecutive
-// columns of a row.
+// bf16 path: v_mfma_f32_16x16x32_bf16 (or 32x32x16) on 128x128, 128x192 or
+// 256x256 output tiles, eight wavefronts each owning a block of MFMA tiles.
+// K advances in steps of 64 through a 2-stage ring of LDS filled straight
+// from HBM with buffer_load ... lds (no register staging; rows past M or N
+// read as zero), each 16-byte chunk at an XOR-swizzled position of its
+// 128-byte row so the operand reads hit distinct banks.  The next stage's
+// loads are in flight while the current one feeds the MFMAs.  Epilogues are
+// fused (store / GELU / residual add, plain or gated per column / QKV
+// scatter) and work on quads of 4 consecutive output columns: the MFMA
+// computes C^T blocks (w rows as MFMA rows), whose accumulator layout gives
+// each lane runs of 4 consecutive columns of a row.
 //
 // float32 path (small float32 workloads): LDS-tiled FMA GEMM, 64x64 tiles.
 // The QKV projection can read its rows gathered, a[idx[m]], from a larger
 // matrix (the per-token hidden state), on both paths.
+#include <type_traits>
+
 #include "common.h"
 
 namespace hsa {
@@ -150,18 +152,20 @@ __device__ __forceinline__ void wait_barrier() {
 }
 
 // Tile configuration: BM x BN output tile, WM x WN wavefronts (each owning a
-// (BM/WM) x (BN/WN) block of 32x32 MFMA tiles), NST LDS stages of BK=64,
+// (BM/WM) x (BN/WN) block of MI x MI MFMA tiles), NST LDS stages of BK=64,
 // tile groups of GM row blocks by default (the launch may pass another
-// group size), at least MINB workgroups per CU (which caps
-// the registers per lane: 128 at two 512-thread workgroups, 256 at one).
-template <int BM_, int BN_, int WM_, int WN_, int NST_, int GM_, int MINB_ = 2>
+// group size), at least MINB workgroups per CU (which caps the registers per
+// lane: 128 at two 512-thread workgroups, 256 at one), MFMA shape MI:
+// 16 = v_mfma_f32_16x16x32_bf16, 32 = v_mfma_f32_32x32x16_bf16.
+template <int BM_, int BN_, int WM_, int WN_, int NST_, int GM_, int MINB_, int MI_>
 struct GemmCfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, NST = NST_, GM = GM_;
-  static constexpr int MINB = MINB_;
+  static constexpr int MINB = MINB_, MI = MI_;
+  static_assert(MI == 16 || MI == 32, "MFMA shape");
   static constexpr int WAVES = WM * WN;
   static constexpr int THREADS = WAVES * 64;
   static constexpr int TM = BM / WM, TN = BN / WN;        // per-wave block
-  static constexpr int FM = TM / 32, FN = TN / 32;        // MFMA tiles per wave
+  static constexpr int FM = TM / MI, FN = TN / MI;        // MFMA tiles per wave
   static constexpr int TILE_A = BM * ROWB, TILE_B = BN * ROWB;
   static constexpr int STAGE = TILE_A + TILE_B;
   static constexpr int LOADS_A = TILE_A / 16 / THREADS;
@@ -232,19 +236,25 @@ __global__ __launch_bounds__(G::THREADS, G::MINB) void gemm_bf16_kernel(
       dma16(sb + (uint32_t)__builtin_amdgcn_readfirstlane((j * G::WAVES + wave) * 1024), voff_b[j], rb);
   };
 
-  // operand read offsets: row (32-block base) + l32, chunk 2*ks + half
-  const int l32 = lane & 31, half = lane >> 5;
-  uint32_t frag[BK / 16];
+  // Operand read offsets.  An MFMA step takes KSTEP = 512/MI values of k; its
+  // 8-value operand run in a lane is row lr = lane % MI of the MI-row block at
+  // 16-byte chunk (64/MI) * ks + lane / MI of the 128-byte LDS row.
+  constexpr int MI = G::MI, KSTEP = 512 / MI, NKS = BK / KSTEP;
+  const int lr = lane % MI, lc = lane / MI;
+  uint32_t frag[NKS];
 #pragma unroll
-  for (int ks = 0; ks < BK / 16; ++ks) frag[ks] = (uint32_t)(l32 * ROWB + gpos(l32, 2 * ks + half) * 16);
+  for (int ks = 0; ks < NKS; ++ks)
+    frag[ks] = (uint32_t)(lr * ROWB + gpos(lr, (64 / MI) * ks + lc) * 16);
 
-  f32x16 acc[G::FM][G::FN];
+  typedef typename std::conditional<MI == 32, f32x16, f32x4>::type Acc;
+  constexpr int NACC = MI * MI / 64;   // accumulator values per lane
+  Acc acc[G::FM][G::FN];
 #pragma unroll
   for (int i = 0; i < G::FM; ++i)
 #pragma unroll
     for (int j = 0; j < G::FN; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+      for (int r = 0; r < NACC; ++r) acc[i][j][r] = 0.f;
 
   const int nk = K / BK;
 #pragma unroll
@@ -263,34 +273,39 @@ __global__ __launch_bounds__(G::THREADS, G::MINB) void gemm_bf16_kernel(
     const char* a_frag = sa + (wm * G::TM) * ROWB;
     const char* b_frag = sa + G::TILE_A + (wn * G::TN) * ROWB;
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
+    for (int ks = 0; ks < NKS; ++ks) {
       bf16x8 af[G::FM], bfr[G::FN];
 #pragma unroll
       for (int i = 0; i < G::FM; ++i)
-        af[i] = *reinterpret_cast<const bf16x8*>(a_frag + i * 32 * ROWB + frag[ks]);
+        af[i] = *reinterpret_cast<const bf16x8*>(a_frag + i * MI * ROWB + frag[ks]);
 #pragma unroll
       for (int j = 0; j < G::FN; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8*>(b_frag + j * 32 * ROWB + frag[ks]);
+        bfr[j] = *reinterpret_cast<const bf16x8*>(b_frag + j * MI * ROWB + frag[ks]);
 #pragma unroll
       for (int i = 0; i < G::FM; ++i)
 #pragma unroll
-        for (int j = 0; j < G::FN; ++j)   // C^T block: w rows as MFMA rows, a rows as columns
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < G::FN; ++j) {   // C^T block: w rows as MFMA rows, a rows as columns
+          if constexpr (MI == 32)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+          else
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+        }
     }
   }
 
-  // acc[i][j][r] = C[row][col] with row = block (i) row l32 and col = block (j)
-  // column 8*(r/4) + 4*(lane/32) + r%4: each quad r = 4g..4g+3 is 4 consecutive
-  // columns of one row, stored with one 8- or 16-byte access.
-  const int32_t row = m0 + wm * G::TM + l32;
+  // acc[i][j][r] = C[row][col] with row = block (i) row lr and col = block (j)
+  // column 8*(r/4) + 4*lc + r%4 (MI = 32) or 4*lc + r (MI = 16): each quad
+  // r = 4g..4g+3 is 4 consecutive columns of one row, stored with one 8- or
+  // 16-byte access.
+  const int32_t row = m0 + wm * G::TM + lr;
 #pragma unroll
   for (int i = 0; i < G::FM; ++i)
 #pragma unroll
     for (int j = 0; j < G::FN; ++j)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int32_t r = row + i * 32;
-        const int32_t col = n0 + wn * G::TN + j * 32 + 8 * g + 4 * half;
+      for (int g = 0; g < NACC / 4; ++g) {
+        const int32_t r = row + i * MI;
+        const int32_t col = n0 + wn * G::TN + j * MI + 8 * g + 4 * lc;
         if (r < M && col < N) {
           const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
           epilogue4<EPI>(ep, N, r, col, v);
@@ -298,28 +313,36 @@ __global__ __launch_bounds__(G::THREADS, G::MINB) void gemm_bf16_kernel(
       }
 }
 
-// Three tile shapes, chosen per GEMM shape (pick_cfg).  Measured on MI355X
-// (interleaved runs, M = 8190 rows) against 256x128, 256x256, 64x192 and
-// 128x64 tiles, 4- and 8-wave layouts and 2-4 stage rings:
-//  * 256x192, 8 waves of 64x96, 2 stages (112 KiB LDS, one workgroup per
-//    CU): out-projection 762, MLP up 986, MLP down 1141, QKV 920 TFLOP/s;
+// Three tile shapes, chosen per GEMM shape (pick_cfg), all on the 16x16x32
+// MFMA.  Measured on MI355X with interleaved runs over 4 rotating weight sets
+// (TFLOP/s for QKV / out-projection / MLP up / MLP down, D 1536, FFN 8960):
+//  * 128x192, 8 waves of 32x96 (80 KiB LDS, two workgroups per CU):
+//    M = 8190: 1031 / 863 / 1040 / 1135, against 945 / 765 / 988 / 1110 for
+//    the same pipeline on 256x192 tiles of 32x32x16 MFMAs.  The 16x16 shape
+//    issues twice the operand reads per flop, but at 16 rows per block a
+//    wave's tile needs half the accumulator registers of the 32x32 form of
+//    the same block count, which leaves room for two workgroups per CU;
 //    192 divides the stack's output widths (1536, 4608), so the tile count
 //    is a whole number of rounds over the chip;
-//  * 128x192, 8 waves of 32x96 (80 KiB, two workgroups per CU): QKV 944;
-//  * 128x128, 8 waves of 32x64 (64 KiB, two per CU): 671 / 906 / 950 / 896,
-//    but the most tiles when M is small.
-typedef GemmCfg<256, 192, 4, 2, 2, 4, 1> CfgWide;
-typedef GemmCfg<128, 192, 4, 2, 2, 4> CfgMain;
-typedef GemmCfg<128, 128, 4, 2, 2, 8> CfgSmall;
+//  * 256x256, 8 waves of 64x128, one workgroup per CU (128 KiB): fewer,
+//    larger tiles for large M: M = 32760: 983 / 746 / 1046 / 1160 against
+//    1014 / 747 / 1017 / 1091 for 128x192;
+//  * 128x128, 8 waves of 32x64 (64 KiB, two per CU): the most tiles when M
+//    is small: M = 2048: 599 / 413 / 777 / 579 against 751 / 357 / 926 / 509.
+// 256x192 and 128x128 tiles of 32x32x16 MFMAs, 256x128, 64x192 and 128x64
+// tiles, 4-wave layouts and 3-4 stage rings measured slower.
+typedef GemmCfg<256, 256, 4, 2, 2, 4, 1, 16> CfgWide;
+typedef GemmCfg<128, 192, 4, 2, 2, 4, 2, 16> CfgMain;
+typedef GemmCfg<128, 128, 4, 2, 2, 8, 2, 16> CfgSmall;
 
 enum { kCfgWide, kCfgMain, kCfgSmall };
 
-// Row blocks per tile group of the 256x192 tiles.  Each layer's weights are
+// Row blocks per tile group of the 256x256 tiles.  Each layer's weights are
 // read cold from HBM once per iteration: with wide outputs (QKV, MLP up) two
 // row blocks per group keep more of W's column tiles streaming at once
-// (interleaved runs over 8 rotating weight sets: MLP up 863 -> 931, QKV
-// 878 -> 904 TFLOP/s); the narrow, long-K shapes (out-projection, MLP down)
-// do best with four.
+// (interleaved runs over 8 rotating weight sets, 256-row tiles: MLP up
+// 863 -> 931, QKV 878 -> 904 TFLOP/s); the narrow, long-K shapes
+// (out-projection, MLP down) do best with four.
 int32_t wide_group_rows(int32_t N) { return N > 2048 ? 2 : CfgWide::GM; }
 
 // Cost model: a CU works through ceil(tiles / 256) tiles of its shape one
@@ -329,7 +352,7 @@ int32_t wide_group_rows(int32_t N) { return N > 2048 ? 2 : CfgWide::GM; }
 int pick_cfg(int32_t M, int32_t N) {
   constexpr int64_t kCus = 256;
   const struct { int id; int64_t bm, bn, eff; } c[3] = {
-      {kCfgWide, 256, 192, 1000}, {kCfgMain, 128, 192, 960}, {kCfgSmall, 128, 128, 900}};
+      {kCfgWide, 256, 256, 1025}, {kCfgMain, 128, 192, 1000}, {kCfgSmall, 128, 128, 900}};
   int best = kCfgWide;
   int64_t best_cost = -1;
   for (const auto& x : c) {
