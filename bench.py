@@ -68,6 +68,8 @@ def parse():
     p.add_argument("--wan14b", action="store_true",
                    help="also time the whole 14B-shaped iteration (40 blocks, N=75600; ~155 GB of HBM)")
     p.add_argument("--no-scaling", action="store_true", help="skip the iteration-time vs active-fraction sweep")
+    p.add_argument("--no-hbm-sweep", action="store_true",
+                   help="skip the Euler and batched-select bandwidth sweeps")
     p.add_argument("--cpu-rows", type=int, default=2048)
     p.add_argument("--euler-tokens", type=int, default=1 << 24,
                    help="tokens for the Euler-pass bandwidth measurement (>= 1 GiB working set)")
@@ -170,6 +172,43 @@ def time_euler(H, n_tokens: int, C: int = 16, frac: float = 0.25, reps: int = 10
     del x, vh, sc, vn, pos, act
     return {"tokens": n_tokens, "active_frac": frac, "bytes": nbytes, "us": round(t * 1e6, 1),
             "gbs": round(nbytes / t / 1e9, 1), "frac_of_hbm_peak": round(nbytes / t / 1e9 / PEAK_HBM_GBS, 4)}
+
+
+def time_select_batch(H, B: int, N: int = 32760, counts=(8190, 8190, 16380), reps: int = 5):
+    """hsa_select_batch over B independent score rows of N tokens (one
+    selection per video): GB/s of algorithmic bytes, each score read once and
+    each group written once (5 B per token)."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(B)
+    score = torch.rand((B, N), generator=g, device="cuda")
+    out = torch.empty((B, N), dtype=torch.uint8, device="cuda")
+    for _ in range(2):
+        H.hsa_select_batch(score, list(counts), out)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        H.hsa_select_batch(score, list(counts), out)
+    e.record()
+    torch.cuda.synchronize()
+    t = s.elapsed_time(e) / 1e3 / reps
+    nbytes = B * N * 5
+    del score, out
+    return {"rows": B, "tokens_per_row": N, "bytes": nbytes, "us": round(t * 1e6, 1),
+            "gbs": round(nbytes / t / 1e9, 1), "frac_of_hbm_peak": round(nbytes / t / 1e9 / PEAK_HBM_GBS, 4)}
+
+
+def hbm_sweep(H, copy_gbs=None):
+    """The two HBM-bound passes over growing working sets, up to past 1 GiB:
+    the Euler + v_hat + score kernel over more tokens, and selection over a
+    batch of videos of the workload's 32760 tokens (the working set of one
+    video, 0.16 MB, is latency-bound and cache-resident)."""
+    out = {"euler": [time_euler(H, n) for n in (32760, 1 << 20, 1 << 22, 1 << 24, 24 << 20)],
+           "select_batch": [time_select_batch(H, b) for b in (1, 64, 512, 2048, 8192)]}
+    if copy_gbs:
+        for r in out["euler"] + out["select_batch"]:
+            r["frac_of_attainable_copy"] = round(r["gbs"] / copy_gbs, 4)
+    return out
 
 
 def device_inputs(c, H, seed_base):
@@ -682,6 +721,8 @@ def main():
         if "attainable" in out:
             out["euler_hbm"]["frac_of_attainable_copy"] = round(
                 out["euler_hbm"]["gbs"] / out["attainable"]["copy_gbs"], 4)
+    if not args.no_hbm_sweep:
+        out["hbm_sweep"] = hbm_sweep(H, out.get("attainable", {}).get("copy_gbs"))
     if not args.no_scaling:
         out["scaling_with_active_fraction"] = step_scaling(H, model, state, c, sigma)
     if not args.no_stages:

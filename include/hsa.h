@@ -200,6 +200,14 @@ hsa_status hsa_active_set(const uint8_t *group, int32_t N, const hsa_schedule *s
 hsa_status hsa_select(const float *score, int32_t N, const int32_t *count, int32_t K,
                       uint8_t *group_out, void *ws, size_t ws_bytes, void *stream);
 
+/* The same selection for a batch of B independent score vectors (one per
+ * video), each ranked and split by the same count[] (host, K entries summing
+ * to N): score [B][N] float32 -> group_out [B][N], row b of the output from
+ * row b of the input only.  Bit-exact per row, as hsa_select.  B, N > 0;
+ * HSA_ERR_SCHEDULE when the counts are negative or do not sum to N. */
+hsa_status hsa_select_batch(const float *score, int32_t B, int32_t N, const int32_t *count,
+                            int32_t K, uint8_t *group_out, void *stream);
+
 /* Cached Euler update (section 2.3) with the L1 score (section 2.1): for
  * each token n with pos[n] >= 0, if update_score: score[n] =
  * sum_c|v_new[pos[n]] - v_hat[n]| / (sum_c|v_hat[n]| + eps); then v_hat[n] =

@@ -148,6 +148,58 @@ def test_select_zero_count_groups():
         _select_case(s, counts)
 
 
+def _select_batch_case(score, counts):
+    s = dev(score, torch.float32)
+    out = torch.full(score.shape, 255, dtype=torch.uint8, device=DEV)
+    H.hsa_select_batch(s, counts, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    for b in range(score.shape[0]):
+        np.testing.assert_array_equal(got[b], O.select_groups(score[b], counts), err_msg=f"row {b}")
+
+
+@pytest.mark.parametrize("B,N,K", [(1, 1, 2), (3, 10, 2), (5, 1001, 3), (4, 1000, 8), (2, 4099, 5),
+                                   (3, 32760, 3), (2, 32768, 4), (2, 40000, 3), (6, 513, 1)])
+def test_select_batch_bit_exact(B, N, K):
+    """Each row of a batch against the oracle's selection of that row: rows
+    staged in LDS (N <= 32768) and read from memory (N = 40000), rows whose
+    start is not 16- or 4-byte aligned (N odd), ties and special values."""
+    say(f"select batch B={B} N={N} K={K}")
+    rs = np.random.default_rng(B * 100000 + N * 10 + K)
+    cuts = np.sort(rs.integers(0, N + 1, K - 1))
+    counts = np.diff(np.concatenate([[0], cuts, [N]])).astype(int).tolist()
+    _select_batch_case(rs.standard_normal((B, N)).astype(np.float32), counts)
+    s = (rs.integers(0, 4, (B, N)) * 0.5).astype(np.float32)
+    for b in range(B):
+        sp = rs.choice(N, size=min(N, 7), replace=False)
+        s[b, sp] = np.array([np.nan, np.inf, -0.0, 0.0, -1.0, -np.inf, np.nan], np.float32)[: sp.size]
+    _select_batch_case(s, counts)
+    # one row constant (every token ties with every boundary key), one row sorted ascending
+    s2 = rs.standard_normal((B, N)).astype(np.float32)
+    s2[0] = 0.25
+    if B > 1:
+        s2[1] = np.sort(s2[1])
+    _select_batch_case(s2, counts)
+
+
+def test_select_batch_rows_independent_and_match_single():
+    """Row b of a batch equals hsa_select on that row alone, and a row's
+    groups do not depend on the other rows."""
+    rs = np.random.default_rng(5)
+    B, N, counts = 4, 32760, [8190, 8190, 16380]
+    score = np.abs(rs.standard_normal((B, N))).astype(np.float32)
+    out = torch.empty((B, N), dtype=torch.uint8, device=DEV)
+    H.hsa_select_batch(dev(score), counts, out)
+    single = torch.empty(N, dtype=torch.uint8, device=DEV)
+    for b in range(B):
+        H.hsa_select(dev(score[b]), counts, single)
+        assert torch.equal(out[b], single)
+    score2 = score.copy()
+    score2[1:] = -score2[1:]
+    H.hsa_select_batch(dev(score2), counts, out)
+    np.testing.assert_array_equal(out[0].cpu().numpy(), O.select_groups(score[0], counts))
+
+
 # ---------------------------------------------------------------- cached Euler
 
 @pytest.mark.parametrize("N,C", [(1, 16), (333, 16), (32760, 16), (100, 8)])

@@ -321,19 +321,35 @@ hsa_status hsa_active_set(const uint8_t* group, int32_t N, const hsa_schedule* s
                            active_idx, pos, n_active_dev, as_stream(stream));
 }
 
+namespace {
+hsa_status check_counts(int32_t N, const int32_t* count, int32_t K) {
+  if (K < 1 || K > HSA_MAX_GROUPS) return HSA_ERR_SHAPE;
+  if (!count) return HSA_ERR_ARG;
+  int64_t sum = 0;
+  for (int k = 0; k < K; ++k) {
+    if (count[k] < 0) return HSA_ERR_SCHEDULE;
+    sum += count[k];
+  }
+  return sum == N ? HSA_OK : HSA_ERR_SCHEDULE;
+}
+}  // namespace
+
 hsa_status hsa_select(const float* score, int32_t N, const int32_t* count, int32_t K,
                       uint8_t* group_out, void* ws, size_t ws_bytes, void* stream) {
   (void)ws;
   (void)ws_bytes;
   if (N <= 0 || K < 1 || K > HSA_MAX_GROUPS) return HSA_ERR_SHAPE;
   if (!score || !count || !group_out) return HSA_ERR_ARG;
-  int64_t sum = 0;
-  for (int k = 0; k < K; ++k) {
-    if (count[k] < 0) return HSA_ERR_SCHEDULE;
-    sum += count[k];
-  }
-  if (sum != N) return HSA_ERR_SCHEDULE;
-  return launch_select(score, N, count, K, group_out, as_stream(stream));
+  RETURN_IF(check_counts(N, count, K));
+  return launch_select(score, 1, N, count, K, group_out, as_stream(stream));
+}
+
+hsa_status hsa_select_batch(const float* score, int32_t B, int32_t N, const int32_t* count,
+                            int32_t K, uint8_t* group_out, void* stream) {
+  if (B <= 0 || N <= 0 || K < 1 || K > HSA_MAX_GROUPS) return HSA_ERR_SHAPE;
+  if (!score || !count || !group_out) return HSA_ERR_ARG;
+  RETURN_IF(check_counts(N, count, K));
+  return launch_select(score, B, N, count, K, group_out, as_stream(stream));
 }
 
 hsa_status hsa_euler(float* x, float* v_hat, float* score, const float* v_new, const int32_t* pos,
@@ -547,7 +563,7 @@ hsa_status hsa_step(const hsa_model* model, const hsa_schedule* sched, hsa_state
   int32_t* n_dev = (int32_t*)(ws + L.n_active);
 
   // 1. regroup by the L1 relative change (before A_i is formed)
-  if (regroup) RETURN_IF(launch_select(st->score, d.N, sched->count, sched->K, st->group, s));
+  if (regroup) RETURN_IF(launch_select(st->score, 1, d.N, sched->count, sched->K, st->group, s));
   // 2. active set; its size is known on the host in closed form
   const int32_t nA = n_active_of(sched, iter);
   RETURN_IF(launch_active_set(st->group, d.N, active_group_mask(sched, iter), nA, st->active_idx,

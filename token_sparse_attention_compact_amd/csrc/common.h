@@ -58,8 +58,8 @@ inline size_t dtype_size(hsa_dtype t) { return t == HSA_BF16 ? 2 : 4; }
 hsa_status launch_active_set(const uint8_t* group, int32_t N, uint32_t active_groups,
                              int32_t expected, int32_t* active_idx, int32_t* pos,
                              int32_t* n_active_dev, hipStream_t s);
-hsa_status launch_select(const float* score, int32_t N, const int32_t* count, int32_t K,
-                         uint8_t* group_out, hipStream_t s);
+hsa_status launch_select(const float* score, int32_t B, int32_t N, const int32_t* count,
+                         int32_t K, uint8_t* group_out, hipStream_t s);
 hsa_status launch_euler(float* x, float* v_hat, float* score, const float* v_new,
                         const int32_t* pos, int32_t N, int32_t C, float dsigma, float eps,
                         int32_t update_score, hipStream_t s);

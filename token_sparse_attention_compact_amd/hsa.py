@@ -28,7 +28,8 @@ FEATURE_BITS = {"qk_norm": FEAT_QK_NORM, "rope3d": FEAT_ROPE3D, "adaln": FEAT_AD
 T_FREQ = 256   # width of the timestep sinusoid (t_w1 is [D][256])
 EXPORTED = [
     "hsa_status_str", "hsa_abi_version", "hsa_workspace_size", "hsa_attn_workspace_size",
-    "hsa_select_workspace_size", "hsa_n_active", "hsa_active_set", "hsa_select", "hsa_euler",
+    "hsa_select_workspace_size", "hsa_n_active", "hsa_active_set", "hsa_select", "hsa_select_batch",
+    "hsa_euler",
     "hsa_attn_active", "hsa_layernorm", "hsa_embed", "hsa_unembed", "hsa_linear",
     "hsa_linear_residual", "hsa_qkv_scatter", "hsa_qk_norm_rope", "hsa_time_embed", "hsa_guidance",
     "hsa_block_forward", "hsa_step",
@@ -104,6 +105,7 @@ def load() -> ct.CDLL:
         "hsa_n_active": ([ct.POINTER(Schedule), I, PI], I),
         "hsa_active_set": ([P, I, ct.POINTER(Schedule), I, P, P, P, P], I),
         "hsa_select": ([P, I, PI, I, P, P, S, P], I),
+        "hsa_select_batch": ([P, I, I, PI, I, P, P], I),
         "hsa_euler": ([P, P, P, P, P, I, I, F, F, I, P], I),
         "hsa_attn_active": ([P, P, P, P, I, I, I, I, F, ct.c_int, P, S, P], I),
         "hsa_layernorm": ([P, P, I, I, P, P, ct.c_int, P], I),
@@ -245,6 +247,18 @@ def hsa_select(score: torch.Tensor, counts: Sequence[int], group_out: torch.Tens
     arr = (ct.c_int32 * len(counts))(*counts)
     _check("hsa_select", load().hsa_select(_ptr(score), score.numel(), arr, len(counts),
                                            _ptr(group_out), None, 0, _stream(stream)))
+
+
+def hsa_select_batch(score: torch.Tensor, counts: Sequence[int], group_out: torch.Tensor, stream=None):
+    """score [B][N] float32 -> group_out [B][N] uint8, each row selected with the same counts."""
+    _need(score, torch.float32, "score")
+    _need(group_out, torch.uint8, "group_out")
+    if score.dim() != 2:
+        raise ValueError(f"score must be [B][N], got shape {tuple(score.shape)}")
+    _shape(group_out, tuple(score.shape), "group_out")
+    arr = (ct.c_int32 * len(counts))(*counts)
+    _check("hsa_select_batch", load().hsa_select_batch(_ptr(score), score.shape[0], score.shape[1], arr,
+                                                       len(counts), _ptr(group_out), _stream(stream)))
 
 
 def hsa_euler(x, v_hat, score, v_new, pos, dsigma: float, update_score: bool, eps: float = 1e-6,
