@@ -1,5 +1,5 @@
 // Internal helpers shared by the HIP kernels and the host API of libhsa.
-// gfx950 (CDNA4) only: 64-wide wavefronts, bf16 MFMA 32x32x16.
+// gfx950 (CDNA4) only: 64-wide wavefronts, bf16 MFMA (32x32x16 and 16x16x32).
 #pragma once
 
 #include <hip/hip_runtime.h>
