@@ -203,8 +203,9 @@ hsa_status hsa_select(const float *score, int32_t N, const int32_t *count, int32
 /* The same selection for a batch of B independent score vectors (one per
  * video), each ranked and split by the same count[] (host, K entries summing
  * to N): score [B][N] float32 -> group_out [B][N], row b of the output from
- * row b of the input only.  Bit-exact per row, as hsa_select.  B, N > 0;
- * HSA_ERR_SCHEDULE when the counts are negative or do not sum to N. */
+ * row b of the input only.  Bit-exact per row, as hsa_select.  B, N > 0 and
+ * B * N <= 2^38 (HSA_ERR_SHAPE otherwise); HSA_ERR_SCHEDULE when the counts
+ * are negative or do not sum to N. */
 hsa_status hsa_select_batch(const float *score, int32_t B, int32_t N, const int32_t *count,
                             int32_t K, uint8_t *group_out, void *stream);
 

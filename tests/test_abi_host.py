@@ -89,6 +89,8 @@ def test_entry_points_reject_bad_arguments_without_a_device():
     assert L.hsa_select_batch(null, 4, 6, counts, 3, null, null) == -1
     assert L.hsa_select_batch(ct.c_void_p(0x1000), 4, 7, counts, 3, ct.c_void_p(0x2000), null) == -7
     assert L.hsa_select_batch(ct.c_void_p(0x1000), 4, 6, counts, 9, ct.c_void_p(0x2000), null) == -2
+    big = (ct.c_int32 * 1)(1 << 30)
+    assert L.hsa_select_batch(ct.c_void_p(0x1000), 1 << 9, 1 << 30, big, 1, ct.c_void_p(0x2000), null) == -2
     assert L.hsa_step(null, null, null, 0, 1.0, 0.9, 0, null, null) == -1
     # misaligned device pointer
     assert L.hsa_layernorm(ct.c_void_p(0x1004), ct.c_void_p(0x2000), 4, 64, null, null, 1, null) == -4

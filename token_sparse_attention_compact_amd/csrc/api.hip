@@ -347,6 +347,7 @@ hsa_status hsa_select(const float* score, int32_t N, const int32_t* count, int32
 hsa_status hsa_select_batch(const float* score, int32_t B, int32_t N, const int32_t* count,
                             int32_t K, uint8_t* group_out, void* stream) {
   if (B <= 0 || N <= 0 || K < 1 || K > HSA_MAX_GROUPS) return HSA_ERR_SHAPE;
+  if ((int64_t)B * N > ((int64_t)1 << 38)) return HSA_ERR_SHAPE;   // grid limits of the fill path
   if (!score || !count || !group_out) return HSA_ERR_ARG;
   RETURN_IF(check_counts(N, count, K));
   return launch_select(score, B, N, count, K, group_out, as_stream(stream));
