@@ -206,12 +206,10 @@ __global__ __launch_bounds__(kThreads) void select_reg_kernel(const float* __res
   // ---- assignment
   uint32_t tk[kMaxB];
   int32_t need[kMaxB];
-  bool split = false;   // some boundary splits its ties by position
 #pragma unroll
   for (int k = 0; k < kMaxB; ++k) {
     tk[k] = __builtin_amdgcn_readfirstlane(live(k) ? s_prefix[k] : kPad);   // no key reaches kPad
     need[k] = __builtin_amdgcn_readfirstlane(live(k) ? s_rem[k] : 0);
-    split |= need[k] > 0;
   }
   uint32_t gp[V];   // 4 group bytes per chunk
 #pragma unroll
@@ -279,7 +277,6 @@ __global__ __launch_bounds__(kThreads) void select_reg_kernel(const float* __res
     }
     __syncthreads();   // tie_pre is reused by the next boundary
   }
-  (void)split;
   const bool aligned4 = (reinterpret_cast<uintptr_t>(out) & 3u) == 0u;
 #pragma unroll
   for (int j = 0; j < V; ++j) {
