@@ -355,3 +355,32 @@ def test_step_graph_capture_replays_match_eager():
         torch.cuda.synchronize()
         for b, e in zip(bufs, eager):
             assert torch.equal(b, e), f"replay {rep} differs from the eager iteration"
+
+
+def test_step_full_size_is_deterministic():
+    """Two runs of the same full-size iteration (N 32760, D 1536, F 8960,
+    2 blocks, regrouping on, the attention's KV range split and merged) from
+    the same state give bit-identical latents, velocities, scores, groups and
+    caches: no kernel on the path accumulates in a run-dependent order."""
+    c = synth.CONFIGS[3].with_(L=2)
+    say("hsa_step full-size determinism")
+    i = 11
+    om = oracle_model(c)
+    s0 = synth.mid_run_state(c)
+    m = device_model(c, om, s0["k_cache"], s0["v_cache"])
+    sched = H.make_schedule(c.T, c.budgets, c.counts())
+    sigma = synth.sigma_schedule(c.T)
+    st = H.DeviceState(m.dims, dev(s0["x"]), dev(s0["group"], torch.uint8), dev(s0["v_hat"]),
+                       dev(s0["score"]))
+    bufs = [st.x, st.v_hat, st.score, st.group] + [b[n] for b in m.blocks for n in ("k_cache", "v_cache")]
+    init = [b.clone() for b in bufs]
+    runs = []
+    for _ in range(2):
+        for b, v in zip(bufs, init):
+            b.copy_(v)
+        H.hsa_step(m, sched, st, i, float(sigma[i]), float(sigma[i + 1]), True)
+        torch.cuda.synchronize()
+        runs.append([b.clone() for b in bufs])
+    for a, b in zip(*runs):
+        assert torch.equal(a, b)
+    assert not torch.equal(runs[0][0], init[0])   # the iteration did move the latents
