@@ -241,3 +241,24 @@ def test_binding_checks_feature_tensors():
     blk["mod"] = torch.zeros(6, 256)
     with pytest.raises(ValueError, match="timestep weights missing"):
         H.DeviceModel(d, torch.zeros(256, 16, dtype=bf), torch.zeros(16, 256, dtype=bf), [blk])
+
+
+def test_header_and_library_from_plain_c(tmp_path):
+    """include/hsa.h compiles as C99 with warnings as errors, and a C program
+    linked against libhsa.so gets the same host-side answers (ABI version,
+    closed-form |A_i|, workspace size, shape errors) as the binding."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    libdir = os.path.dirname(H.lib_path())
+    exe = str(tmp_path / "c_abi_check")
+    cmd = [cc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-I", os.path.join(root, "include"),
+           os.path.join(root, "tests", "c_abi_check.c"), "-L", libdir, "-lhsa",
+           f"-Wl,-rpath,{libdir}", "-o", exe]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0 and "c abi ok" in r.stdout, (r.returncode, r.stdout, r.stderr)
