@@ -209,15 +209,16 @@ def test_guidance_kernel():
 
 # ---------------------------------------------------------------- one block
 
-@pytest.mark.parametrize("features,n_text,branch", [(ALL, 0, 0), (ALL + ("cfg",), 16, 0),
-                                                    (ALL + ("cfg",), 16, 1), (("rope3d",), 0, 0)])
-def test_featured_block_forward_bf16(features, n_text, branch):
-    """One bf16 block (D 256, 2x128 heads) on 211 of 640 tokens with stale cache
-    rows, the timestep projection from the library, and the unconditional
-    branch's text set and caches when branch == 1."""
-    c = tiny(features, "bf16", Dh=128, H_=2, grid=(2, 20, 16), n_text=n_text,
+@pytest.mark.parametrize("features,n_text,branch,Dh", [(ALL, 0, 0, 128), (ALL + ("cfg",), 16, 0, 128),
+                                                       (ALL + ("cfg",), 16, 1, 128), (("rope3d",), 0, 0, 128),
+                                                       (ALL, 0, 0, 64), (ALL + ("cfg",), 16, 1, 64)])
+def test_featured_block_forward_bf16(features, n_text, branch, Dh):
+    """One bf16 block (D 256 as 2x128 or 4x64 heads) on 211 of 640 tokens with
+    stale cache rows, the timestep projection from the library, and the
+    unconditional branch's text set and caches when branch == 1."""
+    c = tiny(features, "bf16", Dh=Dh, H_=256 // Dh, grid=(2, 20, 16), n_text=n_text,
              text_dim=64 if n_text else 0)
-    say(f"featured block bf16 {features} n_text={n_text} branch={branch}")
+    say(f"featured block bf16 {features} n_text={n_text} branch={branch} Dh={Dh}")
     om = oracle_model(c)
     kc, vc = synth.kv_cache(c)
     m = device_model(c, kc[None], vc[None])
