@@ -219,11 +219,12 @@ def test_step_constant_velocity_closed_form():
     np.testing.assert_allclose(host(st.x), expect, rtol=0, atol=1e-5)
 
 
-@pytest.mark.parametrize("i,regroup", [(10, True), (11, False), (12, False)])
-def test_step_mid_run_bf16(i, regroup):
+@pytest.mark.parametrize("i,regroup,Dh", [(10, True, 128), (11, False, 128), (12, False, 128),
+                                          (10, True, 64)])
+def test_step_mid_run_bf16(i, regroup, Dh):
     """One iteration from a synthetic mid-run state (caches, v_hat, scores, groups)."""
-    c = small_bf16()
-    say(f"hsa_step mid-run bf16 i={i}")
+    c = small_bf16(Dh=Dh, H=256 // Dh)
+    say(f"hsa_step mid-run bf16 i={i} Dh={Dh}")
     om = oracle_model(c)
     s0 = synth.mid_run_state(c)
     m = device_model(c, om, s0["k_cache"], s0["v_cache"])
