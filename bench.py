@@ -15,7 +15,8 @@ stream), also at other active fractions and at the 14B-shaped layer, the full
 T = 40 sampling loop from fresh latents (also under other schedules and
 against dense sampling), iteration time
 against the active fraction, the Euler pass on a working set past the
-Infinity Cache, one block's stages (gathered QKV + scatter, attention,
+Infinity Cache and over growing working sets, selection over a batch of up
+to 8192 videos, one block's stages (gathered QKV + scatter, attention,
 out-projection) at four active fractions and two active-set patterns, the
 iteration with the Wan-style block features on (and with
 cross-attention and guidance batch 2), attainable peaks (an MFMA-only probe
