@@ -200,6 +200,22 @@ def test_select_batch_rows_independent_and_match_single():
     np.testing.assert_array_equal(out[0].cpu().numpy(), O.select_groups(score[0], counts))
 
 
+def test_select_batch_full_size_sampled_rows():
+    """The bench's batch (8192 videos of 32760 tokens, counts 8190 / 8190 /
+    16380): every row's group sizes are exact, and sampled rows match the
+    oracle's selection bit for bit."""
+    B, N, counts = 8192, 32760, [8190, 8190, 16380]
+    g = torch.Generator(device=DEV)
+    g.manual_seed(8192)
+    score = torch.rand((B, N), generator=g, device=DEV)
+    out = torch.empty((B, N), dtype=torch.uint8, device=DEV)
+    H.hsa_select_batch(score, counts, out)
+    sizes = torch.stack([(out == k).sum(dim=1) for k in range(3)], dim=1)
+    assert torch.equal(sizes.cpu(), torch.tensor([counts] * B))
+    for b in (0, 1, 4095, 8191):
+        np.testing.assert_array_equal(out[b].cpu().numpy(), O.select_groups(score[b].cpu().numpy(), counts))
+
+
 # ---------------------------------------------------------------- cached Euler
 
 @pytest.mark.parametrize("N,C", [(1, 16), (333, 16), (32760, 16), (100, 8)])
