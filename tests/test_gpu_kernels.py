@@ -242,6 +242,41 @@ def test_euler_matches_oracle(N, C):
         np.testing.assert_array_equal(host(ts)[skipped], sc[skipped])
 
 
+def test_euler_sweep_size_sampled_tokens():
+    """The Euler pass at the largest size the bench sweeps (24M tokens, 25%
+    active, device-generated inputs): 4096 sampled tokens, active and
+    skipped, against the oracle's update of those tokens; skipped tokens'
+    v_hat and score untouched everywhere."""
+    N, C = 24 << 20, 16
+    g = torch.Generator(device=DEV)
+    g.manual_seed(24)
+    x = torch.randn((N, C), generator=g, device=DEV)
+    vh = torch.randn((N, C), generator=g, device=DEV)
+    sc = torch.rand((N,), generator=g, device=DEV)
+    nA = N // 4
+    act = torch.randperm(N, generator=g, device=DEV)[:nA].sort().values.to(torch.int32)
+    pos = torch.full((N,), -1, dtype=torch.int32, device=DEV)
+    pos[act.long()] = torch.arange(nA, dtype=torch.int32, device=DEV)
+    vn = torch.randn((nA, C), generator=g, device=DEV)
+    x0, vh0, sc0 = x.clone(), vh.clone(), sc.clone()
+    ds = np.float32(-0.025)
+    H.hsa_euler(x, vh, sc, vn, pos, float(ds), True)
+    torch.cuda.synchronize()
+    active = pos >= 0
+    assert torch.equal(vh[~active], vh0[~active]) and torch.equal(sc[~active], sc0[~active])
+    rs = np.random.default_rng(24)
+    tok = np.sort(rs.choice(N, 4096, replace=False))
+    t = torch.from_numpy(tok).to(DEV)
+    p = pos[t].cpu().numpy()
+    rows = np.flatnonzero(p >= 0)
+    rx, rv, rsc = O.euler_update(x0[t].cpu().numpy(), vh0[t].cpu().numpy(), sc0[t].cpu().numpy(),
+                                 vn[torch.from_numpy(p[rows]).to(DEV).long()].cpu().numpy(),
+                                 rows.astype(np.int32), ds, update_score=True)
+    np.testing.assert_allclose(x[t].cpu().numpy(), rx, rtol=1e-6, atol=1e-6)
+    np.testing.assert_array_equal(vh[t].cpu().numpy(), rv)
+    np.testing.assert_allclose(sc[t].cpu().numpy(), rsc, rtol=2e-6, atol=0)
+
+
 def test_euler_hand_values():
     import json, os
     g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "euler_hand.json")))
