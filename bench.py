@@ -16,7 +16,8 @@ T = 40 sampling loop from fresh latents (also under other schedules and
 against dense sampling), iteration time
 against the active fraction, the Euler pass on a working set past the
 Infinity Cache and over growing working sets, selection over a batch of up
-to 8192 videos, one block's stages (gathered QKV + scatter, attention,
+to 8192 videos, the block's four GEMMs alone at three active fractions, one
+block's stages (gathered QKV + scatter, attention,
 out-projection) at four active fractions and two active-set patterns, the
 iteration with the Wan-style block features on (and with
 cross-attention and guidance batch 2), attainable peaks (an MFMA-only probe
@@ -568,6 +569,50 @@ def stage_bench(H, model, c, reps: int = 10):
     return rows
 
 
+def gemm_bench(H, model, c, fracs=(1.0, 0.25, 0.0625)):
+    """The block's four GEMMs with their fused epilogues, alone: QKV with the
+    K/V scatter, out-projection + residual, MLP up + GELU, MLP down +
+    residual, at |A|/N in fracs. Each call uses the next layer's weights (30
+    rotating sets, read cold from HBM as in the iteration); HIP events, mean
+    over two passes of the 30 layers."""
+    N, D, F = c.N, c.D, c.F
+    bf = torch.bfloat16
+    out = []
+    for f in fracs:
+        nA = synth.n_active_for_fraction(N, f)
+        a = torch.randn(nA, D, device="cuda").to(bf)
+        u = torch.randn(nA, F, device="cuda").to(bf)
+        q = torch.empty(nA, D, dtype=bf, device="cuda")
+        hid = torch.empty(nA, F, dtype=bf, device="cuda")
+        hres = torch.zeros(nA, D, device="cuda")
+        idx = torch.arange(nA, dtype=torch.int32, device="cuda")
+        kc = torch.empty(N, D, dtype=bf, device="cuda")      # scatter targets (not the model's caches)
+        vc = torch.empty(N, D, dtype=bf, device="cuda")
+        L = len(model.blocks)
+        cnt = [0]
+
+        def nxt():
+            b = model.blocks[cnt[0] % L]
+            cnt[0] += 1
+            return b
+        calls = {
+            "qkv_scatter": (2.0 * nA * D * 3 * D,
+                            lambda: H.hsa_qkv_scatter(a, idx, nA, nxt()["w_qkv"], q, kc, vc)),
+            "out_proj_residual": (2.0 * nA * D * D, lambda: H.hsa_linear_residual(a, nxt()["w_o"], hres)),
+            "mlp_up_gelu": (2.0 * nA * D * F, lambda: H.hsa_linear(a, nxt()["w_1"], hid, act=1)),
+            "mlp_down_residual": (2.0 * nA * F * D, lambda: H.hsa_linear_residual(u, nxt()["w_2"], hres)),
+        }
+        row = {"n_active": nA}
+        for name, (flop, fn) in calls.items():
+            t = _event_time(fn, 2 * L, warmup=L)
+            row[name + "_us"] = round(t * 1e6, 1)
+            row[name + "_tflops"] = round(flop / t / 1e12, 1)
+        out.append(row)
+        del a, u, q, hid, hres, kc, vc
+    torch.cuda.empty_cache()
+    return out
+
+
 def wan14b_iteration(H, steps: int = 2):
     """The whole 14B-shaped iteration (opt-in, --wan14b): 40 blocks, N = 75600
     (21 x 45 x 80), D 5120, 40 x 128 heads, F 13824, 512-token cross-attention,
@@ -728,6 +773,7 @@ def main():
         out["scaling_with_active_fraction"] = step_scaling(H, model, state, c, sigma)
     if not args.no_stages:
         out["stage_bench"] = stage_bench(H, model, c)
+        out["gemm_bench"] = gemm_bench(H, model, c)
     if not args.no_features:
         out["wan_features"] = wan_features(H, model, state, c, sigma, ms)
         if "attainable" in out:
