@@ -343,9 +343,9 @@ def test_layernorm_widths(D, dtype):
                                    (1000, 1536, 1536),
                                    # each tile shape the library picks, ragged in M and N:
                                    # 256x256 (4000 x 4000), 128x192 (2100 x 4000, 1100 x 4000),
-                                   # 128x128 with long K (1030 x 300)
+                                   # 128x128 (1000 x 4000), 128x64 with long K (1030 x 300)
                                    (4000, 4000, 128), (2100, 4000, 128), (1100, 4000, 128),
-                                   (1030, 300, 4160)])
+                                   (1000, 4000, 128), (1030, 300, 4160)])
 def test_linear_bf16(M, N, K):
     say(f"linear bf16 M={M} N={N} K={K}")
     rs = np.random.default_rng(M * 7 + N + K)

@@ -334,8 +334,13 @@ __global__ __launch_bounds__(G::THREADS, G::MINB) void gemm_bf16_kernel(
 typedef GemmCfg<256, 256, 4, 2, 2, 4, 1, 16> CfgWide;
 typedef GemmCfg<128, 192, 4, 2, 2, 4, 2, 16> CfgMain;
 typedef GemmCfg<128, 128, 4, 2, 2, 8, 2, 16> CfgSmall;
+// 128x64, 8 waves of 32x32 (48 KiB, two per CU): narrow outputs at small M,
+// where the larger tiles leave CUs idle: M = 2048, N = 1536: out-projection
+// 447 and MLP down 614 TFLOP/s against 408 and 572 on 128x128 tiles
+// (M = 1638: 363 / 519 against 324 / 448); from M = 4095 the larger tiles win.
+typedef GemmCfg<128, 64, 4, 2, 2, 8, 2, 16> CfgTiny;
 
-enum { kCfgWide, kCfgMain, kCfgSmall };
+enum { kCfgWide, kCfgMain, kCfgSmall, kCfgTiny };
 
 // Row blocks per tile group of the 256x256 tiles.  Each layer's weights are
 // read cold from HBM once per iteration: with wide outputs (QKV, MLP up) two
@@ -350,6 +355,7 @@ int32_t wide_group_rows(int32_t N) { return N > 2048 ? 2 : CfgWide::GM; }
 // time ~ ceil(tiles / 256) * tile area / relative efficiency.  Ties go to
 // the larger tile.
 int pick_cfg(int32_t M, int32_t N) {
+  if (M <= 2048 && N <= 2048) return kCfgTiny;
   constexpr int64_t kCus = 256;
   const struct { int id; int64_t bm, bn, eff; } c[3] = {
       {kCfgWide, 256, 256, 1025}, {kCfgMain, 128, 192, 1000}, {kCfgSmall, 128, 128, 900}};
@@ -430,7 +436,8 @@ hsa_status run(const void* a, const void* w, int32_t M, int32_t N, int32_t K, hs
         launch_bf16<CfgWide, EPI>(a, w, M, N, K, wide_group_rows(N), ep, s);
         break;
       case kCfgMain: launch_bf16<CfgMain, EPI>(a, w, M, N, K, CfgMain::GM, ep, s); break;
-      default: launch_bf16<CfgSmall, EPI>(a, w, M, N, K, CfgSmall::GM, ep, s); break;
+      case kCfgSmall: launch_bf16<CfgSmall, EPI>(a, w, M, N, K, CfgSmall::GM, ep, s); break;
+      default: launch_bf16<CfgTiny, EPI>(a, w, M, N, K, CfgTiny::GM, ep, s); break;
     }
   } else {
     dim3 grid(cdiv(N, FT), cdiv(M, FT));
