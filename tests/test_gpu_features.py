@@ -252,13 +252,14 @@ def test_featured_block_forward_bf16(features, n_text, branch, Dh):
         np.testing.assert_array_equal(other, kc)
 
 
-def test_featured_block_full_size_sampled_rows():
+@pytest.mark.parametrize("frac", [0.25, 0.125])
+def test_featured_block_full_size_sampled_rows(frac):
     """Wan-1.3B-shaped block (D 1536, 12x128 heads, F 8960, N = 32760 on the
     21x30x52 grid) with qk-RMSNorm, 3D rotation and timestep modulation, 25%
-    of the tokens active at random: every active K/V row and 48 sampled
-    output rows against the oracle."""
+    or 12.5% of the tokens active at random: every active K/V row and 48
+    sampled output rows against the oracle."""
     c = synth.CONFIGS[2].with_(features=ALL)
-    nA = synth.n_active_for_fraction(c.N, 0.25)
+    nA = synth.n_active_for_fraction(c.N, frac)
     say(f"featured block full-size nA={nA}")
     om = oracle_model(c)
     kc, vc = synth.kv_cache(c)

@@ -94,7 +94,8 @@ def test_block_forward_small_bf16(n_text, Dh):
     assert rel_l2(host(m.blocks[0]["v_cache"])[idx], vref[idx]) < 5e-3
 
 
-@pytest.mark.parametrize("frac,pattern", [(0.25, "random"), (0.25, "blob"), (0.0625, "blob")])
+@pytest.mark.parametrize("frac,pattern", [(0.25, "random"), (0.25, "blob"), (0.125, "random"),
+                                          (0.0625, "blob")])
 def test_block_forward_full_size_sampled_rows(frac, pattern):
     """Wan-1.3B-shaped block (D 1536, 12x128 heads, F 8960) over N = 32760 cached
     rows, active rows drawn at random or as contiguous spatial blobs (per frame
