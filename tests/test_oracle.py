@@ -372,6 +372,83 @@ def test_cache_rows_hold_last_active_projection():
         np.testing.assert_allclose(st.k_cache, last_k, rtol=1e-5, atol=1e-6)
 
 
+def _stale_block_case(seed=21):
+    """A block with a partial active set over a cache whose skipped rows hold
+    stale values unrelated to the current rows (KV-cache synchronisation,
+    HSA summary section 2.2, items 2-3)."""
+    c = _tiny_cfg(grid=(1, 4, 4), C=4, D=16, H=2, Dh=8, F=32, L=1)
+    m = _model(c)
+    rs = np.random.default_rng(seed)
+    idx = np.array([1, 4, 6, 9, 13])
+    h = rs.standard_normal((idx.size, c.D))
+    k_cache = rs.standard_normal((c.N, c.D))
+    v_cache = rs.standard_normal((c.N, c.D))
+    return c, m, idx, h, k_cache, v_cache
+
+
+def test_active_queries_attend_to_stale_rows_closed_form():
+    # Active queries see every cached row: here one skipped token's stale key
+    # dominates every active query's logits in every head, so the attention
+    # output of each active row is that token's stale value row.  With W_o = I
+    # and W_1 = 0 the block returns h + v_stale exactly (GELU(0) = 0), whatever
+    # the fresh rows are.  Attending over the fresh rows alone gives their
+    # values instead (all equal here), which this checks is not what happens.
+    c, m, idx, _, k_cache, v_cache = _stale_block_case()
+    D = c.D
+    rs = np.random.default_rng(22)
+    u = rs.standard_normal(D)
+    # LayerNorm ignores scale and offset: every active row normalises to LN(u),
+    # so all fresh q (and k, v) rows are equal.
+    h = np.stack([(j + 1.5) * u + 0.25 * j for j in range(idx.size)])
+    blk = m.blocks[0]
+    blk["w_o"] = np.eye(D)
+    blk["w_1"] = np.zeros_like(blk["w_1"])
+    q = O.layer_norm(u[None, :]) @ blk["w_qkv"][:D].T
+    stale = 11
+    assert stale not in idx
+    k_cache[:, :] = 0.0
+    k_cache[stale] = 60.0 * q[0] / np.abs(q[0]).max() ** 2    # logit >= 60 / sqrt(Dh) per head
+    v_stale = np.linspace(-2.0, 3.0, D)
+    v_cache[stale] = v_stale
+    out = O.block_forward(m, 0, h, idx, k_cache, v_cache)
+    # every other logit is q.k_fresh (tiny next to the planted one) or 0
+    np.testing.assert_allclose(out, h + v_stale[None, :], rtol=0, atol=1e-6)
+    v_fresh = O.layer_norm(u[None, :]) @ blk["w_qkv"][2 * D:].T
+    assert np.abs(out - (h + v_fresh)).max() > 0.5
+
+
+def test_block_attention_over_stale_cache_matches_torch_sdpa():
+    # Brute force with torch CPU float64 library ops: write the fresh K/V of the
+    # active rows into a copy of the stale cache, then SDPA of the active
+    # queries over all N rows, out-projection, MLP; compare the block's output.
+    c, m, idx, h, k_cache, v_cache = _stale_block_case()
+    D, H, Dh, N = c.D, c.H, c.Dh, c.N
+    t = lambda a: torch.from_numpy(np.asarray(a, np.float64))
+    w = m.blocks[0]
+    ht = t(h)
+    qkv = Fnn.linear(Fnn.layer_norm(ht, (D,), eps=1e-6), t(w["w_qkv"]))
+    kc, vc = t(k_cache).clone(), t(v_cache).clone()
+    kc[torch.from_numpy(idx)] = qkv[:, D:2 * D]
+    vc[torch.from_numpy(idx)] = qkv[:, 2 * D:]
+    M = idx.size
+    o = Fnn.scaled_dot_product_attention(qkv[:, :D].view(M, H, Dh).transpose(0, 1),
+                                         kc.view(N, H, Dh).transpose(0, 1),
+                                         vc.view(N, H, Dh).transpose(0, 1))
+    ht = ht + Fnn.linear(o.transpose(0, 1).reshape(M, D), t(w["w_o"]))
+    u = Fnn.gelu(Fnn.linear(Fnn.layer_norm(ht, (D,), eps=1e-6), t(w["w_1"])), approximate="tanh")
+    ref = (ht + Fnn.linear(u, t(w["w_2"]))).numpy()
+    kc_o, vc_o = k_cache.copy(), v_cache.copy()
+    out = O.block_forward(m, 0, h, idx, kc_o, vc_o)
+    np.testing.assert_allclose(out, ref, rtol=1e-5, atol=1e-6)   # float32 storage on the oracle side
+    np.testing.assert_allclose(kc_o, kc.numpy(), rtol=1e-6, atol=1e-7)
+    np.testing.assert_allclose(vc_o, vc.numpy(), rtol=1e-6, atol=1e-7)
+    # the stale rows do move the result: attending over the fresh rows alone differs
+    o_fresh = Fnn.scaled_dot_product_attention(qkv[:, :D].view(M, H, Dh).transpose(0, 1),
+                                               qkv[:, D:2 * D].view(M, H, Dh).transpose(0, 1),
+                                               qkv[:, 2 * D:].view(M, H, Dh).transpose(0, 1))
+    assert (o_fresh - o).abs().max().item() > 0.1
+
+
 def test_total_work_matches_budgets():
     # Over T iterations with static groups the number of token evaluations is sum_k n_k s_k:
     # attention work O(|A_i| N) summed over the run.
