@@ -9,7 +9,7 @@ import torch
 
 import synth
 from oracle import hsa_oracle as O
-from tests.gpu_common import DEV, TOL_BF16, TOL_F32, dev, host, rel_l2, say
+from tests.gpu_common import DEV, TOL_BF16, TOL_F32, assert_rows_close, dev, host, rel_l2, say
 
 pytestmark = pytest.mark.gpu
 
@@ -580,7 +580,7 @@ def test_attention_full_size_sampled_rows(frac):
                       c.H, c.Dh)
     rows = np.sort(rs.choice(nA, 64, replace=False))
     ref = O.attention(q[rows], kc, vc, c.H, c.Dh)
-    assert rel_l2(host(o)[rows], ref) < TOL_BF16
+    assert_rows_close(host(o)[rows], ref, TOL_BF16, "attention rows")
 
 
 @pytest.mark.parametrize("frac", [0.25, 0.0625])
@@ -599,4 +599,4 @@ def test_attention_full_size_64_wide_heads(frac):
                       c.H, c.Dh)
     rows = np.sort(rs.choice(nA, 64, replace=False))
     ref = O.attention(q[rows], kc, vc, c.H, c.Dh)
-    assert rel_l2(host(o)[rows], ref) < TOL_BF16
+    assert_rows_close(host(o)[rows], ref, TOL_BF16, "attention rows")

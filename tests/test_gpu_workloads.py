@@ -16,7 +16,7 @@ import torch
 
 import synth
 from oracle import hsa_oracle as O
-from tests.gpu_common import DEV, TOL_BF16, dev, host, rel_l2, say
+from tests.gpu_common import DEV, TOL_BF16, assert_rows_close, dev, host, rel_l2, say
 
 pytestmark = pytest.mark.gpu
 
@@ -52,7 +52,7 @@ def test_attention_14b_shape_sampled_rows():
     torch.cuda.synchronize()
     rows = np.sort(rs.choice(nA, 24, replace=False))
     ref = O.attention(q[rows], kc, vc, c.H, c.Dh)
-    assert rel_l2(host(o)[rows], ref) < TOL_BF16
+    assert_rows_close(host(o)[rows], ref, TOL_BF16, "attention rows")
 
 
 def test_cross_attention_14b_shape():
@@ -67,7 +67,7 @@ def test_cross_attention_14b_shape():
     H.hsa_attn_active(dev(q, torch.bfloat16), dev(kt, torch.bfloat16), dev(vt, torch.bfloat16), o, c.H, c.Dh)
     torch.cuda.synchronize()
     rows = np.sort(rs.choice(nA, 64, replace=False))
-    assert rel_l2(host(o)[rows], O.attention(q[rows], kt, vt, c.H, c.Dh)) < TOL_BF16
+    assert_rows_close(host(o)[rows], O.attention(q[rows], kt, vt, c.H, c.Dh), TOL_BF16, "attention rows")
 
 
 def test_block_forward_14b_shape_with_cross_attention():
@@ -105,9 +105,10 @@ def test_block_forward_14b_shape_with_cross_attention():
     assert rel_l2(host(kt), om.blocks[0]["k_text"]) < 5e-3
     rows = np.sort(np.random.default_rng(7).choice(nA, 24, replace=False))
     ref = O.block_forward(om, 0, h, idx, kc, vc, rows=rows)     # caches updated in place
-    assert rel_l2(host(th)[rows], ref) < TOL_BF16
+    assert_rows_close(host(th)[rows], ref, TOL_BF16, "block output rows")
     k_gpu = host(m.blocks[0]["k_cache"])
-    assert rel_l2(k_gpu[idx], kc[idx]) < TOL_BF16
+    assert_rows_close(k_gpu[idx], kc[idx], TOL_BF16, "K rows")
+    assert_rows_close(host(m.blocks[0]["v_cache"])[idx], vc[idx], TOL_BF16, "V rows")
     skipped = np.setdiff1d(np.arange(c.N), idx)[::97]
     np.testing.assert_array_equal(k_gpu[skipped], kc[skipped])
 
