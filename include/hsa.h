@@ -10,7 +10,8 @@
  *
  * Conventions shared by every call:
  *  - Pointers are DEVICE pointers unless marked (host).  The caller owns every
- *    buffer; the library allocates nothing and keeps no global state.
+ *    buffer; the library allocates nothing and keeps no global state, except
+ *    for the fixed device array of hsa_attn_active_noalloc (at the end).
  *  - `stream` is a hipStream_t passed as void* (NULL = default stream).  Calls
  *    enqueue work on it and return before the work completes.
  *  - Arguments are validated on the host before anything is enqueued.  An
@@ -44,7 +45,8 @@ typedef enum {
   HSA_ERR_ALIGN = -4,     /* a device pointer is not 16-byte aligned        */
   HSA_ERR_WORKSPACE = -5, /* workspace missing or smaller than required     */
   HSA_ERR_HIP = -6,       /* a HIP runtime call failed                      */
-  HSA_ERR_SCHEDULE = -7   /* budgets do not divide T, counts do not sum to N */
+  HSA_ERR_SCHEDULE = -7,  /* budgets do not divide T, counts do not sum to N */
+  HSA_ERR_TOO_LARGE = -8  /* needs more than HSA_NOALLOC_SCRATCH_BYTES       */
 } hsa_status;
 
 typedef enum { HSA_F32 = 0, HSA_BF16 = 1 } hsa_dtype;
@@ -162,7 +164,7 @@ const char *hsa_status_str(int32_t status);
 
 /* Library ABI version (increments when a signature or struct changes); a
  * library built from this header returns HSA_ABI_VERSION. */
-#define HSA_ABI_VERSION 3
+#define HSA_ABI_VERSION 4
 int32_t hsa_abi_version(void);
 
 /* Workspace needed by hsa_step / hsa_block_forward for these dims (host out). */
@@ -318,6 +320,24 @@ hsa_status hsa_block_forward(const hsa_model *model, int32_t layer, float *h,
 hsa_status hsa_step(const hsa_model *model, const hsa_schedule *sched, hsa_state *state,
                     int32_t iter, float sigma_i, float sigma_next, int32_t regroup,
                     const float *v_field, void *stream);
+
+/* Allocation-free active-query attention, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Computes exactly what hsa_attn_active
+ * computes, with the same kernels, arguments and results, but takes no
+ * workspace: the KV-split partials (hsa_attn_workspace_size() bytes) live in
+ * a fixed device array of HSA_NOALLOC_SCRATCH_BYTES that each GPU holds from
+ * the library's load until the process ends.  A call that would need more
+ * returns HSA_ERR_TOO_LARGE and enqueues nothing (use hsa_attn_active with a
+ * workspace then).  The call never allocates or frees memory; its first call
+ * on a device looks up that device's array address (the stream's device
+ * must be current).  All calls on one GPU share its array: calls that
+ * overlap on one GPU (other streams, other threads) race, so serialise
+ * them. */
+#define HSA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+hsa_status hsa_attn_active_noalloc(const void *q, const void *k, const void *v, void *o,
+                                   int32_t n_active, int32_t n_kv, int32_t H, int32_t Dh,
+                                   float scale, hsa_dtype dtype, void *stream);
 
 #ifdef __cplusplus
 }

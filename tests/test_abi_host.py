@@ -40,8 +40,28 @@ def test_abi_version_matches_header_and_binding():
 
 
 def test_status_strings():
-    for code in (0, -1, -2, -3, -4, -5, -6, -7, 99):
+    for code in (0, -1, -2, -3, -4, -5, -6, -7, -8, 99):
         assert H.status_str(code)
+
+
+def test_noalloc_attention_validates_on_the_host():
+    """The allocation-free attention entry point checks its arguments and its
+    scratch limit before any HIP call: a problem whose KV-split partials
+    exceed HSA_NOALLOC_SCRATCH_BYTES returns HSA_ERR_TOO_LARGE (-8)."""
+    text = open(HEADER).read()
+    assert int(eval(re.search(r"#define HSA_NOALLOC_SCRATCH_BYTES (.+)", text).group(1)
+                    .replace("(size_t)", ""))) == H.NOALLOC_SCRATCH_BYTES
+    L = H.load()
+    fake = 4096                                  # aligned, never dereferenced on these paths
+    nA, nkv, Hh, Dh = 2048, 75600, 40, 128       # 82.5 MiB of partials
+    assert H.hsa_attn_workspace_size(nA, nkv, Hh, Dh) > H.NOALLOC_SCRATCH_BYTES
+    assert L.hsa_attn_active_noalloc(fake, fake, fake, fake, nA, nkv, Hh, Dh, 0.088, 1, None) == -8
+    assert L.hsa_attn_active_noalloc(None, fake, fake, fake, 8, 64, 2, 128, 0.088, 1, None) == -1
+    assert L.hsa_attn_active_noalloc(fake + 2, fake, fake, fake, 8, 64, 2, 128, 0.088, 1, None) == -4
+    assert L.hsa_attn_active_noalloc(fake, fake, fake, fake, 8, 64, 2, 96, 0.088, 1, None) == -2
+    assert L.hsa_attn_active_noalloc(fake, fake, fake, fake, 8, 64, 2, 128, -1.0, 1, None) == -1
+    assert L.hsa_attn_active_noalloc(fake, fake, fake, fake, 0, 64, 2, 128, 0.088, 1, None) == 0
+    assert "HSA_NOALLOC_SCRATCH_BYTES" in H.status_str(-8)
 
 
 def test_workspace_size_validation():

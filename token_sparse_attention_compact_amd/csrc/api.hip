@@ -271,6 +271,9 @@ const char* hsa_status_str(int32_t status) {
     case HSA_ERR_WORKSPACE: return "workspace missing or too small";
     case HSA_ERR_HIP: return "HIP runtime error";
     case HSA_ERR_SCHEDULE: return "invalid schedule (budgets must divide T, budget[0] == T, counts sum to N)";
+    case HSA_ERR_TOO_LARGE:
+      return "problem needs more scratch than the allocation-free entry point's fixed array "
+             "(HSA_NOALLOC_SCRATCH_BYTES); call the entry point that takes a workspace";
     default: return "unknown status";
   }
 }

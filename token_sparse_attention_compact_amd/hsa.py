@@ -21,7 +21,8 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "lib
 
 HSA_F32, HSA_BF16 = 0, 1
 MAX_GROUPS = 8
-ABI_VERSION = 3
+ABI_VERSION = 4
+NOALLOC_SCRATCH_BYTES = 64 << 20   # HSA_NOALLOC_SCRATCH_BYTES
 # optional block features (hsa_dims.features)
 FEAT_QK_NORM, FEAT_ROPE3D, FEAT_ADALN, FEAT_CFG = 1, 2, 4, 8
 FEATURE_BITS = {"qk_norm": FEAT_QK_NORM, "rope3d": FEAT_ROPE3D, "adaln": FEAT_ADALN, "cfg": FEAT_CFG}
@@ -32,7 +33,7 @@ EXPORTED = [
     "hsa_euler",
     "hsa_attn_active", "hsa_layernorm", "hsa_embed", "hsa_unembed", "hsa_linear",
     "hsa_linear_residual", "hsa_qkv_scatter", "hsa_qk_norm_rope", "hsa_time_embed", "hsa_guidance",
-    "hsa_block_forward", "hsa_step",
+    "hsa_block_forward", "hsa_step", "hsa_attn_active_noalloc",
 ]
 
 
@@ -108,6 +109,7 @@ def load() -> ct.CDLL:
         "hsa_select_batch": ([P, I, I, PI, I, P, P], I),
         "hsa_euler": ([P, P, P, P, P, I, I, F, F, I, P], I),
         "hsa_attn_active": ([P, P, P, P, I, I, I, I, F, ct.c_int, P, S, P], I),
+        "hsa_attn_active_noalloc": ([P, P, P, P, I, I, I, I, F, ct.c_int, P], I),
         "hsa_layernorm": ([P, P, I, I, P, P, ct.c_int, P], I),
         "hsa_embed": ([P, P, P, P, I, I, I, ct.c_int, P], I),
         "hsa_unembed": ([P, P, P, I, I, I, P, P, ct.c_int, P], I),
@@ -296,6 +298,26 @@ def hsa_attn_active(q, k, v, o, H: int, Dh: int, scale: Optional[float] = None,
     wsb = 0 if ws is None else ws.numel() * ws.element_size()
     _check("hsa_attn_active", load().hsa_attn_active(_ptr(q), _ptr(k), _ptr(v), _ptr(o), nA, nkv, H, Dh,
                                                      scale, dt, _ptr(ws), wsb, _stream(stream)))
+
+
+def hsa_attn_active_noalloc(q, k, v, o, H: int, Dh: int, scale: Optional[float] = None,
+                            stream=None):
+    """hsa_attn_active without a workspace: the library's fixed per-device
+    array holds the KV-split partials (nothing is allocated, here or in the
+    library).  Calls that overlap on one GPU race on that array."""
+    dt = _dt(q)
+    for t in (k, v, o):
+        _need(t, q.dtype, "k/v/o")
+    nA, nkv = q.shape[0], k.shape[0]
+    _shape(q, (nA, H * Dh), "q")
+    _shape(k, (nkv, H * Dh), "k")
+    _shape(v, (nkv, H * Dh), "v")
+    _shape(o, (nA, H * Dh), "o")
+    if scale is None:
+        scale = Dh ** -0.5
+    _check("hsa_attn_active_noalloc",
+           load().hsa_attn_active_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), nA, nkv, H, Dh, scale,
+                                          dt, _stream(stream)))
 
 
 def _mod_pair(shift, scale, D: int, name: str):
