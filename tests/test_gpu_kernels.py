@@ -323,6 +323,35 @@ def test_layernorm_embed_unembed(dtype):
     assert rel_l2(host(vn), O.layer_norm(h) @ w_out.T.astype(np.float64)) < 1e-5
 
 
+@pytest.mark.parametrize("D", [128, 256, 1536, 2048, 5120])
+@pytest.mark.parametrize("rows", [1, 17, 8190])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_embed_unembed_widths(D, rows, dtype):
+    """Gather + embed (weights held per thread across a block of rows) and
+    final LayerNorm + unembed (weights in LDS as float32 when D <= 2048 and D is
+    a multiple of 256; the two-pass kernel otherwise), C = 16, row counts
+    that leave partial blocks, every row within tolerance."""
+    rs = np.random.default_rng(D + rows)
+    C, N = 16, max(2 * rows, 64)
+    x = rs.standard_normal((N, C)).astype(np.float32)
+    w_in = rs.standard_normal((D, C)).astype(np.float32) / 4
+    w_out = rs.standard_normal((C, D)).astype(np.float32) * D ** -0.5
+    if dtype == torch.bfloat16:
+        w_in, w_out = bf(w_in), bf(w_out)
+    idx = np.sort(rs.choice(N, rows, replace=False)).astype(np.int32)
+    th = torch.full((rows + 1, D), 5.0, device=DEV)     # one sentinel row past the end
+    H.hsa_embed(dev(x), dev(idx, torch.int32), rows, dev(w_in, dtype), th[:rows])
+    assert_rows_close(host(th)[:rows], x[idx].astype(np.float64) @ w_in.T.astype(np.float64), 1e-6,
+                      "embed rows")
+    assert torch.all(th[rows] == 5.0)
+    h = (rs.standard_normal((rows, D)) * 2 + 0.5).astype(np.float32)
+    vn = torch.full((rows + 1, C), 5.0, device=DEV)
+    H.hsa_unembed(dev(h), dev(w_out, dtype), vn[:rows], rows)
+    assert_rows_close(host(vn)[:rows], O.layer_norm(h) @ w_out.T.astype(np.float64), 1e-5,
+                      "unembed rows")
+    assert torch.all(vn[rows] == 5.0)
+
+
 @pytest.mark.parametrize("D", [128, 256, 1536, 2000, 5120])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_layernorm_widths(D, dtype):
@@ -343,9 +372,10 @@ def test_layernorm_widths(D, dtype):
                                    (1000, 1536, 1536),
                                    # each tile shape the library picks, ragged in M and N:
                                    # 256x256 (4000 x 4000), 128x192 (2100 x 4000, 1100 x 4000),
-                                   # 128x128 (1000 x 4000), 128x64 with long K (1030 x 300)
+                                   # 128x128 (1000 x 4000, short and long K), 128x64 with
+                                   # long K (1030 x 300)
                                    (4000, 4000, 128), (2100, 4000, 128), (1100, 4000, 128),
-                                   (1000, 4000, 128), (1030, 300, 4160)])
+                                   (1000, 4000, 128), (1000, 4000, 4160), (1030, 300, 4160)])
 def test_linear_bf16(M, N, K):
     say(f"linear bf16 M={M} N={N} K={K}")
     rs = np.random.default_rng(M * 7 + N + K)

@@ -1,13 +1,17 @@
 // Row operations on the active rows: LayerNorm (pre-norm of every sub-layer),
 // gather + embed of the active latents (the active rows enter the model,
 // section 2.2 item 1) and final LayerNorm + unembed to the velocity.
-// All three are bandwidth-bound; one 64-wide wavefront per row with float4
-// accesses.  LayerNorm keeps the row in registers when D is a multiple of
+// All three are bandwidth-bound.  LayerNorm: one 64-wide wavefront per row
+// with float4 accesses, the row kept in registers when D is a multiple of
 // 256 (one read of the row from memory, statistics in float32 from the
-// registers); otherwise, and in unembed, the statistics take two passes.
+// registers), two passes otherwise.  Embed keeps each thread's weights in
+// registers across a block of rows; unembed keeps w_out in LDS and two rows
+// per wavefront in registers (other shapes: two passes per row).
 // LayerNorm and unembed optionally apply the timestep modulation
 // LN(h) (1 + scale) + shift (MOD template flag; shift and scale are [D]
 // vectors read as float4 from L2, the same for every row).
+#include <type_traits>
+
 #include "common.h"
 
 namespace hsa {
@@ -168,38 +172,221 @@ __global__ __launch_bounds__(256) void embed_kernel(const float* __restrict__ x,
   h[t] = acc;
 }
 
-// C == 16: each lane produces 4 consecutive outputs of one row from the
-// latent row (4 x float4, shared by the row's lanes through the cache) and
-// four 16-channel weight rows, so the pass is a handful of vector loads per
-// output quad instead of 32 scalar loads per output.
+// C == 16: a thread owns 4 consecutive output columns and keeps their 4 x 16
+// weights in registers for every row of its block.  The block's latent rows
+// x[idx[j]] are gathered into LDS first (one round of loads for the block),
+// so the row loop is 64 FMAs and one 16-byte store per output quad.
+constexpr int kEmbedRows = 32;     // rows per block
+constexpr int kEmbedThreads = 128; // output quads per block
 template <typename WT>
-__global__ __launch_bounds__(256) void embed_kernel_c16(const float* __restrict__ x,
-                                                        const int32_t* __restrict__ idx,
-                                                        const WT* __restrict__ w_in,
-                                                        float* __restrict__ h, int32_t rows,
-                                                        int32_t D) {
-  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int32_t quads = D / 4;
-  if (t >= (int64_t)rows * quads) return;
-  const int32_t j = (int32_t)(t / quads), d0 = (int32_t)(t % quads) * 4;
-  const f32x4* xr = reinterpret_cast<const f32x4*>(x + (size_t)idx[j] * 16);
-  float xv[16];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const f32x4 v = xr[i];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) xv[4 * i + e] = v[e];
+__global__ __launch_bounds__(kEmbedThreads) void embed_kernel_c16(const float* __restrict__ x,
+                                                                  const int32_t* __restrict__ idx,
+                                                                  const WT* __restrict__ w_in,
+                                                                  float* __restrict__ h,
+                                                                  int32_t rows, int32_t D) {
+  __shared__ f32x4 sx[kEmbedRows][4];
+  const int32_t r0 = blockIdx.x * kEmbedRows;
+  const int32_t nr = min(rows - r0, kEmbedRows);
+  {
+    const int t = threadIdx.x;   // 128 threads: row t/4, chunk t%4
+    if (t / 4 < nr)
+      sx[t / 4][t % 4] = reinterpret_cast<const f32x4*>(x + (size_t)idx[r0 + t / 4] * 16)[t % 4];
   }
-  f32x4 out;
+  const int32_t q = blockIdx.y * kEmbedThreads + threadIdx.x;   // columns 4q .. 4q+3
+  const bool col_ok = 4 * q < D;
+  float w[4][16];
 #pragma unroll
-  for (int o = 0; o < 4; ++o) {
-    const WT* wr = w_in + (size_t)(d0 + o) * 16;
-    float acc = 0.f;
+  for (int o = 0; o < 4; ++o)
 #pragma unroll
-    for (int c = 0; c < 16; ++c) acc = __builtin_fmaf(xv[c], to_f32(wr[c]), acc);
-    out[o] = acc;
+    for (int c = 0; c < 16; ++c) w[o][c] = 0.f;
+  if (col_ok) {
+    // the 4 weight rows are 64 consecutive values: 16-byte loads
+    constexpr int kPer = 16 / (int)sizeof(WT);
+    const u32x4* wr = reinterpret_cast<const u32x4*>(w_in + (size_t)4 * q * 16);
+#pragma unroll
+    for (int i = 0; i < 64 / kPer; ++i) {
+      const u32x4 raw = wr[i];
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) {
+        const int f = i * kPer + e;
+        if constexpr (sizeof(WT) == 2) {
+          const uint32_t word = raw[e >> 1];
+          w[f >> 4][f & 15] = __uint_as_float((e & 1) ? (word & 0xffff0000u) : (word << 16));
+        } else {
+          w[f >> 4][f & 15] = __uint_as_float(raw[e]);
+        }
+      }
+    }
   }
-  *reinterpret_cast<f32x4*>(h + (size_t)j * D + d0) = out;
+  __syncthreads();
+  if (!col_ok) return;
+  for (int32_t j = 0; j < nr; ++j) {
+    float xv[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x4 v = sx[j][i];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) xv[4 * i + e] = v[e];
+    }
+    f32x4 out;
+#pragma unroll
+    for (int o = 0; o < 4; ++o) {
+      float acc = 0.f;
+#pragma unroll
+      for (int c = 0; c < 16; ++c) acc = __builtin_fmaf(xv[c], w[o][c], acc);
+      out[o] = acc;
+    }
+    *reinterpret_cast<f32x4*>(h + (size_t)(r0 + j) * D + 4 * q) = out;
+  }
+}
+
+template <int O, int HALF>
+__device__ __forceinline__ void reduce_halve(float (&a)[16], int lane) {
+  const bool hi = (lane & O) != 0;
+#pragma unroll
+  for (int c = 0; c < HALF; ++c) {
+    const float keep = hi ? a[c + HALF] : a[c];
+    const float send = hi ? a[c] : a[c + HALF];
+    a[c] = keep + __shfl_xor(send, O, kWave);
+  }
+}
+__device__ __forceinline__ float reduce16(float (&a)[16], int lane) {
+  reduce_halve<32, 8>(a, lane);
+  reduce_halve<16, 4>(a, lane);
+  reduce_halve<8, 2>(a, lane);
+  reduce_halve<4, 1>(a, lane);
+  float t = a[0];
+  t += __shfl_xor(t, 2, kWave);
+  t += __shfl_xor(t, 1, kWave);
+  return t;
+}
+
+// C == 16, D = 256 NV: the block copies w_out [16][D] into LDS once (as
+// float32, so the FMAs read it without conversions; D <= 2048); each
+// of its 8 wavefronts then takes rows one at a time, held in registers (lane
+// l: float4 chunks l, l+64, ...) with the next row's load in flight:
+// statistics, normalisation and modulation there, the 16 dot products
+// against the LDS weights, reduced with reduce16.
+constexpr int kUnembedRows = 32;     // rows per block
+constexpr int kUnembedWaves = 8;
+template <typename WT, int NV, bool MOD>
+__global__ __launch_bounds__(kUnembedWaves * kWave) void unembed_c16_reg_kernel(
+    const float* __restrict__ h, const WT* __restrict__ w_out, float* __restrict__ v_new,
+    int32_t rows, ModVec shift, ModVec scale) {
+  constexpr int D = NV * 4 * kWave;
+  __shared__ __attribute__((aligned(16))) float sw[16 * D];   // w_out as float32
+  {
+    // every 16-byte load of the weights issued before the first conversion
+    constexpr int kPer = 16 / (int)sizeof(WT);                  // weights per load
+    constexpr int kThreads = kUnembedWaves * kWave;
+    constexpr int kLoads = (16 * D / kPer + kThreads - 1) / kThreads;
+    const u32x4* src = reinterpret_cast<const u32x4*>(w_out);
+    u32x4 raw[kLoads];
+#pragma unroll
+    for (int k = 0; k < kLoads; ++k) {
+      const int i = threadIdx.x + k * kThreads;
+      if (i < 16 * D / kPer) raw[k] = src[i];
+    }
+#pragma unroll
+    for (int k = 0; k < kLoads; ++k) {
+      const int i = threadIdx.x + k * kThreads;
+      if (i < 16 * D / kPer) {
+        if constexpr (sizeof(WT) == 2) {
+          f32x4 lo, hi;
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            lo[2 * e] = __uint_as_float(raw[k][e] << 16);
+            lo[2 * e + 1] = __uint_as_float(raw[k][e] & 0xffff0000u);
+            hi[2 * e] = __uint_as_float(raw[k][2 + e] << 16);
+            hi[2 * e + 1] = __uint_as_float(raw[k][2 + e] & 0xffff0000u);
+          }
+          reinterpret_cast<f32x4*>(sw)[2 * i] = lo;
+          reinterpret_cast<f32x4*>(sw)[2 * i + 1] = hi;
+        } else {
+          reinterpret_cast<u32x4*>(sw)[i] = raw[k];
+        }
+      }
+    }
+  }
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int32_t r1 = min(rows, (int32_t)(blockIdx.x + 1) * kUnembedRows);
+  int32_t row = blockIdx.x * kUnembedRows + wave;
+  f32x4 nxt[NV];
+  auto load_row = [&](int32_t r) {
+    const f32x4* hr = reinterpret_cast<const f32x4*>(h + (size_t)r * D);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) nxt[i] = hr[lane + kWave * i];
+  };
+  if (row < r1) load_row(row);
+  __syncthreads();
+  for (; row < r1; row += kUnembedWaves) {
+    f32x4 v[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) v[i] = nxt[i];
+    if (row + kUnembedWaves < r1) load_row(row + kUnembedWaves);
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) s += (v[i][0] + v[i][1]) + (v[i][2] + v[i][3]);
+    const float mean = wave_sum(s) / (float)D;
+    float q = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float d = v[i][e] - mean;
+        q += d * d;
+      }
+    const float rstd = 1.0f / sqrtf(wave_sum(q) / (float)D + kLnEps);
+    float acc[16];
+#pragma unroll
+    for (int c = 0; c < 16; ++c) acc[c] = 0.f;
+    // A real loop over the row's chunks (v rotated down one chunk per pass),
+    // so that the compiler issues one chunk's 16 weight reads at a time
+    // instead of hoisting all of them.
+#pragma unroll 1
+    for (int i = 0; i < NV; ++i) {
+      const int col = 4 * (lane + kWave * i);
+      f32x4 n;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) n[e] = (v[0][e] - mean) * rstd;
+#pragma unroll
+      for (int k = 0; k + 1 < NV; ++k) v[k] = v[k + 1];
+      n = modulate4<MOD>(n, shift, scale, lane + kWave * i);
+#pragma unroll
+      for (int c = 0; c < 16; ++c) {
+        const f32x4 w = *reinterpret_cast<const f32x4*>(sw + c * D + col);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[c] = __builtin_fmaf(n[e], w[e], acc[c]);
+      }
+    }
+    const float sum = reduce16(acc, lane);
+    if ((lane & 3) == 0) v_new[(size_t)row * 16 + ((lane >> 2) & 15)] = sum;
+  }
+}
+
+template <typename WT, bool MOD>
+bool launch_unembed_reg(const float* h, const WT* w_out, float* v_new, int32_t rows, int32_t D,
+                        ModVec shift, ModVec scale, hipStream_t s) {
+  if (D % (4 * kWave) != 0 || 16 * D * (int64_t)sizeof(float) > 128 * 1024) return false;
+  const unsigned blocks = (unsigned)cdiv(rows, kUnembedRows);
+  const int nv = D / (4 * kWave);
+  if (nv < 1 || nv > 8) return false;
+  auto launch = [&](auto nv_const) {
+    unembed_c16_reg_kernel<WT, decltype(nv_const)::value, MOD>
+        <<<blocks, kUnembedWaves * kWave, 0, s>>>(h, w_out, v_new, rows, shift, scale);
+  };
+  switch (nv) {
+    case 1: launch(std::integral_constant<int, 1>{}); break;
+    case 2: launch(std::integral_constant<int, 2>{}); break;
+    case 3: launch(std::integral_constant<int, 3>{}); break;
+    case 4: launch(std::integral_constant<int, 4>{}); break;
+    case 5: launch(std::integral_constant<int, 5>{}); break;
+    case 6: launch(std::integral_constant<int, 6>{}); break;
+    case 7: launch(std::integral_constant<int, 7>{}); break;
+    default: launch(std::integral_constant<int, 8>{}); break;
+  }
+  return true;
 }
 
 // v_new[j][c] = sum_d LN(h[j])[d] * w_out[c][d], C == CC known at compile time.
@@ -288,6 +475,11 @@ void unembed_dispatch(const float* h, const void* w_out, float* v_new, int32_t r
                       int32_t C, hsa_dtype dt, ModVec shift, ModVec scale, hipStream_t s) {
   const int blocks = cdiv(rows, kRowsPerBlock);
   if (C == 16) {
+    if (dt == HSA_BF16 ? launch_unembed_reg<bf16, MOD>(h, (const bf16*)w_out, v_new, rows, D, shift,
+                                                       scale, s)
+                       : launch_unembed_reg<float, MOD>(h, (const float*)w_out, v_new, rows, D,
+                                                        shift, scale, s))
+      return;
     if (dt == HSA_BF16)
       unembed_kernel<bf16, 16, MOD><<<blocks, 256, 0, s>>>(h, (const bf16*)w_out, v_new, rows, D,
                                                            shift, scale);
@@ -320,12 +512,11 @@ hsa_status launch_embed(const float* x, const int32_t* idx, const void* w_in, fl
                         int32_t rows, int32_t C, int32_t D, hsa_dtype dt, hipStream_t s) {
   if (rows == 0) return HSA_OK;
   if (C == 16 && D % 4 == 0) {
-    const int64_t total = (int64_t)rows * (D / 4);
-    const unsigned blocks = (unsigned)((total + 255) / 256);
+    const dim3 grid((unsigned)cdiv(rows, kEmbedRows), (unsigned)cdiv(D / 4, kEmbedThreads));
     if (dt == HSA_BF16)
-      embed_kernel_c16<bf16><<<blocks, 256, 0, s>>>(x, idx, (const bf16*)w_in, h, rows, D);
+      embed_kernel_c16<bf16><<<grid, kEmbedThreads, 0, s>>>(x, idx, (const bf16*)w_in, h, rows, D);
     else
-      embed_kernel_c16<float><<<blocks, 256, 0, s>>>(x, idx, (const float*)w_in, h, rows, D);
+      embed_kernel_c16<float><<<grid, kEmbedThreads, 0, s>>>(x, idx, (const float*)w_in, h, rows, D);
     return launch_status();
   }
   const int64_t total = (int64_t)rows * D;
