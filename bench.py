@@ -45,6 +45,9 @@ import synth  # noqa: E402
 METRIC = "active-query attn TFLOP/s + HSA iterations/s at N=32760, 25% active (1 GPU)"
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
+MALL_BYTES = 256 << 20          # Infinity Cache: passes below 4x this are partly cache-resident
+# copy probe launch shapes: (16-byte loads per thread in flight, workgroup cap; 0 = uncapped)
+COPY_VARIANTS = ((4, 8192), (4, 0), (8, 0), (16, 0), (8, 2048))
 ITER = 11
 
 
@@ -130,22 +133,28 @@ def attainable_peaks(reps: int = 3):
     src = torch.ones(256 << 20, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
     nbytes = src.numel() * 4
-    copy = lambda: lib.hsa_probe_copy(ct.c_void_p(src.data_ptr()), ct.c_void_p(dst.data_ptr()),
-                                      ct.c_int64(nbytes), stream)
-    assert copy() == 0
-    torch.cuda.synchronize()
-    s.record()
-    for _ in range(reps):
+    best = None
+    for per_thread, max_blocks in COPY_VARIANTS:
+        copy = lambda: lib.hsa_probe_copy(ct.c_void_p(src.data_ptr()), ct.c_void_p(dst.data_ptr()),
+                                          ct.c_int64(nbytes), per_thread, max_blocks, stream)
         assert copy() == 0
-    e.record()
-    torch.cuda.synchronize()
-    t = s.elapsed_time(e) / 1e3 / reps
-    assert torch.equal(src[:1024], dst[:1024]) and torch.equal(src[-1024:], dst[-1024:])
-    copy_gbs = 2 * src.numel() * 4 / t / 1e9
+        torch.cuda.synchronize()
+        s.record()
+        for _ in range(reps):
+            assert copy() == 0
+        e.record()
+        torch.cuda.synchronize()
+        t = s.elapsed_time(e) / 1e3 / reps
+        assert torch.equal(src[:1024], dst[:1024]) and torch.equal(src[-1024:], dst[-1024:])
+        gbs = 2 * nbytes / t / 1e9
+        if best is None or gbs > best[0]:
+            best = (gbs, per_thread, max_blocks)
     del src, dst, out
-    return {"mfma_bf16_tflops": round(mfma_tflops, 1), "copy_gbs": round(copy_gbs, 1),
+    return {"mfma_bf16_tflops": round(mfma_tflops, 1), "copy_gbs": round(best[0], 1),
+            "copy_variant": {"loads_per_thread": best[1], "max_blocks": best[2] or "uncapped"},
             "probe": "MFMA-only loop, 1024 workgroups x 8 waves x 64000 MFMAs; 1 GiB streaming copy "
-                     "(16-byte non-temporal accesses), read + write bytes"}
+                     "(16-byte non-temporal accesses, read + write bytes), best of "
+                     f"{len(COPY_VARIANTS)} launch shapes"}
 
 
 def time_euler(H, n_tokens: int, C: int = 16, frac: float = 0.25, reps: int = 10):
@@ -207,8 +216,12 @@ def hbm_sweep(H, copy_gbs=None):
     video, 0.16 MB, is latency-bound and cache-resident)."""
     out = {"euler": [time_euler(H, n) for n in (32760, 1 << 20, 1 << 22, 1 << 24, 24 << 20)],
            "select_batch": [time_select_batch(H, b) for b in (1, 64, 512, 2048, 8192)]}
-    if copy_gbs:
-        for r in out["euler"] + out["select_batch"]:
+    for r in out["euler"] + out["select_batch"]:
+        # HBM fractions only where the working set is >= 4x the Infinity Cache
+        if r["bytes"] < 4 * MALL_BYTES:
+            r["cache_resident_part"] = True
+            del r["frac_of_hbm_peak"]
+        elif copy_gbs:
             r["frac_of_attainable_copy"] = round(r["gbs"] / copy_gbs, 4)
     return out
 

@@ -194,8 +194,10 @@ def test_probe_library_exports():
     lib = ct.CDLL(B.PROBE_LIB)
     for name in ("hsa_probe_mfma_peak", "hsa_probe_copy"):
         assert hasattr(lib, name)
-    lib.hsa_probe_copy.argtypes = [ct.c_void_p, ct.c_void_p, ct.c_int64, ct.c_void_p]
-    assert lib.hsa_probe_copy(None, None, 1024, None) == -1          # rejected before any launch
+    lib.hsa_probe_copy.argtypes = [ct.c_void_p, ct.c_void_p, ct.c_int64, ct.c_int32, ct.c_int32,
+                                   ct.c_void_p]
+    assert lib.hsa_probe_copy(None, None, 1024, 4, 0, None) == -1    # rejected before any launch
+    assert lib.hsa_probe_copy(4096, 8192, 1024, 5, 0, None) == -1     # unsupported loads per thread
     assert lib.hsa_probe_mfma_peak(0, 10, None, None) == -1
 
 
@@ -282,3 +284,51 @@ def test_header_and_library_from_plain_c(tmp_path):
     assert r.returncode == 0, r.stderr
     r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
     assert r.returncode == 0 and "c abi ok" in r.stdout, (r.returncode, r.stdout, r.stderr)
+
+
+# Sanitizers for the host side only: each flag sits directly after -Xarch_host,
+# so the device code is compiled as usual and no GPU sanitizer is involved.
+HOST_SANITIZERS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                   "-Xarch_host", "-fno-sanitize-recover=all"]
+
+
+def test_host_validation_under_sanitizers(tmp_path):
+    """The library's host code (argument validation, workspace layout, launch
+    sequencing) built with AddressSanitizer and UndefinedBehaviorSanitizer,
+    and tests/c_abi_check.c (every entry point family called with invalid
+    arguments, plus the host-only calls) built with both and run against it:
+    no sanitizer report, every call returns its documented status."""
+    import concurrent.futures as cf
+    import shutil
+    import subprocess
+    from token_sparse_attention_compact_amd import build as B
+    clang = "/opt/rocm/llvm/bin/clang"
+    if not os.path.exists(clang):
+        pytest.skip("ROCm clang not found")
+    cc = B.hipcc()
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    flags = [f for f in B.FLAGS if f != "-O3"] + ["-O1", "-g"]
+
+    def compile_one(src):
+        obj = str(tmp_path / (os.path.basename(src) + ".o"))
+        cmd = [cc, *flags, *HOST_SANITIZERS, "-c", src, "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        assert r.returncode == 0, r.stdout + r.stderr
+        return obj
+
+    with cf.ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 4)) as ex:
+        objs = list(ex.map(compile_one, B.sources()))
+    lib = str(tmp_path / "libhsa_san.so")
+    r = subprocess.run([cc, "-shared", "-fPIC", f"--offload-arch={B.ARCH}", *objs, "-o", lib],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    exe = str(tmp_path / "c_abi_san")
+    san_c = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all"]
+    r = subprocess.run([clang, "-std=c99", "-g", *san_c, "-I", os.path.join(root, "include"),
+                        os.path.join(root, "tests", "c_abi_check.c"), lib,
+                        f"-Wl,-rpath,{tmp_path}", "-o", exe], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0", UBSAN_OPTIONS="print_stacktrace=1")
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120, env=env)
+    assert r.returncode == 0 and "c abi ok" in r.stdout, (r.returncode, r.stdout, r.stderr[-3000:])
+    assert "runtime error" not in r.stderr and "AddressSanitizer" not in r.stderr, r.stderr[-3000:]

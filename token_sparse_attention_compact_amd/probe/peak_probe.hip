@@ -39,19 +39,21 @@ __global__ __launch_bounds__(512, 1) void mfma_peak_kernel(float* __restrict__ o
   out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
-// Each thread moves 4 x 16 bytes per round; rounds stride over the grid.
+// Each thread moves U x 16 bytes per round (all U loads issued before the
+// first store); rounds stride over the grid.
+template <int U>
 __global__ __launch_bounds__(256) void copy_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
                                                    int64_t n16) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x * 4;
-  for (int64_t i = ((int64_t)blockIdx.x * blockDim.x) * 4 + threadIdx.x; i < n16; i += stride) {
-    u32x4 v[4];
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x * U;
+  for (int64_t i = ((int64_t)blockIdx.x * blockDim.x) * U + threadIdx.x; i < n16; i += stride) {
+    u32x4 v[U];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < U; ++u) {
       const int64_t j = i + (int64_t)u * blockDim.x;
       if (j < n16) v[u] = __builtin_nontemporal_load(src + j);
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < U; ++u) {
       const int64_t j = i + (int64_t)u * blockDim.x;
       if (j < n16) __builtin_nontemporal_store(v[u], dst + j);
     }
@@ -70,16 +72,25 @@ extern "C" int hsa_probe_mfma_peak(int32_t n_wg, int32_t iters, float* out, void
 }
 
 // Copies n_bytes (a multiple of 16; both pointers 16-byte aligned) from src
-// to dst on the device.  Returns 0, or -1 on bad arguments / -6 on a launch
-// error.
-extern "C" int hsa_probe_copy(const void* src, void* dst, int64_t n_bytes, void* stream) {
+// to dst on the device, each thread moving per_thread (4, 8 or 16) x 16 bytes
+// per round, over at most max_blocks workgroups of 256 threads (0: as many as
+// one round over the whole copy needs).  Returns 0, or -1 on bad arguments /
+// -6 on a launch error.
+extern "C" int hsa_probe_copy(const void* src, void* dst, int64_t n_bytes, int32_t per_thread,
+                              int32_t max_blocks, void* stream) {
   if (src == nullptr || dst == nullptr || n_bytes <= 0 || n_bytes % 16 != 0 ||
-      ((uintptr_t)src | (uintptr_t)dst) % 16 != 0)
+      ((uintptr_t)src | (uintptr_t)dst) % 16 != 0 || max_blocks < 0 ||
+      (per_thread != 4 && per_thread != 8 && per_thread != 16))
     return -1;
   const int64_t n16 = n_bytes / 16;
-  const int64_t per_block = 256 * 4;
-  const int64_t blocks = (n16 + per_block - 1) / per_block;
-  const unsigned grid = (unsigned)(blocks < 256 * 32 ? blocks : 256 * 32);
-  copy_kernel<<<grid, 256, 0, (hipStream_t)stream>>>((const u32x4*)src, (u32x4*)dst, n16);
+  const int64_t per_block = 256 * (int64_t)per_thread;
+  int64_t blocks = (n16 + per_block - 1) / per_block;
+  if (max_blocks > 0 && blocks > max_blocks) blocks = max_blocks;
+  if (blocks > 0x7fffffff) blocks = 0x7fffffff;
+  hipStream_t s = (hipStream_t)stream;
+  const unsigned grid = (unsigned)blocks;
+  if (per_thread == 4) copy_kernel<4><<<grid, 256, 0, s>>>((const u32x4*)src, (u32x4*)dst, n16);
+  else if (per_thread == 8) copy_kernel<8><<<grid, 256, 0, s>>>((const u32x4*)src, (u32x4*)dst, n16);
+  else copy_kernel<16><<<grid, 256, 0, s>>>((const u32x4*)src, (u32x4*)dst, n16);
   return hipGetLastError() == hipSuccess ? 0 : -6;
 }
