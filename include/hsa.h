@@ -49,7 +49,9 @@ typedef enum {
   HSA_ERR_TOO_LARGE = -8  /* needs more than HSA_NOALLOC_SCRATCH_BYTES       */
 } hsa_status;
 
-typedef enum { HSA_F32 = 0, HSA_BF16 = 1 } hsa_dtype;
+/* HSA_DTYPE_MAX_ENUM only widens the type: a caller may pass any int32 value
+ * and an unsupported one returns HSA_ERR_DTYPE (it is never a valid dtype). */
+typedef enum { HSA_F32 = 0, HSA_BF16 = 1, HSA_DTYPE_MAX_ENUM = 0x7fffffff } hsa_dtype;
 
 /* Optional block features, OR-ed into hsa_dims.features (0: none, the plain
  * block below).  The pages run HSA on Wan-family DiTs (section 4) but define
