@@ -313,7 +313,7 @@ __global__ __launch_bounds__(G::THREADS, G::MINB) void gemm_bf16_kernel(
       }
 }
 
-// Three tile shapes, chosen per GEMM shape (pick_cfg), all on the 16x16x32
+// Four tile shapes, chosen per GEMM shape (pick_cfg), all on the 16x16x32
 // MFMA.  Measured on MI355X with interleaved runs over 4 rotating weight sets
 // (TFLOP/s for QKV / out-projection / MLP up / MLP down, D 1536, FFN 8960):
 //  * 128x192, 8 waves of 32x96 (80 KiB LDS, two workgroups per CU):
@@ -328,9 +328,11 @@ __global__ __launch_bounds__(G::THREADS, G::MINB) void gemm_bf16_kernel(
 //    larger tiles for large M: M = 32760: 983 / 746 / 1046 / 1160 against
 //    1014 / 747 / 1017 / 1091 for 128x192;
 //  * 128x128, 8 waves of 32x64 (64 KiB, two per CU): the most tiles when M
-//    is small: M = 2048: 599 / 413 / 777 / 579 against 751 / 357 / 926 / 509.
-// 256x192 and 128x128 tiles of 32x32x16 MFMAs, 256x128, 64x192 and 128x64
-// tiles, 4-wave layouts and 3-4 stage rings measured slower.
+//    is small and the output is wide: M = 2048: 599 / 413 / 777 / 579
+//    against 751 / 357 / 926 / 509 (128x192 / 256x256 columns);
+//  * 128x64 (below): narrow outputs at small M.
+// 256x192 and 128x128 tiles of 32x32x16 MFMAs, 256x128, 64x192 tiles,
+// 4-wave layouts and 3-4 stage rings measured slower.
 typedef GemmCfg<256, 256, 4, 2, 2, 4, 1, 16> CfgWide;
 typedef GemmCfg<128, 192, 4, 2, 2, 4, 2, 16> CfgMain;
 typedef GemmCfg<128, 128, 4, 2, 2, 8, 2, 16> CfgSmall;
@@ -353,7 +355,10 @@ int32_t wide_group_rows(int32_t N) { return N > 2048 ? 2 : CfgWide::GM; }
 // Cost model: a CU works through ceil(tiles / 256) tiles of its shape one
 // after another (two co-resident workgroups share the CU's MFMA rate), so
 // time ~ ceil(tiles / 256) * tile area / relative efficiency.  Ties go to
-// the larger tile.
+// the larger tile.  Outside the model: M <= 2048 with N <= 2048 (the
+// out-projection and MLP down at <= 6.25% active) takes the 128x64 tile,
+// which the model would rank below 128x128 but measured 7-16% faster there
+// (more tiles for the chip; the measurements are at CfgTiny).
 int pick_cfg(int32_t M, int32_t N) {
   if (M <= 2048 && N <= 2048) return kCfgTiny;
   constexpr int64_t kCus = 256;
