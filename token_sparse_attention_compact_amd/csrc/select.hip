@@ -37,10 +37,11 @@ struct Counts {
 
 __device__ __forceinline__ uint32_t desc_key(float f) {
   uint32_t u = __float_as_uint(f);
-  if (f != f) u = 0x7f800000u;               // NaN ranks as +inf
-  if ((u & 0x7fffffffu) == 0u) u = 0u;       // -0 ranks as +0
-  const uint32_t asc = (u & 0x80000000u) ? ~u : (u | 0x80000000u);  // monotone in the score
-  return ~asc;                                // larger score -> smaller key
+  u = (f != f) ? 0x7f800000u : u;                  // NaN ranks as +inf
+  u = (u & 0x7fffffffu) == 0u ? 0u : u;            // -0 ranks as +0
+  // monotone in the score: flip every bit of negatives, the sign bit of the rest
+  const uint32_t asc = u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+  return ~asc;                                     // larger score -> smaller key
 }
 
 // Exclusive scan of one int per thread over the workgroup.
@@ -99,189 +100,414 @@ __device__ __forceinline__ void store_groups(uint8_t* out, int32_t n, int32_t N,
   }
 }
 
-template <int V>   // float4 loads per thread: rows of up to 4 * V * kThreads tokens
-__global__ __launch_bounds__(kThreads) void select_reg_kernel(const float* __restrict__ score,
-                                                              int32_t N, Counts cnt, int32_t nb,
-                                                              uint8_t* __restrict__ group_out) {
-  __shared__ int32_t hist[kMaxB][kBins];   // one per boundary in passes 2-3; pass 1 uses [0]
-  __shared__ int32_t wave_tmp[kWaves];
-  __shared__ int32_t tie_pre[V * kWaves];  // ties per (chunk j, wavefront), then their prefix
-  __shared__ uint32_t s_prefix[kMaxB];
-  __shared__ int32_t s_rem[kMaxB];
-  __shared__ int32_t s_size[kMaxB];
+constexpr int kV = 8;          // float4 loads per thread: rows of up to 4 * kV * kThreads tokens
+constexpr int kList = kThreads; // a bucket this small is copied to LDS and finished there
+constexpr int kCopies = 4;     // first-pass histogram copies (by lane % 4): fewer same-address atomics
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
+
+// 16-byte buffer loads of a row's raw score bits (zero past its 4N bytes),
+// thread t taking chunks t + 1024 j; 4-byte loads when the row is not
+// 16-byte aligned (a batch with N % 4 != 0).
+__device__ __forceinline__ void load_row_bits(const float* row, int32_t N, uint32_t (&raw)[kV][4]) {
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(row), 0, N * 4, 0x00020000);
   const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
-  const float* row = score + (size_t)blockIdx.x * N;
-  uint8_t* out = group_out + (size_t)blockIdx.x * N;
-  auto live = [&](int k) { return k < nb && cnt.bound[k] < N; };   // a boundary at N: none pass
-
-  for (int i = tid; i < kBins; i += kThreads) hist[0][i] = 0;
-  if (tid < kMaxB) {
-    s_prefix[tid] = 0u;
-    s_rem[tid] = (tid < nb) ? cnt.bound[tid] : 0;
-    s_size[tid] = 0;
-  }
-  __syncthreads();
-
-  // ---- the row into registers as keys, with the pass-1 histogram (bits 31..21)
-  uint32_t key[V][4];
   if ((reinterpret_cast<uintptr_t>(row) & 15u) == 0u) {
-    f32x4 raw[V];
 #pragma unroll
-    for (int j = 0; j < V; ++j) {
-      const int32_t n = 4 * (tid + j * kThreads);
-      if (n + 3 < N) raw[j] = *reinterpret_cast<const f32x4*>(row + n);
-    }
+    for (int j = 0; j < kV; ++j) {
+      const u32x4 v = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, 16 * (tid + j * kThreads), 0, 0));
 #pragma unroll
-    for (int j = 0; j < V; ++j) {
-      const int32_t n = 4 * (tid + j * kThreads);
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        key[j][e] = (n + 3 < N) ? desc_key(raw[j][e]) : (n + e < N ? desc_key(row[n + e]) : kPad);
+      for (int e = 0; e < 4; ++e) raw[j][e] = v[e];
     }
   } else {
 #pragma unroll
-    for (int j = 0; j < V; ++j) {
-      const int32_t n = 4 * (tid + j * kThreads);
+    for (int j = 0; j < kV; ++j)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) key[j][e] = (n + e < N) ? desc_key(row[n + e]) : kPad;
-    }
+      for (int e = 0; e < 4; ++e)
+        raw[j][e] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, 16 * (tid + j * kThreads) + 4 * e, 0, 0);
   }
-#pragma unroll
-  for (int j = 0; j < V; ++j)
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (key[j][e] != kPad) atomicAdd(&hist[0][key[j][e] >> 21], 1);
-  {
-    int32_t rem[kMaxB];
-#pragma unroll
-    for (int k = 0; k < kMaxB; ++k) rem[k] = __builtin_amdgcn_readfirstlane(s_rem[k]);
-    __syncthreads();
-    const int32_t h0 = hist[0][2 * tid], h1 = hist[0][2 * tid + 1];
-    int32_t tot;
-    const int32_t before = block_exclusive_scan(h0 + h1, wave_tmp, &tot);
-#pragma unroll
-    for (int k = 0; k < kMaxB; ++k)
-      if (live(k)) take_bucket(before, h0, h1, rem[k], 21, &s_prefix[k], &s_rem[k], &s_size[k]);
-    __syncthreads();
-  }
+}
 
-  // ---- passes 2 and 3 (bits 20..10, 9..0), every boundary in one sweep
+// One wavefront finishes a boundary from the list of its bucket's keys
+// (n <= kList entries; `fixed` the key bits the bucket shares, `lo` the
+// number still free): while more than 64 keys remain in the bucket, a digit
+// pass of up to 11 bits (histogram in `hist`, scanned by the wavefront: lane
+// l sums bins 32 l .. 32 l + 31); then the remaining keys are gathered into
+// `small` and ranked directly.  On return *prefix is the key t at the
+// boundary's rank and *rem the number of keys equal to t that rank before it.
+// Wavefront-local: LDS operations of one wavefront take effect in order.
+__device__ __forceinline__ void finish_bucket(const uint32_t* list, int32_t n, int32_t* hist,
+                                              uint32_t* small, uint32_t fixed, int lo,
+                                              uint32_t* prefix, int32_t* rem_io) {
+  // entries are read from LDS again in every pass: the wavefront's registers
+  // still hold its row's keys
+  constexpr int M = kList / kWave;   // list entries per lane
+  const int lane = threadIdx.x & (kWave - 1);
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  uint32_t pre = __builtin_amdgcn_readfirstlane(*prefix);
+  int32_t rem = __builtin_amdgcn_readfirstlane(*rem_io);
+  while (lo > 0) {   // lo == 0: every bit fixed, pre is t and rem its tie count
+    int32_t total = 0;
+    for (int m = 0; m < M; ++m) {
+      const int i = lane + kWave * m;
+      total += __popcll(__ballot(i < n && (list[i < n ? i : 0] & fixed) == pre));
+    }
+    if (total <= kWave) {   // gather the bucket's keys, one per lane, and rank them
+      int32_t at = 0;
+      for (int m = 0; m < M; ++m) {
+        const int i = lane + kWave * m;
+        const uint32_t c = list[i < n ? i : 0];
+        const bool in = i < n && (c & fixed) == pre;
+        const uint64_t bal = __ballot(in);
+        if (in) small[at + __popcll(bal & lt_mask)] = c;
+        at += __popcll(bal);
+      }
+      const uint32_t x = lane < total ? small[lane] : 0u;
+      int32_t less = 0, leq = 0;
+      for (int i = 0; i < total; ++i) {
+        const uint32_t y = small[i];
+        less += y < x ? 1 : 0;
+        leq += y <= x ? 1 : 0;
+      }
+      const bool hit = lane < total && less <= rem && rem < leq;   // x is the key at rank rem
+      const int src = __builtin_ctzll(__ballot(hit));               // some lane holds it
+      pre = (uint32_t)__shfl((int)x, src, kWave);
+      rem = rem - __shfl(less, src, kWave);
+      break;
+    }
+    const int width = lo < 11 ? lo : 11;
+    const int sh = lo - width;
+    const uint32_t dm = (1u << width) - 1u;
+    for (int i = 0; i < kBins / kWave; i += 4)
+      *reinterpret_cast<i32x4_t*>(&hist[32 * lane + i]) = i32x4_t{0, 0, 0, 0};
+    for (int m = 0; m < M; ++m) {
+      const int i = lane + kWave * m;
+      const uint32_t c = list[i < n ? i : 0];
+      if (i < n && (c & fixed) == pre) atomicAdd(&hist[(c >> sh) & dm], 1);
+    }
+    int32_t sum = 0;
+    for (int i = 0; i < kBins / kWave; i += 4) {
+      const i32x4_t v = *reinterpret_cast<const i32x4_t*>(&hist[32 * lane + i]);
+      sum += (v[0] + v[1]) + (v[2] + v[3]);
+    }
+    int32_t inc = sum;
 #pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-    const int sh = pass == 0 ? 10 : 0;
-    const uint32_t dm = pass == 0 ? 0x7ffu : 0x3ffu;
-    const uint32_t mask = pass == 0 ? 0xffe00000u : 0xfffffc00u;   // bits already fixed
-    uint32_t pre[kMaxB];
-    int32_t rem[kMaxB];
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int32_t y = __shfl_up(inc, o, kWave);
+      if (lane >= o) inc += y;
+    }
+    const int32_t excl = inc - sum;
+    const bool mine = excl <= rem && rem < inc;   // exactly one lane's bins hold rank rem
+    int32_t digit = 0, left = rem - excl;
+    if (mine) {
+      for (int i = 0; i < kBins / kWave; ++i) {
+        const int32_t h = hist[32 * lane + i];
+        if (left < h) {
+          digit = 32 * lane + i;
+          break;
+        }
+        left -= h;
+      }
+    }
+    const int src = __builtin_ctzll(__ballot(mine));
+    pre |= (uint32_t)__shfl(digit, src, kWave) << sh;
+    rem = __shfl(left, src, kWave);
+    fixed |= dm << sh;
+    lo = sh;
+  }
+  if (lane == 0) {
+    *prefix = pre;
+    *rem_io = rem;
+  }
+}
+
+// Rows of up to 32768 tokens, keys in registers (thread t holds tokens
+// 4 (t + 1024 j) + e), NB = K - 1 group boundaries known at compile time.
+// Each workgroup takes rows blockIdx.x, blockIdx.x + gridDim.x, ...  Per row:
+//  1. The smallest and largest key give the bits every key shares; the digit
+//     passes start below them, so a narrow score distribution spreads over
+//     the first pass's 2048 bins instead of a handful.
+//  2. First pass: every key into one histogram (kept as four copies by lane
+//     so that lanes of a wavefront collide less), serving every boundary.
+//  3. While a boundary's bucket holds more than kList keys, another digit
+//     pass over the registers, counting only the bucket's keys.
+//  4. Then one sweep copies each boundary's bucket keys to an LDS list, and
+//     wavefront k finishes boundary k from its list (finish_bucket): t_k is
+//     the key at the boundary's rank and need_k the number of keys equal to
+//     t_k that rank before it.
+//  5. Assignment: group = number of boundaries whose key the token's key
+//     reaches, ties with t_k split by their index-order position.
+template <int NB>
+__global__ __launch_bounds__(kThreads) void select_reg_kernel(const float* __restrict__ score,
+                                                              int32_t B, int32_t N, Counts cnt,
+                                                              uint8_t* __restrict__ group_out) {
+  constexpr int kHist = NB > kCopies ? NB : kCopies;
+  __shared__ int32_t hist[kHist][kBins];   // first pass: copies by lane; later: one per boundary
+  __shared__ uint32_t s_list[NB][kList];
+  __shared__ int32_t s_nlist[NB];
+  __shared__ uint32_t s_small[NB][kWave];
+  __shared__ int32_t wave_tmp[kWaves];
+  __shared__ uint32_t red_min[kWaves], red_max[kWaves];
+  __shared__ int32_t tie_pre[kV * kWaves];
+  __shared__ uint32_t s_prefix[NB];   // key bits of boundary k's bucket (bits fixed so far)
+  __shared__ int32_t s_rem[NB];       // the boundary's rank inside that bucket
+  __shared__ int32_t s_size[NB];      // keys in that bucket
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  auto live = [&](int k) { return cnt.bound[k] < N; };   // a boundary at N: no token passes it
+
+  for (int32_t b = blockIdx.x; b < B; b += gridDim.x) {
+    // ---- this row's keys
+    uint32_t key[kV][4];
+    load_row_bits(score + (size_t)b * N, N, key);
 #pragma unroll
-    for (int k = 0; k < kMaxB; ++k) {
-      pre[k] = __builtin_amdgcn_readfirstlane(live(k) ? s_prefix[k] : kPad);   // kPad & mask matches no key
-      rem[k] = __builtin_amdgcn_readfirstlane(s_rem[k]);
-      if (live(k))
-        for (int i = tid; i < kBins; i += kThreads) hist[k][i] = 0;
+    for (int j = 0; j < kV; ++j) {
+      const int32_t left = N - 4 * (tid + j * kThreads);   // tokens of this chunk inside the row
+#pragma unroll
+      for (int e = 0; e < 4; ++e) key[j][e] = desc_key(__uint_as_float(key[j][e])) | (e < left ? 0u : kPad);
+    }
+    uint32_t kmin = kPad, kmax = 0u;
+#pragma unroll
+    for (int j = 0; j < kV; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (key[j][e] != kPad) {
+          kmin = min(kmin, key[j][e]);
+          kmax = max(kmax, key[j][e]);
+        }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, kWave));
+      kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, kWave));
+    }
+    if (lane == 0) {
+      red_min[wave] = kmin;
+      red_max[wave] = kmax;
+    }
+#pragma unroll
+    for (int c = 0; c < kCopies; ++c)
+      for (int i = tid; i < kBins; i += kThreads) hist[c][i] = 0;
+    if (tid < NB) {
+      s_rem[tid] = cnt.bound[tid];
+      s_size[tid] = N;
+      s_nlist[tid] = 0;
     }
     __syncthreads();
+    kmin = red_min[0];
+    kmax = red_max[0];
 #pragma unroll
-    for (int j = 0; j < V; ++j)
+    for (int w = 1; w < kWaves; ++w) {
+      kmin = min(kmin, red_min[w]);
+      kmax = max(kmax, red_max[w]);
+    }
+    // Slots past the row's end take the row's largest key: they sit after
+    // every token (index >= N), so they rank after every real key equal to
+    // it, and every boundary rank is < N: t_k and need_k are unchanged, and
+    // no pass needs to tell them apart.  They are never stored.
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t m = key[j][e] & mask;
+    for (int j = 0; j < kV; ++j)
 #pragma unroll
-        for (int k = 0; k < kMaxB; ++k)
-          if (k < nb && m == pre[k]) atomicAdd(&hist[k][(key[j][e] >> sh) & dm], 1);
+      for (int e = 0; e < 4; ++e) key[j][e] = key[j][e] == kPad ? kmax : key[j][e];
+    // bits below `lo` still differ between keys; every key has kmin's bits above
+    const uint32_t diff = kmin ^ kmax;
+    int lo = diff == 0u ? 0 : 32 - __clz(diff);
+    uint32_t fixed = lo == 32 ? 0u : ~((1u << lo) - 1u);
+    if (tid < NB) s_prefix[tid] = kmin & fixed;
+
+    // ---- first pass over every key (all keys share the fixed bits)
+    if (lo > 0) {
+      const int width = lo < 11 ? lo : 11;
+      const int sh = lo - width;
+      const uint32_t dm = (1u << width) - 1u;
+      int32_t* h = hist[lane & (kCopies - 1)];
+#pragma unroll
+      for (int j = 0; j < kV; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          atomicAdd(&h[(key[j][e] >> sh) & dm], 1);
+      __syncthreads();
+      int32_t h0 = 0, h1 = 0;
+#pragma unroll
+      for (int c = 0; c < kCopies; ++c) {
+        h0 += hist[c][2 * tid];
+        h1 += hist[c][2 * tid + 1];
       }
-    __syncthreads();
-    for (int k = 0; k < nb; ++k) {
-      if (!live(k)) continue;   // uniform across the workgroup
-      const int32_t h0 = hist[k][2 * tid], h1 = hist[k][2 * tid + 1];
       int32_t tot;
       const int32_t before = block_exclusive_scan(h0 + h1, wave_tmp, &tot);
-      take_bucket(before, h0, h1, rem[k], sh, &s_prefix[k], &s_rem[k], &s_size[k]);
+#pragma unroll
+      for (int k = 0; k < NB; ++k)
+        if (live(k)) take_bucket(before, h0, h1, cnt.bound[k], sh, &s_prefix[k], &s_rem[k], &s_size[k]);
+      fixed |= dm << sh;
+      lo = sh;
     }
     __syncthreads();
-  }
 
-  // ---- assignment
-  uint32_t tk[kMaxB];
-  int32_t need[kMaxB];
+    // ---- further passes over the registers while a bucket is larger than its
+    // list; every live boundary narrows in each pass (they share `fixed`)
+    while (lo > 0) {
+      bool big[NB];
+      uint32_t pre[NB];
+      int32_t rem[NB];
+      bool any = false;
 #pragma unroll
-  for (int k = 0; k < kMaxB; ++k) {
-    tk[k] = __builtin_amdgcn_readfirstlane(live(k) ? s_prefix[k] : kPad);   // no key reaches kPad
-    need[k] = __builtin_amdgcn_readfirstlane(live(k) ? s_rem[k] : 0);
-  }
-  uint32_t gp[V];   // 4 group bytes per chunk
+      for (int k = 0; k < NB; ++k) {
+        any = any || (live(k) && __builtin_amdgcn_readfirstlane(s_size[k]) > kList);
+        big[k] = live(k);
+        pre[k] = __builtin_amdgcn_readfirstlane(s_prefix[k]);
+        rem[k] = __builtin_amdgcn_readfirstlane(s_rem[k]);
+      }
+      if (!any) break;
+      const int width = lo < 11 ? lo : 11;
+      const int sh = lo - width;
+      const uint32_t dm = (1u << width) - 1u;
 #pragma unroll
-  for (int j = 0; j < V; ++j) gp[j] = 0u;
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+      for (int k = 0; k < NB; ++k)
+        if (big[k])
+          for (int i = tid; i < kBins; i += kThreads) hist[k][i] = 0;
+      __syncthreads();
 #pragma unroll
-  for (int k = 0; k < kMaxB; ++k) {
-    if (k >= nb) break;
-    if (need[k] == 0) {   // every tie with t_k ranks at or past the boundary
+      for (int j = 0; j < kV; ++j)
 #pragma unroll
-      for (int j = 0; j < V; ++j)
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t m = key[j][e] & fixed;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) gp[j] += (key[j][e] != kPad && key[j][e] >= tk[k]) ? 1u << (8 * e) : 0u;
-      continue;
+          for (int k = 0; k < NB; ++k)
+            if (big[k] && m == pre[k]) atomicAdd(&hist[k][(key[j][e] >> sh) & dm], 1);
+        }
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+        if (!big[k]) continue;   // uniform
+        const int32_t h0 = hist[k][2 * tid], h1 = hist[k][2 * tid + 1];
+        int32_t tot;
+        const int32_t before = block_exclusive_scan(h0 + h1, wave_tmp, &tot);
+        take_bucket(before, h0, h1, rem[k], sh, &s_prefix[k], &s_rem[k], &s_size[k]);
+      }
+      __syncthreads();
+      fixed |= dm << sh;
+      lo = sh;
     }
-    // ties per (chunk, wavefront): index order is chunk-major, then wavefront,
-    // lane and element
+
+    // ---- every bucket holds at most kList keys, or every bit is fixed:
+    // copy the buckets' keys to their lists: per chunk of 4 keys a wavefront
+    // counts its bucket keys (ballots), reserves that much room, then writes.
+    if (lo > 0) {
+      uint32_t pre[NB];
 #pragma unroll
-    for (int j = 0; j < V; ++j) {
-      int32_t c = 0;
+      for (int k = 0; k < NB; ++k) pre[k] = __builtin_amdgcn_readfirstlane(s_prefix[k]);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) c += __popcll(__ballot(key[j][e] == tk[k]));
-      if (lane == 0) tie_pre[j * kWaves + wave] = c;
+      for (int j = 0; j < kV; ++j)
+#pragma unroll
+        for (int k = 0; k < NB; ++k) {
+          if (!live(k)) continue;
+          uint64_t bal[4];
+          int32_t cnt = 0;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            bal[e] = __ballot((key[j][e] & fixed) == pre[k]);
+            cnt += __popcll(bal[e]);
+          }
+          if (cnt == 0) continue;   // uniform
+          int32_t at = 0;
+          if (lane == 0) at = atomicAdd(&s_nlist[k], cnt);
+          at = __shfl(at, 0, kWave);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if ((bal[e] >> lane) & 1ull) s_list[k][at + __popcll(bal[e] & lt_mask)] = key[j][e];
+            at += __popcll(bal[e]);
+          }
+        }
+      __syncthreads();
+      // wavefront k finishes boundary k from its list, no workgroup barrier
+      if (wave < NB && live(wave))
+        finish_bucket(s_list[wave], s_nlist[wave], hist[wave], s_small[wave], fixed, lo,
+                      &s_prefix[wave], &s_rem[wave]);
+      __syncthreads();
     }
-    __syncthreads();
-    if (wave == 0) {   // exclusive scan of the V * kWaves counts, 64 lanes over runs
-      constexpr int E = V * kWaves, PER = (E + kWave - 1) / kWave;
-      int32_t v[PER], sum = 0;
+
+    // ---- assignment: every bit of each boundary's key is fixed
+    uint32_t tk[NB];
+    int32_t need[NB];
 #pragma unroll
-      for (int q = 0; q < PER; ++q) {
-        const int i = lane * PER + q;
-        v[q] = i < E ? tie_pre[i] : 0;
-        sum += v[q];
-      }
-      int32_t inc = sum;
-#pragma unroll
-      for (int o = 1; o < kWave; o <<= 1) {
-        const int32_t y = __shfl_up(inc, o, kWave);
-        if (lane >= o) inc += y;
-      }
-      int32_t run = inc - sum;
-#pragma unroll
-      for (int q = 0; q < PER; ++q) {
-        const int i = lane * PER + q;
-        if (i < E) tie_pre[i] = run;
-        run += v[q];
-      }
+    for (int k = 0; k < NB; ++k) {
+      tk[k] = live(k) ? __builtin_amdgcn_readfirstlane(s_prefix[k]) : kPad;   // no key reaches kPad
+      need[k] = live(k) ? __builtin_amdgcn_readfirstlane(s_rem[k]) : 0;
     }
-    __syncthreads();
+    uint32_t gp[kV];   // 4 group bytes per chunk
 #pragma unroll
-    for (int j = 0; j < V; ++j) {
-      int32_t before = tie_pre[j * kWaves + wave];
-      bool eq[4];
+    for (int j = 0; j < kV; ++j) gp[j] = 0u;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        eq[e] = key[j][e] == tk[k];
-        before += __popcll(__ballot(eq[e]) & lt_mask);
+    for (int k = 0; k < NB; ++k) {
+      if (need[k] == 0) {   // every tie with t_k ranks at or past the boundary
+#pragma unroll
+        for (int j = 0; j < kV; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) gp[j] += key[j][e] >= tk[k] ? 1u << (8 * e) : 0u;
+        continue;
       }
+      // ties per (chunk, wavefront): index order is chunk-major, then wavefront,
+      // lane and element
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bool ge = eq[e] ? before >= need[k] : (key[j][e] != kPad && key[j][e] > tk[k]);
-        gp[j] += ge ? 1u << (8 * e) : 0u;
-        before += eq[e] ? 1 : 0;
+      for (int j = 0; j < kV; ++j) {
+        int32_t c = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) c += __popcll(__ballot(key[j][e] == tk[k]));
+        if (lane == 0) tie_pre[j * kWaves + wave] = c;
       }
+      __syncthreads();
+      if (wave == 0) {   // exclusive scan of the kV * kWaves counts, 64 lanes over runs
+        constexpr int E = kV * kWaves, PER = (E + kWave - 1) / kWave;
+        int32_t v[PER], sum = 0;
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+          const int i = lane * PER + q;
+          v[q] = i < E ? tie_pre[i] : 0;
+          sum += v[q];
+        }
+        int32_t inc = sum;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+          const int32_t y = __shfl_up(inc, o, kWave);
+          if (lane >= o) inc += y;
+        }
+        int32_t run = inc - sum;
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+          const int i = lane * PER + q;
+          if (i < E) tie_pre[i] = run;
+          run += v[q];
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < kV; ++j) {
+        int32_t before = tie_pre[j * kWaves + wave];
+        bool eq[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          eq[e] = key[j][e] == tk[k];
+          before += __popcll(__ballot(eq[e]) & lt_mask);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool ge = eq[e] ? before >= need[k] : key[j][e] > tk[k];
+          gp[j] += ge ? 1u << (8 * e) : 0u;
+          before += eq[e] ? 1 : 0;
+        }
+      }
+      __syncthreads();   // tie_pre is reused by the next boundary
     }
-    __syncthreads();   // tie_pre is reused by the next boundary
-  }
-  const bool aligned4 = (reinterpret_cast<uintptr_t>(out) & 3u) == 0u;
+    uint8_t* out = group_out + (size_t)b * N;
+    const bool aligned4 = (reinterpret_cast<uintptr_t>(out) & 3u) == 0u;
 #pragma unroll
-  for (int j = 0; j < V; ++j) {
-    const int32_t n = 4 * (tid + j * kThreads);
-    if (n < N) store_groups(out, n, N, gp[j], aligned4);
+    for (int j = 0; j < kV; ++j) {
+      const int32_t n = 4 * (tid + j * kThreads);
+      if (n < N) store_groups(out, n, N, gp[j], aligned4);
+    }
+    __syncthreads();   // the shared state is reset for the next row
   }
 }
 
@@ -398,9 +624,22 @@ hsa_status launch_select(const float* score, int32_t B, int32_t N, const int32_t
     acc += count[k];
     c.bound[k] = acc;
   }
-  if (N <= 4 * 8 * kThreads)
-    select_reg_kernel<8><<<B, kThreads, 0, s>>>(score, N, c, K - 1, group_out);
-  else
+  if (N <= 4 * kV * kThreads) {
+    // one resident workgroup per CU; each walks rows with stride = grid
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess)
+      (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    const unsigned grid = (unsigned)(B < cus ? B : cus);
+    switch (K - 1) {
+      case 1: select_reg_kernel<1><<<grid, kThreads, 0, s>>>(score, B, N, c, group_out); break;
+      case 2: select_reg_kernel<2><<<grid, kThreads, 0, s>>>(score, B, N, c, group_out); break;
+      case 3: select_reg_kernel<3><<<grid, kThreads, 0, s>>>(score, B, N, c, group_out); break;
+      case 4: select_reg_kernel<4><<<grid, kThreads, 0, s>>>(score, B, N, c, group_out); break;
+      case 5: select_reg_kernel<5><<<grid, kThreads, 0, s>>>(score, B, N, c, group_out); break;
+      case 6: select_reg_kernel<6><<<grid, kThreads, 0, s>>>(score, B, N, c, group_out); break;
+      default: select_reg_kernel<7><<<grid, kThreads, 0, s>>>(score, B, N, c, group_out); break;
+    }
+  } else
     select_mem_kernel<<<B, kThreads, 0, s>>>(score, N, c, K - 1, group_out);
   return launch_status();
 }
