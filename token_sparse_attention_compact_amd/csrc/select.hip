@@ -44,16 +44,39 @@ __device__ __forceinline__ uint32_t desc_key(float f) {
   return ~asc;                                     // larger score -> smaller key
 }
 
+// Inclusive prefix sum over the 64 lanes of a wavefront with DPP (row shifts
+// within rows of 16 lanes, then row broadcasts of lanes 15 and 31): no LDS
+// traffic, unlike shuffles.  Lanes that a shift leaves without a source add 0.
+__device__ __forceinline__ int32_t wave_incl_scan(int32_t x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);   // row_bcast:15 -> rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);   // row_bcast:31 -> rows 2, 3
+  return x;
+}
+
+// Smallest and largest value over the wavefront (the same DPP pattern; lanes
+// without a source take the identity), returned to every lane.
+__device__ __forceinline__ void wave_min_max(uint32_t& mn, uint32_t& mx) {
+  int a = (int)mn, b = (int)mx;
+  const int id_min = (int)0xffffffffu, id_max = 0;
+#define HSA_DPP_STEP(ctrl, rows)                                                              \
+  a = (int)min((uint32_t)a, (uint32_t)__builtin_amdgcn_update_dpp(id_min, a, ctrl, rows, 0xf, false)); \
+  b = (int)max((uint32_t)b, (uint32_t)__builtin_amdgcn_update_dpp(id_max, b, ctrl, rows, 0xf, false));
+  HSA_DPP_STEP(0x111, 0xf) HSA_DPP_STEP(0x112, 0xf) HSA_DPP_STEP(0x114, 0xf)
+  HSA_DPP_STEP(0x118, 0xf) HSA_DPP_STEP(0x142, 0xa) HSA_DPP_STEP(0x143, 0xc)
+#undef HSA_DPP_STEP
+  mn = (uint32_t)__builtin_amdgcn_readlane(a, 63);
+  mx = (uint32_t)__builtin_amdgcn_readlane(b, 63);
+}
+
 // Exclusive scan of one int per thread over the workgroup.
 __device__ int32_t block_exclusive_scan(int32_t v, int32_t* wave_tmp, int32_t* total) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
-  int32_t inc = v;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int32_t y = __shfl_up(inc, o, kWave);
-    if (lane >= o) inc += y;
-  }
+  const int32_t inc = wave_incl_scan(v);
   if (lane == kWave - 1) wave_tmp[wave] = inc;
   __syncthreads();
   int32_t off = 0, tot = 0;
@@ -140,79 +163,66 @@ __device__ __forceinline__ void load_row_bits(const float* row, int32_t N, uint3
 __device__ __forceinline__ void finish_bucket(const uint32_t* list, int32_t n, int32_t* hist,
                                               uint32_t* small, uint32_t fixed, int lo,
                                               uint32_t* prefix, int32_t* rem_io) {
-  // entries are read from LDS again in every pass: the wavefront's registers
-  // still hold its row's keys
-  constexpr int M = kList / kWave;   // list entries per lane
+  constexpr int M = kList / kWave;   // list entries per lane, loaded once
   const int lane = threadIdx.x & (kWave - 1);
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   uint32_t pre = __builtin_amdgcn_readfirstlane(*prefix);
   int32_t rem = __builtin_amdgcn_readfirstlane(*rem_io);
+  uint32_t c[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) c[m] = list[lane + kWave * m < n ? lane + kWave * m : 0];
   while (lo > 0) {   // lo == 0: every bit fixed, pre is t and rem its tie count
     int32_t total = 0;
-    for (int m = 0; m < M; ++m) {
-      const int i = lane + kWave * m;
-      total += __popcll(__ballot(i < n && (list[i < n ? i : 0] & fixed) == pre));
-    }
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+      total += __popcll(__ballot(lane + kWave * m < n && (c[m] & fixed) == pre));
     if (total <= kWave) {   // gather the bucket's keys, one per lane, and rank them
       int32_t at = 0;
+#pragma unroll
       for (int m = 0; m < M; ++m) {
-        const int i = lane + kWave * m;
-        const uint32_t c = list[i < n ? i : 0];
-        const bool in = i < n && (c & fixed) == pre;
+        const bool in = lane + kWave * m < n && (c[m] & fixed) == pre;
         const uint64_t bal = __ballot(in);
-        if (in) small[at + __popcll(bal & lt_mask)] = c;
+        if (in) small[at + __popcll(bal & lt_mask)] = c[m];
         at += __popcll(bal);
       }
       const uint32_t x = lane < total ? small[lane] : 0u;
       int32_t less = 0, leq = 0;
-      for (int i = 0; i < total; ++i) {
-        const uint32_t y = small[i];
+      for (int i = 0; i < total; ++i) {   // i is uniform: the key of lane i from a register
+        const uint32_t y = (uint32_t)__builtin_amdgcn_readlane((int)x, i);
         less += y < x ? 1 : 0;
         leq += y <= x ? 1 : 0;
       }
       const bool hit = lane < total && less <= rem && rem < leq;   // x is the key at rank rem
       const int src = __builtin_ctzll(__ballot(hit));               // some lane holds it
-      pre = (uint32_t)__shfl((int)x, src, kWave);
-      rem = rem - __shfl(less, src, kWave);
+      pre = (uint32_t)__builtin_amdgcn_readlane((int)x, src);
+      rem = rem - __builtin_amdgcn_readlane(less, src);
       break;
     }
     const int width = lo < 11 ? lo : 11;
     const int sh = lo - width;
     const uint32_t dm = (1u << width) - 1u;
+#pragma unroll
     for (int i = 0; i < kBins / kWave; i += 4)
       *reinterpret_cast<i32x4_t*>(&hist[32 * lane + i]) = i32x4_t{0, 0, 0, 0};
-    for (int m = 0; m < M; ++m) {
-      const int i = lane + kWave * m;
-      const uint32_t c = list[i < n ? i : 0];
-      if (i < n && (c & fixed) == pre) atomicAdd(&hist[(c >> sh) & dm], 1);
-    }
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+      if (lane + kWave * m < n && (c[m] & fixed) == pre) atomicAdd(&hist[(c[m] >> sh) & dm], 1);
     int32_t sum = 0;
+#pragma unroll
     for (int i = 0; i < kBins / kWave; i += 4) {
       const i32x4_t v = *reinterpret_cast<const i32x4_t*>(&hist[32 * lane + i]);
       sum += (v[0] + v[1]) + (v[2] + v[3]);
     }
-    int32_t inc = sum;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const int32_t y = __shfl_up(inc, o, kWave);
-      if (lane >= o) inc += y;
-    }
+    const int32_t inc = wave_incl_scan(sum);
     const int32_t excl = inc - sum;
-    const bool mine = excl <= rem && rem < inc;   // exactly one lane's bins hold rank rem
-    int32_t digit = 0, left = rem - excl;
-    if (mine) {
-      for (int i = 0; i < kBins / kWave; ++i) {
-        const int32_t h = hist[32 * lane + i];
-        if (left < h) {
-          digit = 32 * lane + i;
-          break;
-        }
-        left -= h;
-      }
-    }
-    const int src = __builtin_ctzll(__ballot(mine));
-    pre |= (uint32_t)__shfl(digit, src, kWave) << sh;
-    rem = __shfl(left, src, kWave);
+    // the lane whose 32 bins hold rank rem; then 32 lanes scan those bins
+    const int src = __builtin_ctzll(__ballot(excl <= rem && rem < inc));
+    const int32_t left0 = rem - __builtin_amdgcn_readlane(excl, src);
+    const int32_t hb = lane < 32 ? hist[32 * src + lane] : 0;
+    const int32_t hinc = wave_incl_scan(hb);
+    const int bin = __builtin_ctzll(__ballot(lane < 32 && left0 < hinc));   // first bin reaching rank
+    pre |= (uint32_t)(32 * src + bin) << sh;
+    rem = left0 - (__builtin_amdgcn_readlane(hinc, bin) - __builtin_amdgcn_readlane(hb, bin));
     fixed |= dm << sh;
     lo = sh;
   }
@@ -511,6 +521,298 @@ __global__ __launch_bounds__(kThreads) void select_reg_kernel(const float* __res
   }
 }
 
+// One or two group boundaries (K <= 3, every workload here), rows of up to
+// 32768 tokens: the same passes as select_reg_kernel, but the row's keys sit
+// in LDS (token order, 128 KiB) and every pass reads them from there, so a
+// thread's registers hold only the next row's raw scores, loaded while this
+// row is ranked.  Each workgroup takes rows blockIdx.x, blockIdx.x +
+// gridDim.x, ...; slots past a row's end take the row's largest key.
+template <int NB>
+__global__ __launch_bounds__(kThreads) void select_lds_kernel(const float* __restrict__ score,
+                                                              int32_t B, int32_t N, Counts cnt,
+                                                              uint8_t* __restrict__ group_out) {
+  static_assert(NB >= 1 && NB <= 2, "LDS holds two boundaries' histograms and lists");
+  __shared__ __attribute__((aligned(16))) uint32_t s_key[4 * kV * kThreads];
+  __shared__ int32_t hist[2][kBins];   // first pass: two copies by lane; later: one per boundary
+  __shared__ uint32_t s_list[NB][kList];
+  __shared__ uint32_t s_small[NB][kWave];
+  __shared__ int32_t s_wcount[NB][kWaves];
+  __shared__ int32_t wave_tmp[kWaves];
+  __shared__ uint32_t red_min[kWaves], red_max[kWaves];
+  __shared__ int32_t tie_pre[kV * kWaves];
+  __shared__ uint32_t s_prefix[NB];
+  __shared__ int32_t s_rem[NB], s_size[NB], s_nlist[NB];
+  auto live = [&](int k) { return cnt.bound[k] < N; };   // a boundary at N: no token passes it
+
+  uint32_t raw[kV][4];
+  if (blockIdx.x < (uint32_t)B) load_row_bits(score + (size_t)blockIdx.x * N, N, raw);
+  for (int32_t b = blockIdx.x; b < B; b += gridDim.x) {
+    // The thread id is made opaque per row, so that the addresses derived
+    // from it are recomputed in each row instead of held in registers across
+    // the whole loop (which would spill, and every spill reload waits for
+    // the next row's loads in flight).
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    auto keys4 = [&](int j) { return *reinterpret_cast<const u32x4*>(&s_key[4 * (tid + j * kThreads)]); };
+    // ---- keys, the smallest and largest; into LDS; the next row's loads go out
+    uint32_t kmin = kPad, kmax = 0u;
+#pragma unroll
+    for (int j = 0; j < kV; ++j) {
+      const int32_t left = N - 4 * (tid + j * kThreads);   // tokens of this chunk inside the row
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        raw[j][e] = desc_key(__uint_as_float(raw[j][e])) | (e < left ? 0u : kPad);
+        if (raw[j][e] != kPad) {
+          kmin = min(kmin, raw[j][e]);
+          kmax = max(kmax, raw[j][e]);
+        }
+      }
+    }
+    wave_min_max(kmin, kmax);
+    if (lane == 0) {
+      red_min[wave] = kmin;
+      red_max[wave] = kmax;
+    }
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+      for (int i = tid; i < kBins; i += kThreads) hist[c][i] = 0;
+    if (tid < NB) {
+      s_rem[tid] = cnt.bound[tid];
+      s_size[tid] = N;
+    }
+    __syncthreads();
+    kmin = red_min[0];
+    kmax = red_max[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) {
+      kmin = min(kmin, red_min[w]);
+      kmax = max(kmax, red_max[w]);
+    }
+#pragma unroll
+    for (int j = 0; j < kV; ++j) {
+      u32x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = raw[j][e] == kPad ? kmax : raw[j][e];
+      *reinterpret_cast<u32x4*>(&s_key[4 * (tid + j * kThreads)]) = v;
+    }
+    if (b + (int32_t)gridDim.x < B) load_row_bits(score + (size_t)(b + gridDim.x) * N, N, raw);
+    // bits below `lo` still differ between keys; every key has kmin's bits above
+    const uint32_t diff = kmin ^ kmax;
+    int lo = diff == 0u ? 0 : 32 - __clz(diff);
+    uint32_t fixed = lo == 32 ? 0u : ~((1u << lo) - 1u);
+    if (tid < NB) s_prefix[tid] = kmin & fixed;
+    __syncthreads();
+
+    // ---- first pass over every key
+    if (lo > 0) {
+      const int width = lo < 11 ? lo : 11;
+      const int sh = lo - width;
+      const uint32_t dm = (1u << width) - 1u;
+      int32_t* h = hist[lane & 1];
+#pragma unroll
+      for (int j = 0; j < kV; ++j) {
+        const u32x4 v = keys4(j);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) atomicAdd(&h[(v[e] >> sh) & dm], 1);
+      }
+      __syncthreads();
+      const int32_t hb[2] = {hist[0][2 * tid] + hist[1][2 * tid], hist[0][2 * tid + 1] + hist[1][2 * tid + 1]};
+      int32_t tot;
+      const int32_t before = block_exclusive_scan(hb[0] + hb[1], wave_tmp, &tot);
+#pragma unroll
+      for (int k = 0; k < NB; ++k)
+        if (live(k)) take_bucket(before, hb[0], hb[1], cnt.bound[k], sh, &s_prefix[k], &s_rem[k], &s_size[k]);
+      fixed |= dm << sh;
+      lo = sh;
+    }
+    __syncthreads();
+
+    // ---- further passes while a bucket is larger than its list (every live
+    // boundary narrows in each, as they share `fixed`)
+    while (lo > 0) {
+      uint32_t pre[NB];
+      int32_t rem[NB];
+      bool any = false;
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+        any = any || (live(k) && __builtin_amdgcn_readfirstlane(s_size[k]) > kList);
+        pre[k] = __builtin_amdgcn_readfirstlane(s_prefix[k]);
+        rem[k] = __builtin_amdgcn_readfirstlane(s_rem[k]);
+      }
+      if (!any) break;
+      const int width = lo < 11 ? lo : 11;
+      const int sh = lo - width;
+      const uint32_t dm = (1u << width) - 1u;
+#pragma unroll
+      for (int k = 0; k < NB; ++k)
+        for (int i = tid; i < kBins; i += kThreads) hist[k][i] = 0;
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < kV; ++j) {
+        const u32x4 v = keys4(j);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int k = 0; k < NB; ++k)
+            if (live(k) && (v[e] & fixed) == pre[k]) atomicAdd(&hist[k][(v[e] >> sh) & dm], 1);
+      }
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+        if (!live(k)) continue;   // uniform
+        const int32_t h0 = hist[k][2 * tid], h1 = hist[k][2 * tid + 1];
+        int32_t tot;
+        const int32_t before = block_exclusive_scan(h0 + h1, wave_tmp, &tot);
+        take_bucket(before, h0, h1, rem[k], sh, &s_prefix[k], &s_rem[k], &s_size[k]);
+      }
+      __syncthreads();
+      fixed |= dm << sh;
+      lo = sh;
+    }
+
+    // ---- the buckets' keys to their lists (each wavefront counts its keys,
+    // one barrier, then writes after the waves before it); wavefront k then
+    // finishes boundary k
+    if (lo > 0) {
+      uint32_t pre[NB];
+#pragma unroll
+      for (int k = 0; k < NB; ++k) pre[k] = __builtin_amdgcn_readfirstlane(s_prefix[k]);
+      int32_t c[NB];
+#pragma unroll
+      for (int k = 0; k < NB; ++k) c[k] = 0;
+#pragma unroll
+      for (int j = 0; j < kV; ++j) {
+        const u32x4 v = keys4(j);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int k = 0; k < NB; ++k) c[k] += __popcll(__ballot((v[e] & fixed) == pre[k]));
+      }
+      if (lane == 0) {
+#pragma unroll
+        for (int k = 0; k < NB; ++k) s_wcount[k][wave] = c[k];
+      }
+      __syncthreads();
+      int32_t at[NB];
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+        at[k] = 0;
+        for (int w = 0; w < wave; ++w) at[k] += s_wcount[k][w];
+      }
+#pragma unroll
+      for (int j = 0; j < kV; ++j) {
+        const u32x4 v = keys4(j);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int k = 0; k < NB; ++k) {
+            const bool in = (v[e] & fixed) == pre[k];
+            const uint64_t bal = __ballot(in);
+            if (live(k) && in) s_list[k][at[k] + __popcll(bal & lt_mask)] = v[e];
+            at[k] += __popcll(bal);
+          }
+      }
+      if (wave == kWaves - 1 && lane == 0) {
+#pragma unroll
+        for (int k = 0; k < NB; ++k) s_nlist[k] = at[k];
+      }
+      __syncthreads();
+      if (wave < NB && live(wave))
+        finish_bucket(s_list[wave], s_nlist[wave], hist[wave], s_small[wave], fixed, lo,
+                      &s_prefix[wave], &s_rem[wave]);
+      __syncthreads();
+    }
+
+    // ---- assignment: every bit of each boundary's key is fixed
+    uint32_t tk[NB];
+    int32_t need[NB];
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      tk[k] = live(k) ? __builtin_amdgcn_readfirstlane(s_prefix[k]) : kPad;   // no key reaches kPad
+      need[k] = live(k) ? __builtin_amdgcn_readfirstlane(s_rem[k]) : 0;
+    }
+    uint32_t gp[kV];   // 4 group bytes per chunk
+#pragma unroll
+    for (int j = 0; j < kV; ++j) gp[j] = 0u;
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      if (need[k] == 0) {   // every tie with t_k ranks at or past the boundary
+#pragma unroll
+        for (int j = 0; j < kV; ++j) {
+          const u32x4 v = keys4(j);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) gp[j] += v[e] >= tk[k] ? 1u << (8 * e) : 0u;
+        }
+        continue;
+      }
+      // ties per (chunk, wavefront): index order is chunk-major, then wavefront,
+      // lane and element
+#pragma unroll
+      for (int j = 0; j < kV; ++j) {
+        const u32x4 v = keys4(j);
+        int32_t c = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) c += __popcll(__ballot(v[e] == tk[k]));
+        if (lane == 0) tie_pre[j * kWaves + wave] = c;
+      }
+      __syncthreads();
+      if (wave == 0) {   // exclusive scan of the kV * kWaves counts, 64 lanes over runs
+        constexpr int E = kV * kWaves, PER = (E + kWave - 1) / kWave;
+        int32_t v[PER], sum = 0;
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+          const int i = lane * PER + q;
+          v[q] = i < E ? tie_pre[i] : 0;
+          sum += v[q];
+        }
+        int32_t inc = sum;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+          const int32_t y = __shfl_up(inc, o, kWave);
+          if (lane >= o) inc += y;
+        }
+        int32_t run = inc - sum;
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+          const int i = lane * PER + q;
+          if (i < E) tie_pre[i] = run;
+          run += v[q];
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < kV; ++j) {
+        const u32x4 v = keys4(j);
+        int32_t before = tie_pre[j * kWaves + wave];
+        bool eq[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          eq[e] = v[e] == tk[k];
+          before += __popcll(__ballot(eq[e]) & lt_mask);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool ge = eq[e] ? before >= need[k] : v[e] > tk[k];
+          gp[j] += ge ? 1u << (8 * e) : 0u;
+          before += eq[e] ? 1 : 0;
+        }
+      }
+      __syncthreads();   // tie_pre is reused by the next boundary
+    }
+    uint8_t* out = group_out + (size_t)b * N;
+    const bool aligned4 = (reinterpret_cast<uintptr_t>(out) & 3u) == 0u;
+#pragma unroll
+    for (int j = 0; j < kV; ++j) {
+      const int32_t n = 4 * (tid + j * kThreads);
+      if (n < N) store_groups(out, n, N, gp[j], aligned4);
+    }
+    __syncthreads();   // the shared state (keys included) is rewritten for the next row
+  }
+}
+
 // Rows past the register capacity: the same passes, reading the scores from
 // memory each time (the row stays in L2 / the Infinity Cache between passes).
 __global__ __launch_bounds__(kThreads) void select_mem_kernel(const float* __restrict__ score,
@@ -631,8 +933,8 @@ hsa_status launch_select(const float* score, int32_t B, int32_t N, const int32_t
       (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     const unsigned grid = (unsigned)(B < cus ? B : cus);
     switch (K - 1) {
-      case 1: select_reg_kernel<1><<<grid, kThreads, 0, s>>>(score, B, N, c, group_out); break;
-      case 2: select_reg_kernel<2><<<grid, kThreads, 0, s>>>(score, B, N, c, group_out); break;
+      case 1: select_lds_kernel<1><<<grid, kThreads, 0, s>>>(score, B, N, c, group_out); break;
+      case 2: select_lds_kernel<2><<<grid, kThreads, 0, s>>>(score, B, N, c, group_out); break;
       case 3: select_reg_kernel<3><<<grid, kThreads, 0, s>>>(score, B, N, c, group_out); break;
       case 4: select_reg_kernel<4><<<grid, kThreads, 0, s>>>(score, B, N, c, group_out); break;
       case 5: select_reg_kernel<5><<<grid, kThreads, 0, s>>>(score, B, N, c, group_out); break;
