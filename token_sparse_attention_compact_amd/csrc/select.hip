@@ -38,7 +38,7 @@ struct Counts {
 __device__ __forceinline__ uint32_t desc_key(float f) {
   uint32_t u = __float_as_uint(f);
   u = (f != f) ? 0x7f800000u : u;                  // NaN ranks as +inf
-  u = (u & 0x7fffffffu) == 0u ? 0u : u;            // -0 ranks as +0
+  u = (u == 0x80000000u) ? 0u : u;                 // -0 ranks as +0
   // monotone in the score: flip every bit of negatives, the sign bit of the rest
   const uint32_t asc = u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
   return ~asc;                                     // larger score -> smaller key
@@ -108,6 +108,23 @@ __device__ __forceinline__ void take_bucket(int32_t before, int32_t h0, int32_t 
     *prefix |= (uint32_t)(2 * tid + 1) << sh;
     *rem_out = rem - before - h0;
     *size_out = h1;
+  }
+}
+
+// The same for four bins 4t .. 4t + 3.
+__device__ __forceinline__ void take_bucket4(int32_t before, const int32_t (&h)[4], int32_t rem,
+                                             int sh, uint32_t* prefix, int32_t* rem_out,
+                                             int32_t* size_out) {
+  const int tid = threadIdx.x;
+  int32_t run = before;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if (run <= rem && rem < run + h[q]) {
+      *prefix |= (uint32_t)(4 * tid + q) << sh;
+      *rem_out = rem - run;
+      *size_out = h[q];
+    }
+    run += h[q];
   }
 }
 
@@ -229,6 +246,57 @@ __device__ __forceinline__ void finish_bucket(const uint32_t* list, int32_t n, i
   if (lane == 0) {
     *prefix = pre;
     *rem_io = rem;
+  }
+}
+
+// One lane adds v to the LDS counter *p; every lane gets the value before.
+// (Written out so that the compiler does not rebuild it as a whole-wavefront
+// atomic; the wait is inside the same statement.)
+__device__ __forceinline__ int32_t lds_reserve(int32_t* p, int32_t v) {
+  int32_t old = 0;
+  if ((threadIdx.x & (kWave - 1)) == 0) {
+    const uint32_t a = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) int32_t*)p;
+    asm volatile("ds_add_rtn_u32 %0, %1, %2\n\ts_waitcnt lgkmcnt(0)" : "=v"(old) : "v"(a), "v"(v) : "memory");
+  }
+  return __builtin_amdgcn_readfirstlane(old);
+}
+
+// Lanes below this one whose bit is set in m.
+__device__ __forceinline__ int32_t lanes_below(uint64_t m) {
+  return (int32_t)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// The threads t = 0, 1, .. of one boundary (whole wavefronts, four per key)
+// rank the n keys of its list, whose slots from n on hold kPad: the four
+// lanes 4i .. 4i + 3 take key i and a quarter of the list each, counting the
+// keys below key i and those at most key i, then add their counts.  The key
+// whose range [less, leq) holds rank rem is the boundary key t_k, and
+// rem - less is the number of its ties ranked before the boundary; every lane
+// holding t_k writes the same two values.  rem is read by the caller before
+// any thread can write *rem_out.
+__device__ __forceinline__ void rank_in_list(const uint32_t* list, int32_t n, int t, int32_t rem,
+                                             uint32_t* prefix_out, int32_t* rem_out) {
+  const int i = t >> 2, q = t & 3;
+  const int32_t m = ((n + 15) >> 4) << 2;   // quarter length, a multiple of 4 (slots past n hold kPad)
+  const uint32_t x = i < n ? list[i] : kPad;
+  const uint32_t* part = list + q * m;
+  int32_t less = 0, leq = 0;
+  for (int r = 0; r < m; r += 4) {
+    const u32x4 y = *reinterpret_cast<const u32x4*>(&part[r]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      less += y[e] < x ? 1 : 0;
+      leq += y[e] <= x ? 1 : 0;
+    }
+  }
+  // the four lanes of key i: quad permutations [1,0,3,2] then [2,3,0,1]
+  less += __builtin_amdgcn_update_dpp(0, less, 0xb1, 0xf, 0xf, false);
+  leq += __builtin_amdgcn_update_dpp(0, leq, 0xb1, 0xf, 0xf, false);
+  less += __builtin_amdgcn_update_dpp(0, less, 0x4e, 0xf, 0xf, false);
+  leq += __builtin_amdgcn_update_dpp(0, leq, 0x4e, 0xf, 0xf, false);
+  if (q == 0 && i < n && less <= rem && rem < leq) {
+    *prefix_out = x;
+    *rem_out = rem - less;
   }
 }
 
@@ -534,17 +602,30 @@ __global__ __launch_bounds__(kThreads) void select_lds_kernel(const float* __res
   static_assert(NB >= 1 && NB <= 2, "LDS holds two boundaries' histograms and lists");
   __shared__ __attribute__((aligned(16))) uint32_t s_key[4 * kV * kThreads];
   __shared__ int32_t hist[2][kBins];   // first pass: two copies by lane; later: one per boundary
-  __shared__ uint32_t s_list[NB][kList];
+  __shared__ __attribute__((aligned(16))) uint32_t s_list[NB][kList];
   __shared__ uint32_t s_small[NB][kWave];
-  __shared__ int32_t s_wcount[NB][kWaves];
   __shared__ int32_t wave_tmp[kWaves];
   __shared__ uint32_t red_min[kWaves], red_max[kWaves];
   __shared__ int32_t tie_pre[kV * kWaves];
   __shared__ uint32_t s_prefix[NB];
   __shared__ int32_t s_rem[NB], s_size[NB], s_nlist[NB];
-  auto live = [&](int k) { return cnt.bound[k] < N; };   // a boundary at N: no token passes it
+  // The bounds in scalar registers, opaque to the compiler: a bound picked by
+  // a k that differs between wavefronts must not become a load from the
+  // kernel arguments (that load would wait for every load and store in
+  // flight, the next row's prefetch included).
+  int32_t bnd[NB];
+#pragma unroll
+  for (int k = 0; k < NB; ++k) {
+    bnd[k] = cnt.bound[k];
+    asm volatile("" : "+s"(bnd[k]));
+  }
+  auto live = [&](int k) { return bnd[k] < N; };   // a boundary at N: no token passes it
+  auto bound_of = [&](int k) { return NB == 1 || k == 0 ? bnd[0] : bnd[NB - 1]; };
 
   uint32_t raw[kV][4];
+  uint32_t gp[kV];   // group bytes of the previous row, 4 per chunk, stored once
+                     // this row's scores have arrived (so that no wait for the
+                     // next row's loads also waits for these stores)
   if (blockIdx.x < (uint32_t)B) load_row_bits(score + (size_t)blockIdx.x * N, N, raw);
   for (int32_t b = blockIdx.x; b < B; b += gridDim.x) {
     // The thread id is made opaque per row, so that the addresses derived
@@ -561,6 +642,13 @@ __global__ __launch_bounds__(kThreads) void select_lds_kernel(const float* __res
     uint32_t kmin = kPad, kmax = 0u;
 #pragma unroll
     for (int j = 0; j < kV; ++j) {
+      if (4 * (j + 1) * kThreads <= N) {   // uniform: the whole chunk lies inside the row
+#pragma unroll
+        for (int e = 0; e < 4; ++e) raw[j][e] = desc_key(__uint_as_float(raw[j][e]));
+        kmin = min(kmin, min(min(raw[j][0], raw[j][1]), min(raw[j][2], raw[j][3])));
+        kmax = max(kmax, max(max(raw[j][0], raw[j][1]), max(raw[j][2], raw[j][3])));
+        continue;
+      }
       const int32_t left = N - 4 * (tid + j * kThreads);   // tokens of this chunk inside the row
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -571,6 +659,22 @@ __global__ __launch_bounds__(kThreads) void select_lds_kernel(const float* __res
         }
       }
     }
+    if (b != (int32_t)blockIdx.x) {
+      // the stores take an address that depends on every key, so that they
+      // issue after this row's scores have arrived
+      int32_t after_keys = 0;
+      asm volatile("" : "+v"(after_keys) : "v"(kmin), "v"(kmax));
+      uint8_t* prev = group_out + (size_t)(b - gridDim.x) * N + after_keys;
+      const bool aligned4 = (reinterpret_cast<uintptr_t>(prev) & 3u) == 0u;
+#pragma unroll
+      for (int j = 0; j < kV; ++j) {
+        const int32_t n = 4 * (tid + j * kThreads);
+        if (aligned4 && 4 * (j + 1) * kThreads <= N)   // uniform
+          *reinterpret_cast<uint32_t*>(prev + n) = gp[j];
+        else if (n < N)
+          store_groups(prev, n, N, gp[j], aligned4);
+      }
+    }
     wave_min_max(kmin, kmax);
     if (lane == 0) {
       red_min[wave] = kmin;
@@ -579,9 +683,13 @@ __global__ __launch_bounds__(kThreads) void select_lds_kernel(const float* __res
 #pragma unroll
     for (int c = 0; c < 2; ++c)
       for (int i = tid; i < kBins; i += kThreads) hist[c][i] = 0;
+#pragma unroll
+    for (int k = 0; k < NB; ++k)
+      for (int i = tid; i < kList; i += kThreads) s_list[k][i] = kPad;   // slots past a bucket's size
     if (tid < NB) {
-      s_rem[tid] = cnt.bound[tid];
+      s_rem[tid] = bound_of(tid);
       s_size[tid] = N;
+      s_nlist[tid] = 0;
     }
     __syncthreads();
     kmin = red_min[0];
@@ -594,8 +702,9 @@ __global__ __launch_bounds__(kThreads) void select_lds_kernel(const float* __res
 #pragma unroll
     for (int j = 0; j < kV; ++j) {
       u32x4 v;
+      const bool whole = 4 * (j + 1) * kThreads <= N;   // uniform
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = raw[j][e] == kPad ? kmax : raw[j][e];
+      for (int e = 0; e < 4; ++e) v[e] = (!whole && raw[j][e] == kPad) ? kmax : raw[j][e];
       *reinterpret_cast<u32x4*>(&s_key[4 * (tid + j * kThreads)]) = v;
     }
     if (b + (int32_t)gridDim.x < B) load_row_bits(score + (size_t)(b + gridDim.x) * N, N, raw);
@@ -606,12 +715,13 @@ __global__ __launch_bounds__(kThreads) void select_lds_kernel(const float* __res
     if (tid < NB) s_prefix[tid] = kmin & fixed;
     __syncthreads();
 
-    // ---- first pass over every key
+    // ---- first pass over every key: a 12-bit digit, both halves of `hist`
+    // as one histogram of 4096 bins
     if (lo > 0) {
-      const int width = lo < 11 ? lo : 11;
+      const int width = lo < 12 ? lo : 12;
       const int sh = lo - width;
       const uint32_t dm = (1u << width) - 1u;
-      int32_t* h = hist[lane & 1];
+      int32_t* h = &hist[0][0];
 #pragma unroll
       for (int j = 0; j < kV; ++j) {
         const u32x4 v = keys4(j);
@@ -619,26 +729,28 @@ __global__ __launch_bounds__(kThreads) void select_lds_kernel(const float* __res
         for (int e = 0; e < 4; ++e) atomicAdd(&h[(v[e] >> sh) & dm], 1);
       }
       __syncthreads();
-      const int32_t hb[2] = {hist[0][2 * tid] + hist[1][2 * tid], hist[0][2 * tid + 1] + hist[1][2 * tid + 1]};
+      const i32x4_t h4 = *reinterpret_cast<const i32x4_t*>(&h[4 * tid]);
+      const int32_t hb[4] = {h4[0], h4[1], h4[2], h4[3]};
       int32_t tot;
-      const int32_t before = block_exclusive_scan(hb[0] + hb[1], wave_tmp, &tot);
+      const int32_t before = block_exclusive_scan((hb[0] + hb[1]) + (hb[2] + hb[3]), wave_tmp, &tot);
 #pragma unroll
       for (int k = 0; k < NB; ++k)
-        if (live(k)) take_bucket(before, hb[0], hb[1], cnt.bound[k], sh, &s_prefix[k], &s_rem[k], &s_size[k]);
+        if (live(k)) take_bucket4(before, hb, bnd[k], sh, &s_prefix[k], &s_rem[k], &s_size[k]);
       fixed |= dm << sh;
       lo = sh;
     }
     __syncthreads();
 
-    // ---- further passes while a bucket is larger than its list (every live
-    // boundary narrows in each, as they share `fixed`)
+    // ---- further passes while a bucket is too large to be ranked directly
+    // (four threads per key; every live boundary narrows in each pass, as
+    // they share `fixed`)
     while (lo > 0) {
       uint32_t pre[NB];
       int32_t rem[NB];
       bool any = false;
 #pragma unroll
       for (int k = 0; k < NB; ++k) {
-        any = any || (live(k) && __builtin_amdgcn_readfirstlane(s_size[k]) > kList);
+        any = any || (live(k) && 4 * __builtin_amdgcn_readfirstlane(s_size[k]) > kThreads / NB);
         pre[k] = __builtin_amdgcn_readfirstlane(s_prefix[k]);
         rem[k] = __builtin_amdgcn_readfirstlane(s_rem[k]);
       }
@@ -673,81 +785,85 @@ __global__ __launch_bounds__(kThreads) void select_lds_kernel(const float* __res
       lo = sh;
     }
 
-    // ---- the buckets' keys to their lists (each wavefront counts its keys,
-    // one barrier, then writes after the waves before it); wavefront k then
-    // finishes boundary k
+    // ---- the buckets' keys to their lists: per chunk of 4 keys a wavefront
+    // counts its bucket keys (ballots), reserves that much room, then writes;
+    // then each boundary's bucket is ranked (the bucket's size is s_size)
     if (lo > 0) {
       uint32_t pre[NB];
 #pragma unroll
       for (int k = 0; k < NB; ++k) pre[k] = __builtin_amdgcn_readfirstlane(s_prefix[k]);
-      int32_t c[NB];
-#pragma unroll
-      for (int k = 0; k < NB; ++k) c[k] = 0;
+      const uint32_t span = lo == 32 ? 0xffffffffu : 1u << lo;   // lo == 32: no bit fixed, every key
 #pragma unroll
       for (int j = 0; j < kV; ++j) {
         const u32x4 v = keys4(j);
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
+        for (int k = 0; k < NB; ++k) {
+          if (!live(k)) continue;   // uniform
+          bool in[4];
+          uint64_t bal[4];
+          int32_t c = 0;
 #pragma unroll
-          for (int k = 0; k < NB; ++k) c[k] += __popcll(__ballot((v[e] & fixed) == pre[k]));
-      }
-      if (lane == 0) {
-#pragma unroll
-        for (int k = 0; k < NB; ++k) s_wcount[k][wave] = c[k];
-      }
-      __syncthreads();
-      int32_t at[NB];
-#pragma unroll
-      for (int k = 0; k < NB; ++k) {
-        at[k] = 0;
-        for (int w = 0; w < wave; ++w) at[k] += s_wcount[k][w];
-      }
-#pragma unroll
-      for (int j = 0; j < kV; ++j) {
-        const u32x4 v = keys4(j);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-#pragma unroll
-          for (int k = 0; k < NB; ++k) {
-            const bool in = (v[e] & fixed) == pre[k];
-            const uint64_t bal = __ballot(in);
-            if (live(k) && in) s_list[k][at[k] + __popcll(bal & lt_mask)] = v[e];
-            at[k] += __popcll(bal);
+          for (int e = 0; e < 4; ++e) {
+            in[e] = v[e] - pre[k] < span;   // the bucket: keys pre[k] .. pre[k] + span - 1
+            bal[e] = __ballot(in[e]);
+            c += __popcll(bal[e]);
           }
-      }
-      if (wave == kWaves - 1 && lane == 0) {
+          if (c == 0) continue;   // uniform
+          int32_t at = lds_reserve(&s_nlist[k], c);
 #pragma unroll
-        for (int k = 0; k < NB; ++k) s_nlist[k] = at[k];
+          for (int e = 0; e < 4; ++e) {
+            if (in[e]) s_list[k][at + lanes_below(bal[e])] = v[e];
+            at += __popcll(bal[e]);
+          }
+        }
       }
+      // boundary k takes threads k * kThreads / NB ..: a bucket of up to a
+      // quarter as many keys is ranked by comparing every pair, a larger one
+      // by the part's first wavefront in digit passes
+      constexpr int kPart = kThreads / NB;
+      const int kb = tid / kPart, t = tid % kPart;
+      const int32_t rem = __builtin_amdgcn_readfirstlane(s_rem[kb]);   // before any thread rewrites it
       __syncthreads();
-      if (wave < NB && live(wave))
-        finish_bucket(s_list[wave], s_nlist[wave], hist[wave], s_small[wave], fixed, lo,
-                      &s_prefix[wave], &s_rem[wave]);
+      const int32_t n = __builtin_amdgcn_readfirstlane(s_nlist[kb]);
+      if (bound_of(kb) < N) {
+        if (4 * n <= kPart) {
+          if (t < ((4 * n + kWave - 1) & ~(kWave - 1)))   // wavefronts holding a key
+            rank_in_list(s_list[kb], n, t, rem, &s_prefix[kb], &s_rem[kb]);
+        } else if (t < kWave) {
+          finish_bucket(s_list[kb], n, hist[kb], s_small[kb], fixed, lo, &s_prefix[kb], &s_rem[kb]);
+        }
+      }
       __syncthreads();
     }
 
-    // ---- assignment: every bit of each boundary's key is fixed
-    uint32_t tk[NB];
+    // ---- assignment: every bit of each boundary's key is fixed.  A key
+    // passes boundary k if it is above t_k, or equals t_k and does not rank
+    // among the first need[k] ties (index order); with need[k] == 0 every
+    // tie passes, so one compare per boundary settles every key.
+    uint32_t tk[NB], thr[NB];
     int32_t need[NB];
 #pragma unroll
     for (int k = 0; k < NB; ++k) {
       tk[k] = live(k) ? __builtin_amdgcn_readfirstlane(s_prefix[k]) : kPad;   // no key reaches kPad
       need[k] = live(k) ? __builtin_amdgcn_readfirstlane(s_rem[k]) : 0;
+      thr[k] = need[k] == 0 ? tk[k] : tk[k] + 1u;   // ties counted apart below
     }
-    uint32_t gp[kV];   // 4 group bytes per chunk
 #pragma unroll
-    for (int j = 0; j < kV; ++j) gp[j] = 0u;
+    for (int j = 0; j < kV; ++j) {
+      const u32x4 v = keys4(j);
+      uint32_t g = 0u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        uint32_t c = 0u;
+#pragma unroll
+        for (int k = 0; k < NB; ++k) c += v[e] >= thr[k] ? 1u : 0u;
+        g |= c << (8 * e);
+      }
+      gp[j] = g;
+    }
 #pragma unroll
     for (int k = 0; k < NB; ++k) {
-      if (need[k] == 0) {   // every tie with t_k ranks at or past the boundary
-#pragma unroll
-        for (int j = 0; j < kV; ++j) {
-          const u32x4 v = keys4(j);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) gp[j] += v[e] >= tk[k] ? 1u << (8 * e) : 0u;
-        }
-        continue;
-      }
+      if (need[k] == 0) continue;   // uniform
       // ties per (chunk, wavefront): index order is chunk-major, then wavefront,
       // lane and element
 #pragma unroll
@@ -795,21 +911,28 @@ __global__ __launch_bounds__(kThreads) void select_lds_kernel(const float* __res
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const bool ge = eq[e] ? before >= need[k] : v[e] > tk[k];
-          gp[j] += ge ? 1u << (8 * e) : 0u;
+          gp[j] += (eq[e] && before >= need[k]) ? 1u << (8 * e) : 0u;
           before += eq[e] ? 1 : 0;
         }
       }
       __syncthreads();   // tie_pre is reused by the next boundary
     }
-    uint8_t* out = group_out + (size_t)b * N;
+    __syncthreads();   // the shared state (keys included) is rewritten for the next row
+  }
+  // the last row's groups
+  const int32_t last = blockIdx.x + ((B - 1 - (int32_t)blockIdx.x) / (int32_t)gridDim.x) * gridDim.x;
+  if ((int32_t)blockIdx.x < B) {
+    uint8_t* out = group_out + (size_t)last * N;
     const bool aligned4 = (reinterpret_cast<uintptr_t>(out) & 3u) == 0u;
+    const int tid = threadIdx.x;
 #pragma unroll
     for (int j = 0; j < kV; ++j) {
       const int32_t n = 4 * (tid + j * kThreads);
-      if (n < N) store_groups(out, n, N, gp[j], aligned4);
+      if (aligned4 && 4 * (j + 1) * kThreads <= N)   // uniform
+        *reinterpret_cast<uint32_t*>(out + n) = gp[j];
+      else if (n < N)
+        store_groups(out, n, N, gp[j], aligned4);
     }
-    __syncthreads();   // the shared state (keys included) is rewritten for the next row
   }
 }
 
