@@ -91,7 +91,7 @@ static int check_rejections(void) {
          HSA_ERR_ARG);
   EXPECT(hsa_attn_active(DEV, DEV, DEV, DEV, 10, 100, 2, 64, 0.1f, (hsa_dtype)7, NULL, 0, NULL),
          HSA_ERR_DTYPE);
-  EXPECT(hsa_attn_active_noalloc(DEV, DEV, DEV, DEV, 2048, 75600, 40, 128, 0.088f, HSA_BF16, NULL),
+  EXPECT(hsa_attn_active_noalloc(DEV, DEV, DEV, DEV, 256, 75600, 200, 128, 0.088f, HSA_BF16, NULL),
          HSA_ERR_TOO_LARGE);
   EXPECT(hsa_attn_active_noalloc(NULL, DEV, DEV, DEV, 8, 64, 2, 128, 0.088f, HSA_BF16, NULL), HSA_ERR_ARG);
   EXPECT(hsa_euler((float *)DEV, (float *)DEV, (float *)DEV, (float *)DEV, (int32_t *)DEV, 100, 6, -0.1f,

@@ -53,7 +53,7 @@ def test_noalloc_attention_validates_on_the_host():
                     .replace("(size_t)", ""))) == H.NOALLOC_SCRATCH_BYTES
     L = H.load()
     fake = 4096                                  # aligned, never dereferenced on these paths
-    nA, nkv, Hh, Dh = 2048, 75600, 40, 128       # 82.5 MiB of partials
+    nA, nkv, Hh, Dh = 256, 75600, 200, 128       # 180 MiB of partials (14 KV splits per item)
     assert H.hsa_attn_workspace_size(nA, nkv, Hh, Dh) > H.NOALLOC_SCRATCH_BYTES
     assert L.hsa_attn_active_noalloc(fake, fake, fake, fake, nA, nkv, Hh, Dh, 0.088, 1, None) == -8
     assert L.hsa_attn_active_noalloc(None, fake, fake, fake, 8, 64, 2, 128, 0.088, 1, None) == -1

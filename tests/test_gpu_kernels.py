@@ -529,6 +529,23 @@ def test_attention_bf16(nA, nkv, Dh):
     assert err < 1e-2
 
 
+@pytest.mark.parametrize("Dh", [128, 64])
+def test_attention_bf16_whole_and_split_items(Dh):
+    """More (query tile, head) items than one round of the chip: 24 heads x
+    11 query tiles = 264 items, of which 256 run whole over the KV range and
+    the last 8 (head 23, query tiles 3..10) in KV parts merged afterwards.
+    Sampled rows against the oracle; every sampled row past query 768 takes
+    head 23 from merged partials and the other heads from whole items."""
+    nA, nkv, Hh = 2816, 4096, 24
+    say(f"attention bf16 whole + split items Dh={Dh}")
+    rs = np.random.default_rng(41 + Dh)
+    q, k, v = (bf(rs.standard_normal((n, Hh * Dh))) for n in (nA, nkv, nkv))
+    o = torch.empty(nA, Hh * Dh, dtype=torch.bfloat16, device=DEV)
+    H.hsa_attn_active(dev(q, torch.bfloat16), dev(k, torch.bfloat16), dev(v, torch.bfloat16), o, Hh, Dh)
+    rows = np.concatenate([np.arange(0, 8), rs.choice(np.arange(768, nA), 40, replace=False), [nA - 1]])
+    assert_rows_close(host(o)[rows], O.attention(q[rows], k, v, Hh, Dh), TOL_BF16, "attention rows")
+
+
 @pytest.mark.parametrize("nA,nkv,Dh", [(1, 1, 64), (77, 256, 64), (256, 256, 64), (50, 300, 128)])
 def test_attention_f32(nA, nkv, Dh):
     _attn_case(nA, nkv, 2, Dh, torch.float32, 1e-5)

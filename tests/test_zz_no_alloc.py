@@ -51,8 +51,9 @@ def test_noalloc_attention_matches_workspace_entry_point():
 
 
 def test_noalloc_attention_rejects_a_problem_past_its_scratch():
-    # 40 heads x 128 over 75600 rows with 2048 queries: the KV split needs 82.5 MiB.
-    nA, nkv, Hh, Dh = 2048, 75600, 40, 128
+    # 200 heads x 128 over 75600 rows with 256 queries: every (query tile, head)
+    # item is split 14 ways over the KV range, 180 MiB of partials.
+    nA, nkv, Hh, Dh = 256, 75600, 200, 128
     assert H.hsa_attn_workspace_size(nA, nkv, Hh, Dh) > H.NOALLOC_SCRATCH_BYTES
     q = torch.zeros(nA, Hh * Dh, dtype=torch.bfloat16, device=DEV)
     kv = torch.zeros(nkv, Hh * Dh, dtype=torch.bfloat16, device=DEV)

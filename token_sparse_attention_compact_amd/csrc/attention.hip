@@ -38,12 +38,16 @@
 //    O and l are then rescaled, which is exact after the final division.
 //    Row sums are float32 adds (v_dot2 over the packed pairs would be fewer
 //    instructions but holds up the MFMA issue far more).
-//  * When |A_i| is small the KV range is split across workgroups; the
-//    partials (O/l in bf16, max, sum) are merged in a fixed split order
-//    (deterministic).
-//  * Workgroup ids are remapped so each XCD runs a contiguous range of
-//    (split, head, query tile): the workgroups sharing an XCD's L2 stream
-//    the same head's K/V at the same time.
+//  * Work items are (query tile, head) pairs.  When they do not fill whole
+//    rounds of the chip, the first n_full items (whole rounds) run over the
+//    full KV range and the remaining ones are split over the KV range into
+//    `splits` parts, whose partials (O/l in bf16, max, sum) are merged in a
+//    fixed split order (deterministic).  At 384 items on 256 CUs: 256 whole
+//    items, then 128 items in two halves, so the chip stays full to the end
+//    and only a third of the rows go through partials.
+//  * Workgroup ids are remapped (within the whole and the split segment) so
+//    each XCD runs a contiguous range of items: the workgroups sharing an
+//    XCD's L2 stream the same head's K/V at the same time.
 // float32: a plain LDS-tiled kernel (float32 arithmetic).
 #include "common.h"
 
@@ -160,21 +164,27 @@ template <int DH_>
 __device__ __forceinline__ void attn_bf16_body(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     bf16* __restrict__ o, bf16* __restrict__ part_o, float* __restrict__ part_ml, int32_t nA,
-    int32_t nkv, int32_t H, float c, int32_t n_qt, int32_t splits, int32_t tiles_per_split,
-    char* smem) {
+    int32_t nkv, int32_t H, float c, int32_t n_qt, int32_t n_full, int32_t splits,
+    int32_t tiles_per_split, char* smem) {
   typedef AttnShape<DH_> S;
   constexpr int DH = S::DH, ROWB = S::ROWB, TILEB = S::TILEB, LOADS = S::LOADS;
   constexpr int NS = S::NS, NDB = S::NDB, EPS = S::EPS;
   const char* const sK = smem;
-  const char* const sV = smem + NST * TILEB;
   const uint32_t sK_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
   const uint32_t sV_lds = sK_lds + NST * TILEB;
 
-  const int32_t total = n_qt * H * splits;
-  const int32_t t = xcd_remap(blockIdx.x, total);
-  const int32_t qt = t % n_qt;
-  const int32_t h = (t / n_qt) % H;
-  const int32_t sp = t / (n_qt * H);
+  // item i = qt + n_qt * h; items below n_full whole, the rest in `splits`
+  // parts (part sp of split item n_full + il at workgroup n_full + sp * L + il)
+  const int32_t n_items = n_qt * H;
+  const int32_t L = n_items - n_full;
+  const int32_t bid = blockIdx.x;
+  const bool split = bid >= n_full;
+  const int32_t t = split ? xcd_remap(bid - n_full, L * splits) : xcd_remap(bid, n_full);
+  const int32_t il = split ? t % L : 0;             // index among the split items
+  const int32_t sp = split ? t / L : 0;
+  const int32_t item = split ? n_full + il : t;
+  const int32_t qt = item % n_qt;
+  const int32_t h = item / n_qt;
   const int32_t D = H * DH;
 
   const int tid = threadIdx.x;
@@ -183,8 +193,8 @@ __device__ __forceinline__ void attn_bf16_body(
   const int half = lane >> 5;
   const int l32 = lane & 31;
 
-  const int32_t kv_begin = sp * tiles_per_split * BKV;
-  const int32_t kv_end = min(nkv, kv_begin + tiles_per_split * BKV);
+  const int32_t kv_begin = split ? sp * tiles_per_split * BKV : 0;
+  const int32_t kv_end = split ? min(nkv, kv_begin + tiles_per_split * BKV) : nkv;
   const int32_t ntiles = (kv_end - kv_begin + BKV - 1) / BKV;
 
   // ---- per-lane load offsets (bytes within a tile of this head), fixed for all tiles
@@ -220,11 +230,16 @@ __device__ __forceinline__ void attn_bf16_body(
   // V (transposing reads): 16-lane group g points at keys kbase + i/4, dims d0 + 4*(i%4)
   const int grp = lane >> 4, gi = lane & 15;
   const int vrow = 4 * (grp >> 1) + (gi >> 2);   // key within a 8-key step (plus 16*jp + 8*second + 32*kb)
-  uint32_t voffr[DH / 32];
+  // LDS byte address of this lane's V read in stage 0, sub-tile 0, with the
+  // V region's base (64 KiB at Dh = 128) folded in and hidden from the
+  // compiler, so a read's stage and key offsets (< 64 KiB) go into the
+  // instruction's offset field instead of an add per read
+  uint32_t vrd[DH / 32];
 #pragma unroll
   for (int db = 0; db < DH / 32; ++db) {
     const int chunk = 4 * db + 2 * (grp & 1) + ((gi & 3) >> 1);
-    voffr[db] = (uint32_t)(vrow * ROWB + v_pos<DH>(vrow, chunk) * 16 + 8 * (gi & 1));
+    vrd[db] = sV_lds + (uint32_t)(vrow * ROWB + v_pos<DH>(vrow, chunk) * 16 + 8 * (gi & 1));
+    asm volatile("" : "+v"(vrd[db]));
   }
 
   f32x16 acc_o[DH / 32];
@@ -289,7 +304,7 @@ __device__ __forceinline__ void attn_bf16_body(
   // P^T = exp2(s) as bf16 MFMA fragments (packed pairs); row-sum partial in
   // float32 over two independent chains
   auto probs = [&](const f32x16& s, u32x4* pw) {
-    float l2[2] = {0.f, 0.f};
+    float l2[2] = {-0.f, -0.f};   // -0 + x == x: the first adds fold away
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
       const float p0 = __builtin_amdgcn_exp2f(s[r]);
@@ -301,16 +316,16 @@ __device__ __forceinline__ void attn_bf16_body(
     return l2[0] + l2[1];
   };
   // O^T += V^T P^T over the sub-tile: k-step jp covers keys 16*jp + 4*half + {0..3, 8..11}
-  auto vfrag = [&](const char* vt, int j) {   // j: k-step jp = j/NDB, dims block db = j%NDB
-    const int jp = j / NDB, db = j % NDB;
-    const char* vk = vt + 16 * jp * ROWB;
-    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vk + voffr[db]));
-    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vk + 8 * ROWB + voffr[db]));
+  auto vfrag = [&](uint32_t vt, int j) {   // vt: sub-tile offset in the V region; j: k-step
+    const int jp = j / NDB, db = j % NDB;  // jp = j / NDB, dims block db = j % NDB
+    const uint32_t a = vrd[db] + vt + 16 * jp * ROWB;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)a);
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(a + 8 * ROWB));
     const u32x4 raw = {__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
                        __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]};
     return __builtin_bit_cast(bf16x8, raw);
   };
-  auto accumulate = [&](const char* vt, const u32x4* pw) {
+  auto accumulate = [&](uint32_t vt, const u32x4* pw) {
     bf16x8 vf[2];
     vf[0] = vfrag(vt, 0);
 #pragma unroll
@@ -321,8 +336,9 @@ __device__ __forceinline__ void attn_bf16_body(
     }
   };
   // LDS addresses of sub-tile u's K and V rows
-  auto k_sub = [&](int u) { return sK + ((u >> 1) % NST) * TILEB + (u & 1) * SUB * ROWB; };
-  auto v_sub = [&](int u) { return sV + ((u >> 1) % NST) * TILEB + (u & 1) * SUB * ROWB; };
+  static_assert((NST & (NST - 1)) == 0, "ring of a power-of-two stages");
+  auto k_sub = [&](int u) { return sK + ((u >> 1) & (NST - 1)) * TILEB + (u & 1) * SUB * ROWB; };
+  auto v_sub = [&](int u) { return (uint32_t)(((u >> 1) & (NST - 1)) * TILEB + (u & 1) * SUB * ROWB); };
 
   // Q in registers before the LDS pipeline starts (a builtin, so the compiler's own
   // wait accounting sees it and adds no vmcnt waits for Q inside the loop)
@@ -348,17 +364,17 @@ __device__ __forceinline__ void attn_bf16_body(
       if (it + 2 < ntiles) wait_tiles_barrier<DH, 1>();
       else wait_tiles_barrier<DH, 0>();
       if (it + NST - 1 < ntiles) {
-        const int ns = (it + NST - 1) % NST;
+        const int ns = (it + NST - 1) & (NST - 1);
         issue_tile<DH>(k, v, kv_begin + (it + NST - 1) * BKV, nkv, D, h, sK_lds + ns * TILEB,
                    sV_lds + ns * TILEB, voff_k, voff_v, wave);
       }
     }
     const char* kt = k_sub(u + 1);
-    const char* vt = v_sub(u - 1);
+    const uint32_t vt = v_sub(u - 1);
     bf16x8 kf[2], vf[2];
     kf[0] = kfrag(kt, 0);
     if (pv) vf[0] = vfrag(vt, 0);
-    float l2[2] = {0.f, 0.f};
+    float l2[2] = {-0.f, -0.f};   // -0 + x == x: the first adds fold away
     // slot j: S^T MFMA j of sub-tile u+1, the first EPS/2 exponentials of the
     // slot's score elements of sub-tile u, PV MFMA j of sub-tile u-1, the rest
     // of them with their bf16 packing and the row-sum adds
@@ -429,6 +445,18 @@ __device__ __forceinline__ void attn_bf16_body(
   } else {
     step(sa, sb, pwa, pwb, 0, false);
     int u = 1;
+    // whole ring cycles (2 * NST sub-tiles) unrolled from u = 1 mod 2 * NST:
+    // every stage offset is then a constant that the LDS reads carry as an
+    // immediate, instead of address arithmetic in each step
+    for (int cyc = 0; 2 * NST * cyc + 2 * NST + 1 < nsub; ++cyc) {
+      const int u0 = 2 * NST * cyc + 1;
+#pragma unroll
+      for (int c = 0; c < 2 * NST; c += 2) {
+        step(sb, sa, pwb, pwa, u0 + c, true);
+        step(sa, sb, pwa, pwb, u0 + c + 1, true);
+      }
+      u = u0 + 2 * NST;
+    }
     for (; u + 2 < nsub; u += 2) {
       step(sb, sa, pwb, pwa, u, true);
       step(sa, sb, pwa, pwb, u + 1, true);
@@ -451,8 +479,9 @@ __device__ __forceinline__ void attn_bf16_body(
   // acc_o[db][r] <-> dim db*32 + 8*(r/4) + 4*half + r%4, query l32; the
   // split partials are stored normalised (O / l, bf16) with their (m, l)
   const float inv = 1.0f / l_tot;
-  bf16* orow = splits == 1 ? o + (size_t)qi * D + h * DH
-                           : part_o + ((size_t)(sp * H + h) * nA + qi) * DH;
+  // partial row of a split item: (part, split item, query within the tile)
+  const size_t prow = ((size_t)sp * L + il) * BQ + (qi - qt * BQ);
+  bf16* orow = split ? part_o + prow * DH : o + (size_t)qi * D + h * DH;
 #pragma unroll
   for (int db = 0; db < DH / 32; ++db)
 #pragma unroll
@@ -462,8 +491,7 @@ __device__ __forceinline__ void attn_bf16_body(
       for (int e = 0; e < 4; ++e) w4[e] = (bf16)(acc_o[db][4 * j + e] * inv);
       *reinterpret_cast<bf16x4*>(orow + db * 32 + 8 * j + 4 * half) = w4;
     }
-  if (splits > 1 && half == 0) {
-    const size_t prow = (size_t)(sp * H + h) * nA + qi;
+  if (split && half == 0) {
     part_ml[prow * 2 + 0] = m_run;
     part_ml[prow * 2 + 1] = l_tot;
   }
@@ -472,46 +500,56 @@ __device__ __forceinline__ void attn_bf16_body(
 #define HSA_ATTN_ARGS                                                                        \
   const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,        \
       bf16 *__restrict__ o, bf16 *__restrict__ part_o, float *__restrict__ part_ml, int32_t nA, \
-      int32_t nkv, int32_t H, float c, int32_t n_qt, int32_t splits, int32_t tiles_per_split
+      int32_t nkv, int32_t H, float c, int32_t n_qt, int32_t n_full, int32_t splits,         \
+      int32_t tiles_per_split
 
 __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_d128_kernel(HSA_ATTN_ARGS) {
   __shared__ __attribute__((aligned(1024))) char smem[2 * NST * AttnShape<128>::TILEB];
-  attn_bf16_body<128>(q, k, v, o, part_o, part_ml, nA, nkv, H, c, n_qt, splits, tiles_per_split, smem);
+  attn_bf16_body<128>(q, k, v, o, part_o, part_ml, nA, nkv, H, c, n_qt, n_full, splits,
+                      tiles_per_split, smem);
 }
 
 __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_d64_kernel(HSA_ATTN_ARGS) {
   __shared__ __attribute__((aligned(1024))) char smem[2 * NST * AttnShape<64>::TILEB];
-  attn_bf16_body<64>(q, k, v, o, part_o, part_ml, nA, nkv, H, c, n_qt, splits, tiles_per_split, smem);
+  attn_bf16_body<64>(q, k, v, o, part_o, part_ml, nA, nkv, H, c, n_qt, n_full, splits,
+                     tiles_per_split, smem);
 }
 #undef HSA_ATTN_ARGS
 
 // Merge split partials in split order: with weights w_s = l_s 2^(m_s - M),
-// O = sum_s w_s (O_s / l_s) / sum_s w_s.  One thread per 8 dims of a
-// (query, head) row: 16-byte partial reads and output writes.
+// O = sum_s w_s (O_s / l_s) / sum_s w_s.  One thread per 8 dims of a query row
+// of a split item (items n_full .. n_qt * H - 1): 16-byte partial reads and
+// output writes.
 template <int HD>
 __global__ __launch_bounds__(256) void attn_merge_kernel(const bf16* __restrict__ part_o,
                                                          const float* __restrict__ part_ml,
                                                          bf16* __restrict__ o, int32_t nA,
-                                                         int32_t H, int32_t splits) {
+                                                         int32_t H, int32_t n_qt, int32_t n_full,
+                                                         int32_t splits) {
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t rows = (int64_t)nA * H;
-  const int64_t row = t / (HD / 8);
+  const int32_t L = n_qt * H - n_full;
+  const int64_t rows = (int64_t)L * BQ;
+  const int64_t row = t / (HD / 8);   // il * BQ + query within the tile
   const int d8 = (int)(t % (HD / 8)) * 8;
   if (row >= rows) return;
-  const int32_t qi = (int32_t)(row / H), h = (int32_t)(row % H);
+  const int32_t il = (int32_t)(row / BQ), qin = (int32_t)(row % BQ);
+  const int32_t item = n_full + il;
+  const int32_t qt = item % n_qt, h = item / n_qt;
+  const int32_t qi = qt * BQ + qin;
+  if (qi >= nA) return;
   float M = -INFINITY;
-  for (int s = 0; s < splits; ++s) M = fmaxf(M, part_ml[((size_t)(s * H + h) * nA + qi) * 2]);
-  float L = 0.f;
+  for (int s = 0; s < splits; ++s) M = fmaxf(M, part_ml[((size_t)s * rows + row) * 2]);
+  float Lsum = 0.f;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int s = 0; s < splits; ++s) {
-    const size_t pr = (size_t)(s * H + h) * nA + qi;
+    const size_t pr = (size_t)s * rows + row;
     const float w = __builtin_amdgcn_exp2f(part_ml[pr * 2] - M) * part_ml[pr * 2 + 1];
-    L += w;
+    Lsum += w;
     const bf16x8 po = *reinterpret_cast<const bf16x8*>(part_o + pr * HD + d8);
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(w, (float)po[e], acc[e]);
   }
-  const float inv = 1.0f / L;
+  const float inv = 1.0f / Lsum;
   bf16x8 w8;
 #pragma unroll
   for (int e = 0; e < 8; ++e) w8[e] = (bf16)(acc[e] * inv);
@@ -576,30 +614,47 @@ __global__ __launch_bounds__(256) void attn_plain_kernel(const T* __restrict__ q
 }
 
 struct SplitPlan {
-  int32_t n_qt, splits, tiles_per_split;
+  int32_t n_qt, n_full, splits, tiles_per_split;
+  // partial rows: every part of every split item, BQ rows each
+  int64_t part_rows(int32_t H) const {
+    return splits > 1 ? (int64_t)splits * (n_qt * H - n_full) * BQ : 0;
+  }
 };
 
+// One workgroup per CU at a time (128 KiB of LDS each).  Items (query tile,
+// head) take `ntiles` KV tiles each.  Candidates: n_full items in whole
+// rounds of 256 run unsplit, the remaining L items split into s parts; the
+// cost is the rounds times the tiles per workgroup, plus one tile per
+// partial row block merged.  The cheapest candidate wins; ties go to the
+// fewest split items, then the fewest parts.  Every part covers >= 8 tiles.
 SplitPlan plan_split(int32_t nA, int32_t nkv, int32_t H) {
-  // One workgroup per CU at a time (128 KiB of LDS each): pick the number of
-  // KV splits s that minimises (rounds of 256 workgroups) x (tiles per split),
-  // the smallest such s (least merge work), with at least 8 tiles per split.
   constexpr int32_t kCus = 256;
   SplitPlan p;
   p.n_qt = cdiv(nA, BQ);
   const int32_t ntiles = cdiv(nkv, BKV);
-  const int32_t base = p.n_qt * H;
+  const int32_t items = p.n_qt * H;
   const int32_t smax = max(1, min(16, ntiles / 8));
   int64_t best = -1;
-  int32_t best_s = 1;
-  for (int32_t s = 1; s <= smax; ++s) {
-    const int64_t cost = (int64_t)cdiv((int64_t)base * s, kCus) * cdiv(ntiles, s);
-    if (best < 0 || cost < best) {
-      best = cost;
-      best_s = s;
+  p.n_full = items;
+  p.splits = 1;
+  for (int32_t nf = (items / kCus) * kCus; nf >= 0; nf -= kCus) {
+    const int32_t L = items - nf;
+    for (int32_t s = 1; s <= smax; ++s) {
+      if (L == 0 && s > 1) break;
+      const int32_t tps = cdiv(ntiles, s);
+      const int64_t cost = (int64_t)(nf / kCus) * ntiles + (int64_t)cdiv((int64_t)L * s, kCus) * tps +
+                           (s > 1 ? (int64_t)L * s / kCus : 0);
+      if (best < 0 || cost < best) {
+        best = cost;
+        p.n_full = nf;
+        p.splits = s;
+      }
     }
   }
-  p.tiles_per_split = cdiv(ntiles, best_s);
+  if (p.splits == 1) p.n_full = items;   // nothing split
+  p.tiles_per_split = cdiv(ntiles, p.splits);
   p.splits = cdiv(ntiles, p.tiles_per_split);
+  if (p.splits == 1) p.n_full = items;
   return p;
 }
 
@@ -611,7 +666,7 @@ size_t attn_workspace_bytes(int32_t n_active, int32_t n_kv, int32_t H, int32_t D
   if (n_active <= 0 || n_kv <= 0) return 0;
   const SplitPlan p = plan_split(n_active, n_kv, H);
   if (p.splits <= 1) return 0;
-  const size_t rows = (size_t)p.splits * H * n_active;
+  const size_t rows = (size_t)p.part_rows(H);
   return align_up(rows * Dh * sizeof(bf16), 256) + rows * 2 * sizeof(float);
 }
 
@@ -624,28 +679,30 @@ hsa_status launch_attention(const void* q, const void* k, const void* v, void* o
     bf16* part_o = nullptr;
     float* part_ml = nullptr;
     if (p.splits > 1) {
-      const size_t rows = (size_t)p.splits * H * n_active;
+      const size_t rows = (size_t)p.part_rows(H);
       if (ws == nullptr || ws_bytes < attn_workspace_bytes(n_active, n_kv, H, Dh))
         return HSA_ERR_WORKSPACE;
       part_o = (bf16*)ws;
       part_ml = (float*)((char*)ws + align_up(rows * Dh * sizeof(bf16), 256));
     }
-    const int32_t total = p.n_qt * H * p.splits;
+    const int32_t total = p.n_full + (p.n_qt * H - p.n_full) * p.splits;
     if (Dh == 128)
       attn_bf16_d128_kernel<<<total, kAttnThreads, 0, s>>>(
           (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, part_o, part_ml, n_active,
-          n_kv, H, scale * kLog2e, p.n_qt, p.splits, p.tiles_per_split);
+          n_kv, H, scale * kLog2e, p.n_qt, p.n_full, p.splits, p.tiles_per_split);
     else
       attn_bf16_d64_kernel<<<total, kAttnThreads, 0, s>>>(
           (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, part_o, part_ml, n_active,
-          n_kv, H, scale * kLog2e, p.n_qt, p.splits, p.tiles_per_split);
+          n_kv, H, scale * kLog2e, p.n_qt, p.n_full, p.splits, p.tiles_per_split);
     if (p.splits > 1) {
-      const int64_t threads = (int64_t)n_active * H * (Dh / 8);
+      const int64_t threads = (int64_t)(p.n_qt * H - p.n_full) * BQ * (Dh / 8);
       const unsigned blocks = (unsigned)((threads + 255) / 256);
       if (Dh == 128)
-        attn_merge_kernel<128><<<blocks, 256, 0, s>>>(part_o, part_ml, (bf16*)o, n_active, H, p.splits);
+        attn_merge_kernel<128><<<blocks, 256, 0, s>>>(part_o, part_ml, (bf16*)o, n_active, H, p.n_qt,
+                                                       p.n_full, p.splits);
       else
-        attn_merge_kernel<64><<<blocks, 256, 0, s>>>(part_o, part_ml, (bf16*)o, n_active, H, p.splits);
+        attn_merge_kernel<64><<<blocks, 256, 0, s>>>(part_o, part_ml, (bf16*)o, n_active, H, p.n_qt,
+                                                      p.n_full, p.splits);
     }
     return launch_status();
   }
