@@ -159,11 +159,15 @@ def _select_batch_case(score, counts):
 
 
 @pytest.mark.parametrize("B,N,K", [(1, 1, 2), (3, 10, 2), (5, 1001, 3), (4, 1000, 8), (2, 4099, 5),
-                                   (3, 32760, 3), (2, 32768, 4), (2, 40000, 3), (6, 513, 1)])
+                                   (3, 32760, 3), (2, 32768, 4), (2, 40000, 3), (6, 513, 1),
+                                   (5, 1000, 2), (300, 1000, 3), (260, 2052, 2), (270, 1001, 3)])
 def test_select_batch_bit_exact(B, N, K):
     """Each row of a batch against the oracle's selection of that row: rows
     staged in LDS (N <= 32768) and read from memory (N = 40000), rows whose
-    start is not 16- or 4-byte aligned (N odd), ties and special values."""
+    start is not 16- or 4-byte aligned (N odd), ties and special values.
+    More rows than CUs (B = 260..300): a workgroup ranks several rows, each
+    loaded while the previous one is ranked (straight into LDS when rows are
+    16-byte aligned, N % 4 == 0; into registers otherwise)."""
     say(f"select batch B={B} N={N} K={K}")
     rs = np.random.default_rng(B * 100000 + N * 10 + K)
     cuts = np.sort(rs.integers(0, N + 1, K - 1))

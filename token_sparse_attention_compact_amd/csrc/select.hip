@@ -589,18 +589,36 @@ __global__ __launch_bounds__(kThreads) void select_reg_kernel(const float* __res
   }
 }
 
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// 16 bytes per lane from a buffer straight into LDS at lds_addr + 16 * lane,
+// after every LDS read of this wavefront has returned (the loads may land on
+// what those reads were reading).  The instruction has no register result;
+// its completion is waited for with vmcnt(0).
+__device__ __forceinline__ void lds_dma16_after_reads(uint32_t lds_addr, uint32_t voff, i32x4_t rsrc) {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 // One or two group boundaries (K <= 3, every workload here), rows of up to
-// 32768 tokens: the same passes as select_reg_kernel, but the row's keys sit
-// in LDS (token order, 128 KiB) and every pass reads them from there, so a
-// thread's registers hold only the next row's raw scores, loaded while this
-// row is ranked.  Each workgroup takes rows blockIdx.x, blockIdx.x +
-// gridDim.x, ...; slots past a row's end take the row's largest key.
-template <int NB>
+// 32768 tokens: the same passes as select_reg_kernel.  Each workgroup takes
+// rows blockIdx.x, blockIdx.x + gridDim.x, ...; slots past a row's end take
+// the row's largest key.  The next row is read while this one is ranked:
+//  * DMA (rows 16-byte aligned): the next row's scores go straight from HBM
+//    into LDS (token order, 128 KiB; each wavefront loads exactly the chunks
+//    its own threads read back), and the row being ranked is held as keys in
+//    registers, so no pass reads LDS for keys;
+//  * otherwise: the next row's scores load into registers and the row being
+//    ranked sits in LDS as keys, which every pass reads from there.
+template <int NB, bool DMA>
 __global__ __launch_bounds__(kThreads) void select_lds_kernel(const float* __restrict__ score,
                                                               int32_t B, int32_t N, Counts cnt,
                                                               uint8_t* __restrict__ group_out) {
   static_assert(NB >= 1 && NB <= 2, "LDS holds two boundaries' histograms and lists");
-  __shared__ __attribute__((aligned(16))) uint32_t s_key[4 * kV * kThreads];
+  __shared__ __attribute__((aligned(16))) uint32_t s_key[4 * kV * kThreads];   // keys, or (DMA) the next row's scores
   __shared__ int32_t hist[2][kBins];   // first pass: two copies by lane; later: one per boundary
   __shared__ __attribute__((aligned(16))) uint32_t s_list[NB][kList];
   __shared__ uint32_t s_small[NB][kWave];
@@ -622,11 +640,25 @@ __global__ __launch_bounds__(kThreads) void select_lds_kernel(const float* __res
   auto live = [&](int k) { return bnd[k] < N; };   // a boundary at N: no token passes it
   auto bound_of = [&](int k) { return NB == 1 || k == 0 ? bnd[0] : bnd[NB - 1]; };
 
-  uint32_t raw[kV][4];
+  uint32_t raw[kV][4];   // the next row's scores, or (DMA) this row's keys
   uint32_t gp[kV];   // group bytes of the previous row, 4 per chunk, stored once
                      // this row's scores have arrived (so that no wait for the
                      // next row's loads also waits for these stores)
-  if (blockIdx.x < (uint32_t)B) load_row_bits(score + (size_t)blockIdx.x * N, N, raw);
+  const uint32_t s_key_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint32_t*)s_key;
+  // DMA: row r's scores into s_key, each wavefront its own threads' chunks
+  auto dma_row = [&](int32_t r) {
+    const uint64_t a = reinterpret_cast<uint64_t>(score + (size_t)r * N);
+    const i32x4_t rsrc = {(int32_t)(uint32_t)a, (int32_t)(uint32_t)(a >> 32), N * 4, 0x00020000};
+    const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+#pragma unroll
+    for (int j = 0; j < kV; ++j)
+      lds_dma16_after_reads(s_key_lds + 16u * (uint32_t)(w * kWave + j * kThreads),
+                            16u * (uint32_t)(threadIdx.x + j * kThreads), rsrc);
+  };
+  if (blockIdx.x < (uint32_t)B) {
+    if constexpr (DMA) dma_row(blockIdx.x);
+    else load_row_bits(score + (size_t)blockIdx.x * N, N, raw);
+  }
   for (int32_t b = blockIdx.x; b < B; b += gridDim.x) {
     // The thread id is made opaque per row, so that the addresses derived
     // from it are recomputed in each row instead of held in registers across
@@ -637,8 +669,20 @@ __global__ __launch_bounds__(kThreads) void select_lds_kernel(const float* __res
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    auto keys4 = [&](int j) { return *reinterpret_cast<const u32x4*>(&s_key[4 * (tid + j * kThreads)]); };
-    // ---- keys, the smallest and largest; into LDS; the next row's loads go out
+    auto keys4 = [&](int j) {
+      if constexpr (DMA) return u32x4{raw[j][0], raw[j][1], raw[j][2], raw[j][3]};
+      else return *reinterpret_cast<const u32x4*>(&s_key[4 * (tid + j * kThreads)]);
+    };
+    if constexpr (DMA) {   // this row's scores, landed in LDS while the previous row was ranked
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int j = 0; j < kV; ++j) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(&s_key[4 * (tid + j * kThreads)]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) raw[j][e] = v[e];
+      }
+    }
+    // ---- keys, the smallest and largest; (DMA) the next row's loads go out
     uint32_t kmin = kPad, kmax = 0u;
 #pragma unroll
     for (int j = 0; j < kV; ++j) {
@@ -658,6 +702,9 @@ __global__ __launch_bounds__(kThreads) void select_lds_kernel(const float* __res
           kmax = max(kmax, raw[j][e]);
         }
       }
+    }
+    if constexpr (DMA) {
+      if (b + (int32_t)gridDim.x < B) dma_row(b + gridDim.x);
     }
     if (b != (int32_t)blockIdx.x) {
       // the stores take an address that depends on every key, so that they
@@ -705,9 +752,15 @@ __global__ __launch_bounds__(kThreads) void select_lds_kernel(const float* __res
       const bool whole = 4 * (j + 1) * kThreads <= N;   // uniform
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] = (!whole && raw[j][e] == kPad) ? kmax : raw[j][e];
-      *reinterpret_cast<u32x4*>(&s_key[4 * (tid + j * kThreads)]) = v;
+      if constexpr (DMA) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) raw[j][e] = v[e];
+      } else {
+        *reinterpret_cast<u32x4*>(&s_key[4 * (tid + j * kThreads)]) = v;
+      }
     }
-    if (b + (int32_t)gridDim.x < B) load_row_bits(score + (size_t)(b + gridDim.x) * N, N, raw);
+    if constexpr (!DMA)
+      if (b + (int32_t)gridDim.x < B) load_row_bits(score + (size_t)(b + gridDim.x) * N, N, raw);
     // bits below `lo` still differ between keys; every key has kmin's bits above
     const uint32_t diff = kmin ^ kmax;
     int lo = diff == 0u ? 0 : 32 - __clz(diff);
@@ -1055,9 +1108,17 @@ hsa_status launch_select(const float* score, int32_t B, int32_t N, const int32_t
     if (hipGetDevice(&dev) == hipSuccess)
       (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     const unsigned grid = (unsigned)(B < cus ? B : cus);
+    // rows start on 16-byte boundaries: the next row can be loaded into LDS directly
+    const bool dma = N % 4 == 0 && (reinterpret_cast<uintptr_t>(score) & 15u) == 0;
     switch (K - 1) {
-      case 1: select_lds_kernel<1><<<grid, kThreads, 0, s>>>(score, B, N, c, group_out); break;
-      case 2: select_lds_kernel<2><<<grid, kThreads, 0, s>>>(score, B, N, c, group_out); break;
+      case 1:
+        if (dma) select_lds_kernel<1, true><<<grid, kThreads, 0, s>>>(score, B, N, c, group_out);
+        else select_lds_kernel<1, false><<<grid, kThreads, 0, s>>>(score, B, N, c, group_out);
+        break;
+      case 2:
+        if (dma) select_lds_kernel<2, true><<<grid, kThreads, 0, s>>>(score, B, N, c, group_out);
+        else select_lds_kernel<2, false><<<grid, kThreads, 0, s>>>(score, B, N, c, group_out);
+        break;
       case 3: select_reg_kernel<3><<<grid, kThreads, 0, s>>>(score, B, N, c, group_out); break;
       case 4: select_reg_kernel<4><<<grid, kThreads, 0, s>>>(score, B, N, c, group_out); break;
       case 5: select_reg_kernel<5><<<grid, kThreads, 0, s>>>(score, B, N, c, group_out); break;
