@@ -716,7 +716,7 @@ def oracle_dit_lite_run():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): this build has no "
+        print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): the library has no "
               f"multi-GPU path; the per-GPU kernel is what is measured.", file=sys.stderr)
         sys.exit(2)
     from token_sparse_attention_compact_amd import hsa as H

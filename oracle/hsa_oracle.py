@@ -12,7 +12,7 @@ the method's data are stored (latents, caches, activations handed from one
 operation to the next): float32 in float32 workloads, bfloat16 for the
 activations and caches of bfloat16 workloads (see `Store`).
 
-Readings where the pages leave a step open (each is listed in the design doc):
+Readings where the pages leave a step open:
   * iteration index i is 0-based, i in [0, T): every group is active at i = 0;
   * sigma_i = 1 - i/T;
   * block = pre-LayerNorm (no affine, eps 1e-6) multi-head self-attention
