@@ -160,7 +160,8 @@ def _select_batch_case(score, counts):
 
 @pytest.mark.parametrize("B,N,K", [(1, 1, 2), (3, 10, 2), (5, 1001, 3), (4, 1000, 8), (2, 4099, 5),
                                    (3, 32760, 3), (2, 32768, 4), (2, 40000, 3), (6, 513, 1),
-                                   (5, 1000, 2), (300, 1000, 3), (260, 2052, 2), (270, 1001, 3)])
+                                   (5, 1000, 2), (300, 1000, 3), (260, 2052, 2), (270, 1001, 3),
+                                   (3, 32768, 3), (2, 4, 2)])
 def test_select_batch_bit_exact(B, N, K):
     """Each row of a batch against the oracle's selection of that row: rows
     staged in LDS (N <= 32768) and read from memory (N = 40000), rows whose
@@ -547,6 +548,24 @@ def test_attention_bf16_whole_and_split_items(Dh):
     o = torch.empty(nA, Hh * Dh, dtype=torch.bfloat16, device=DEV)
     H.hsa_attn_active(dev(q, torch.bfloat16), dev(k, torch.bfloat16), dev(v, torch.bfloat16), o, Hh, Dh)
     rows = np.concatenate([np.arange(0, 8), rs.choice(np.arange(768, nA), 40, replace=False), [nA - 1]])
+    assert_rows_close(host(o)[rows], O.attention(q[rows], k, v, Hh, Dh), TOL_BF16, "attention rows")
+
+
+@pytest.mark.parametrize("nA,nkv,Hh", [(256 * 256, 4096, 1), (256 * 256 + 1, 4096, 1),
+                                       (256 * 255 + 1, 4096, 1), (256 * 512 + 300, 2048, 1)])
+def test_attention_bf16_split_plan_edges(nA, nkv, Hh):
+    """Edges of the whole/split plan with one head: exactly one round of 256
+    query-tile items (nothing split), one item more (that item, a last tile
+    holding a single query, split over the KV range), one round with a
+    ragged last tile, and two rounds plus a ragged item.  Sampled rows
+    (first, around the tile and round boundaries, last) against the oracle."""
+    say(f"attention bf16 plan edges nA={nA} nkv={nkv}")
+    Dh = 128
+    rs = np.random.default_rng(nA + nkv)
+    q, k, v = (bf(rs.standard_normal((n, Hh * Dh))) for n in (nA, nkv, nkv))
+    o = torch.empty(nA, Hh * Dh, dtype=torch.bfloat16, device=DEV)
+    H.hsa_attn_active(dev(q, torch.bfloat16), dev(k, torch.bfloat16), dev(v, torch.bfloat16), o, Hh, Dh)
+    rows = np.unique(np.clip(np.array([0, 1, 255, 256, 65535, 65536, nA - 2, nA - 1]), 0, nA - 1))
     assert_rows_close(host(o)[rows], O.attention(q[rows], k, v, Hh, Dh), TOL_BF16, "attention rows")
 
 
