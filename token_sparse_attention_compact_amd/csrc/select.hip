@@ -6,20 +6,28 @@
 // Deterministic radix select, one workgroup of 1024 threads per row of a
 // [B][N] batch (independent selections with the same counts):
 //   * each score maps to a 32-bit key that increases as the score decreases;
-//     for rows of up to 32768 tokens the keys stay in registers (thread t
-//     holds tokens 4 (t + 1024 j) + e), so the row crosses HBM once: 4N
-//     bytes of scores in, N bytes of groups out;
-//   * the first pass (top 11 key bits) histograms every key as it is loaded
-//     and serves every group boundary b_k (k = 1..K-1) at once; two more
-//     passes (11 and 10 bits) narrow each boundary to the key t_k of the token
-//     at rank b_k and the number need_k of tokens with key t_k that still rank
-//     before it (every boundary's histogram filled in the same sweep; only
-//     keys in a boundary's bucket are counted);
+//     for rows of up to 32768 tokens thread t holds tokens 4 (t + 1024 j) + e,
+//     so the row crosses HBM once: 4N bytes of scores in, N bytes of groups
+//     out.  Persistent workgroups (one per CU) walk the rows of the batch,
+//     loading the next row while the current one is ranked;
+//   * the smallest and largest key give the bits every key shares, and the
+//     digit passes start below them;
+//   * one or two boundaries (K <= 3, select_lds_kernel): a first pass of a
+//     12-bit digit over every key serves both boundaries; further 11-bit
+//     passes only while a boundary's bucket holds more keys than a quarter
+//     of its threads; then each bucket's keys go to an LDS list, which four
+//     threads per key rank by comparing every pair (rank_in_list).  This
+//     gives t_k, the key of the token at rank b_k, and need_k, the number of
+//     tokens with key t_k that still rank before it;
+//   * three to seven boundaries (select_reg_kernel): the same with an 11-bit
+//     first pass into four histogram copies, narrowing passes while a bucket
+//     exceeds 1024 keys, and each list finished by one wavefront
+//     (finish_bucket);
 //   * assignment: group = number of boundaries whose key the token's key
 //     reaches.  When some need_k > 0, the ties with t_k are split by their
 //     index-order position: ballots count them per (wavefront, 4096-token
 //     chunk), and one wavefront scans those counts.
-//   Longer rows take the same passes reading the scores from memory.
+//   Longer rows take three fixed passes, reading the scores from memory.
 // The result is unique, so it matches any correct implementation bit for bit.
 #include "common.h"
 
@@ -619,7 +627,7 @@ __global__ __launch_bounds__(kThreads) void select_lds_kernel(const float* __res
                                                               uint8_t* __restrict__ group_out) {
   static_assert(NB >= 1 && NB <= 2, "LDS holds two boundaries' histograms and lists");
   __shared__ __attribute__((aligned(16))) uint32_t s_key[4 * kV * kThreads];   // keys, or (DMA) the next row's scores
-  __shared__ int32_t hist[2][kBins];   // first pass: two copies by lane; later: one per boundary
+  __shared__ int32_t hist[2][kBins];   // first pass: one histogram of 4096 bins; later: one per boundary
   __shared__ __attribute__((aligned(16))) uint32_t s_list[NB][kList];
   __shared__ uint32_t s_small[NB][kWave];
   __shared__ int32_t wave_tmp[kWaves];
