@@ -187,6 +187,53 @@ def test_select_batch_bit_exact(B, N, K):
     _select_batch_case(s2, counts)
 
 
+def _score_rows(kind, rs, B, N):
+    """B rows of N scores of one distribution family (float32)."""
+    if kind == "uniform":
+        return rs.random((B, N)).astype(np.float32)
+    if kind == "abs_normal":
+        return np.abs(rs.standard_normal((B, N))).astype(np.float32)
+    if kind == "lognormal_wide":        # keys spread over many exponents
+        return np.exp(rs.standard_normal((B, N)) * 8).astype(np.float32)
+    if kind == "signed":                # both signs: the key's top bit differs
+        return rs.standard_normal((B, N)).astype(np.float32)
+    if kind == "narrow":                # all keys share their top 20-odd bits
+        return (1.0 + rs.random((B, N)) * 1e-4).astype(np.float32)
+    if kind == "few_values":            # heavy ties at every boundary
+        return rs.integers(0, 5, (B, N)).astype(np.float32)
+    if kind == "denormals":             # values below float32's normal range, and zeros of both signs
+        s = (rs.random((B, N)) * 1e-39).astype(np.float32)
+        s[:, ::7] = -0.0
+        s[:, 3::11] = 0.0
+        return s
+    if kind == "sorted":                # the bucket's keys in one chunk of the row
+        return np.sort(rs.random((B, N)), axis=1).astype(np.float32)
+    if kind == "specials":              # NaN, +-inf, +-0 mixed into normal scores
+        s = rs.standard_normal((B, N)).astype(np.float32)
+        m = rs.random((B, N))
+        s[m < 0.05] = np.nan
+        s[(m >= 0.05) & (m < 0.08)] = np.inf
+        s[(m >= 0.08) & (m < 0.1)] = -np.inf
+        s[(m >= 0.1) & (m < 0.12)] = -0.0
+        return s
+    raise ValueError(kind)
+
+
+@pytest.mark.parametrize("kind", ["uniform", "abs_normal", "lognormal_wide", "signed", "narrow",
+                                  "few_values", "denormals", "sorted", "specials"])
+def test_select_batch_distributions(kind):
+    """Score distributions that drive the digit passes differently (wide and
+    narrow key ranges, heavy ties, special values, denormals, sorted rows),
+    300 rows (more than the CUs: a workgroup ranks several rows, loading the
+    next while it ranks the current one) at an aligned and a ragged row
+    length, two and three groups; every row against the oracle."""
+    rs = np.random.default_rng(sum(ord(ch) for ch in kind))
+    for N, counts in ((2048, [512, 512, 1024]), (1999, [1000, 999])):
+        score = _score_rows(kind, rs, 300, N)
+        say(f"select distributions {kind} N={N}")
+        _select_batch_case(score, counts)
+
+
 def test_select_batch_rows_independent_and_match_single():
     """Row b of a batch equals hsa_select on that row alone, and a row's
     groups do not depend on the other rows."""
