@@ -1094,6 +1094,389 @@ __global__ void fill_u8_kernel(uint8_t* p, int64_t n, uint8_t v) {
   if (i < n) p[i] = v;
 }
 
+// ---------------------------------------------------------------- two rows per CU
+// Batches of more rows than CUs (K <= 3, rows of up to 16384 * 2 tokens):
+// two 512-thread workgroups per CU, each ranking its own row with 64 keys
+// per thread in registers (thread t holds tokens 4 (t + 512 j) + e).  While
+// one workgroup waits (its row's loads, a barrier, a block-wide scan, the
+// ranking of a bucket) the other's sweeps keep the SIMDs busy.  The passes
+// are those of select_lds_kernel: a 12-bit first digit below the row's
+// shared key bits, 11-bit passes while a bucket is too large to rank
+// directly, the buckets' keys to LDS lists ranked by two threads per key,
+// one compare per key and boundary to assign, ties at t_k by index.
+namespace two {
+
+constexpr int kT = 512;
+constexpr int kW = kT / kWave;       // wavefronts per workgroup
+constexpr int kC = 16;               // 16-byte chunks per thread: rows of up to 4 kC kT = 32768 tokens
+constexpr int kFirstBins = 4096;     // first pass; later passes take 2048 bins per boundary
+constexpr int kL = 512;              // list slots per boundary
+
+// 16-byte buffer loads of a row's raw score bits (zero past its 4N bytes);
+// 4-byte loads when the row is not 16-byte aligned.
+__device__ __forceinline__ void load_row(const float* row, int32_t N, uint32_t (&raw)[kC][4]) {
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(row), 0, N * 4, 0x00020000);
+  const int tid = threadIdx.x;
+  if ((reinterpret_cast<uintptr_t>(row) & 15u) == 0u) {
+#pragma unroll
+    for (int j = 0; j < kC; ++j) {
+      const u32x4 v = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, 16 * (tid + j * kT), 0, 0));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) raw[j][e] = v[e];
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kC; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        raw[j][e] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, 16 * (tid + j * kT) + 4 * e, 0, 0);
+  }
+}
+
+// Exclusive prefix over the workgroup's threads (thread order) and the total.
+__device__ int32_t block_scan(int32_t v, int32_t* wave_tmp, int32_t* total) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int32_t inc = wave_incl_scan(v);
+  if (lane == kWave - 1) wave_tmp[wave] = inc;
+  __syncthreads();
+  int32_t off = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kW; ++w) {
+    const int32_t c = wave_tmp[w];
+    off += (w < wave) ? c : 0;
+    tot += c;
+  }
+  __syncthreads();
+  *total = tot;
+  return off + inc - v;
+}
+
+// Bucket of this thread's eight bins (8t .. 8t + 7) that holds rank rem.
+__device__ __forceinline__ void take_bucket8(int32_t before, const int32_t (&h)[8], int32_t rem,
+                                             int sh, uint32_t* prefix, int32_t* rem_out,
+                                             int32_t* size_out) {
+  const int tid = threadIdx.x;
+  int32_t run = before;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    if (run <= rem && rem < run + h[q]) {
+      *prefix |= (uint32_t)(8 * tid + q) << sh;
+      *rem_out = rem - run;
+      *size_out = h[q];
+    }
+    run += h[q];
+  }
+}
+
+// rank_in_list with two threads per key: lanes 2i, 2i + 1 take key i and half
+// of the list each (slots from n on hold kPad).
+__device__ __forceinline__ void rank_in_list2(const uint32_t* list, int32_t n, int t, int32_t rem,
+                                              uint32_t* prefix_out, int32_t* rem_out) {
+  const int i = t >> 1, q = t & 1;
+  const int32_t m = ((n + 7) >> 3) << 2;   // half length, a multiple of 4
+  const uint32_t x = i < n ? list[i] : kPad;
+  const uint32_t* part = list + q * m;
+  int32_t less = 0, leq = 0;
+  for (int r = 0; r < m; r += 4) {   // r uniform
+    const u32x4 y = *reinterpret_cast<const u32x4*>(&part[r]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      less += y[e] < x ? 1 : 0;
+      leq += y[e] <= x ? 1 : 0;
+    }
+  }
+  // the two lanes of key i: quad permutation [1,0,3,2]
+  less += __builtin_amdgcn_update_dpp(0, less, 0xb1, 0xf, 0xf, false);
+  leq += __builtin_amdgcn_update_dpp(0, leq, 0xb1, 0xf, 0xf, false);
+  if (q == 0 && i < n && less <= rem && rem < leq) {
+    *prefix_out = x;
+    *rem_out = rem - less;
+  }
+}
+
+template <int NB>
+__global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(4))) void select_two_kernel(const float* __restrict__ score,
+                                                           int32_t B, int32_t N, Counts cnt,
+                                                           uint8_t* __restrict__ group_out) {
+  static_assert(NB >= 1 && NB <= 2, "two boundaries' histograms fit the first pass's bins");
+  __shared__ __attribute__((aligned(16))) int32_t hist[kFirstBins];
+  __shared__ __attribute__((aligned(16))) uint32_t s_list[NB][kL];
+  __shared__ int32_t wave_tmp[kW];
+  __shared__ uint32_t red_min[kW], red_max[kW];
+  __shared__ int32_t tie_pre[kC * kW];
+  __shared__ uint32_t s_prefix[NB];
+  __shared__ int32_t s_rem[NB], s_size[NB], s_nlist[NB];
+  constexpr int kPart = kT / NB;        // threads per boundary when ranking
+  constexpr int kRankMax = kPart / 2;   // a bucket ranked directly: two threads per key
+  static_assert(2 * ((kRankMax + 7) / 8) * 4 <= kL, "list slots cover both halves");
+  int32_t bnd[NB];   // the bounds in scalar registers (see select_lds_kernel)
+#pragma unroll
+  for (int k = 0; k < NB; ++k) {
+    bnd[k] = cnt.bound[k];
+    asm volatile("" : "+s"(bnd[k]));
+  }
+  auto live = [&](int k) { return bnd[k] < N; };
+  auto bound_of = [&](int k) { return NB == 1 || k == 0 ? bnd[0] : bnd[NB - 1]; };
+
+  for (int32_t b = blockIdx.x; b < B; b += gridDim.x) {
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    uint32_t key[kC][4];
+    load_row(score + (size_t)b * N, N, key);
+    // ---- keys, the smallest and largest
+    uint32_t kmin = kPad, kmax = 0u;
+#pragma unroll
+    for (int j = 0; j < kC; ++j) {
+      if (4 * (j + 1) * kT <= N) {   // uniform: the whole chunk lies inside the row
+#pragma unroll
+        for (int e = 0; e < 4; ++e) key[j][e] = desc_key(__uint_as_float(key[j][e]));
+        kmin = min(kmin, min(min(key[j][0], key[j][1]), min(key[j][2], key[j][3])));
+        kmax = max(kmax, max(max(key[j][0], key[j][1]), max(key[j][2], key[j][3])));
+        continue;
+      }
+      const int32_t left = N - 4 * (tid + j * kT);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        key[j][e] = desc_key(__uint_as_float(key[j][e])) | (e < left ? 0u : kPad);
+        if (key[j][e] != kPad) {
+          kmin = min(kmin, key[j][e]);
+          kmax = max(kmax, key[j][e]);
+        }
+      }
+    }
+    wave_min_max(kmin, kmax);
+    if (lane == 0) {
+      red_min[wave] = kmin;
+      red_max[wave] = kmax;
+    }
+#pragma unroll
+    for (int i = 0; i < kFirstBins / kT; i += 4)
+      *reinterpret_cast<i32x4_t*>(&hist[kFirstBins / kT * tid + i]) = i32x4_t{0, 0, 0, 0};
+#pragma unroll
+    for (int k = 0; k < NB; ++k) s_list[k][tid] = kPad;   // slots past a bucket's size
+    if (tid < NB) {
+      s_rem[tid] = bound_of(tid);
+      s_size[tid] = N;
+      s_nlist[tid] = 0;
+    }
+    __syncthreads();
+    kmin = red_min[0];
+    kmax = red_max[0];
+#pragma unroll
+    for (int w = 1; w < kW; ++w) {
+      kmin = min(kmin, red_min[w]);
+      kmax = max(kmax, red_max[w]);
+    }
+#pragma unroll
+    for (int j = 0; j < kC; ++j)
+      if (4 * (j + 1) * kT > N)   // uniform: slots past the row's end take its largest key
+#pragma unroll
+        for (int e = 0; e < 4; ++e) key[j][e] = key[j][e] == kPad ? kmax : key[j][e];
+    const uint32_t diff = kmin ^ kmax;
+    int lo = diff == 0u ? 0 : 32 - __clz(diff);
+    uint32_t fixed = lo == 32 ? 0u : ~((1u << lo) - 1u);
+    if (tid < NB) s_prefix[tid] = kmin & fixed;
+    __syncthreads();
+
+    // ---- first pass over every key: a 12-bit digit, 4096 bins
+    if (lo > 0) {
+      const int width = lo < 12 ? lo : 12;
+      const int sh = lo - width;
+      const uint32_t dm = (1u << width) - 1u;
+#pragma unroll
+      for (int j = 0; j < kC; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) atomicAdd(&hist[(key[j][e] >> sh) & dm], 1);
+      __syncthreads();
+      const i32x4_t ha = *reinterpret_cast<const i32x4_t*>(&hist[8 * tid]);
+      const i32x4_t hb = *reinterpret_cast<const i32x4_t*>(&hist[8 * tid + 4]);
+      const int32_t h8[8] = {ha[0], ha[1], ha[2], ha[3], hb[0], hb[1], hb[2], hb[3]};
+      int32_t tot;
+      const int32_t before = block_scan(((h8[0] + h8[1]) + (h8[2] + h8[3])) + ((h8[4] + h8[5]) + (h8[6] + h8[7])),
+                                        wave_tmp, &tot);
+#pragma unroll
+      for (int k = 0; k < NB; ++k)
+        if (live(k)) take_bucket8(before, h8, bnd[k], sh, &s_prefix[k], &s_rem[k], &s_size[k]);
+      fixed |= dm << sh;
+      lo = sh;
+    }
+    __syncthreads();
+
+    // ---- further passes while a bucket is too large to rank directly (every
+    // live boundary narrows in each, as they share `fixed`)
+    while (lo > 0) {
+      uint32_t pre[NB];
+      int32_t rem[NB];
+      bool any = false;
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+        any = any || (live(k) && __builtin_amdgcn_readfirstlane(s_size[k]) > kRankMax);
+        pre[k] = __builtin_amdgcn_readfirstlane(s_prefix[k]);
+        rem[k] = __builtin_amdgcn_readfirstlane(s_rem[k]);
+      }
+      if (!any) break;
+      const int width = lo < 11 ? lo : 11;
+      const int sh = lo - width;
+      const uint32_t dm = (1u << width) - 1u;
+#pragma unroll
+      for (int i = 0; i < NB * 2048 / kT; i += 4)
+        *reinterpret_cast<i32x4_t*>(&hist[NB * 2048 / kT * tid + i]) = i32x4_t{0, 0, 0, 0};
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < kC; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int k = 0; k < NB; ++k)
+            if (live(k) && (key[j][e] & fixed) == pre[k]) atomicAdd(&hist[k * 2048 + ((key[j][e] >> sh) & dm)], 1);
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+        if (!live(k)) continue;   // uniform
+        const i32x4_t hv = *reinterpret_cast<const i32x4_t*>(&hist[k * 2048 + 4 * tid]);
+        const int32_t h4[4] = {hv[0], hv[1], hv[2], hv[3]};
+        int32_t tot;
+        const int32_t before = block_scan((h4[0] + h4[1]) + (h4[2] + h4[3]), wave_tmp, &tot);
+        take_bucket4(before, h4, rem[k], sh, &s_prefix[k], &s_rem[k], &s_size[k]);
+      }
+      __syncthreads();
+      fixed |= dm << sh;
+      lo = sh;
+    }
+
+    // ---- the buckets' keys to their lists (room reserved per chunk of 4
+    // keys and wavefront), then each boundary's bucket ranked by two threads
+    // per key
+    if (lo > 0) {
+      uint32_t pre[NB];
+#pragma unroll
+      for (int k = 0; k < NB; ++k) pre[k] = __builtin_amdgcn_readfirstlane(s_prefix[k]);
+      const uint32_t span = 1u << lo;   // lo < 32 after the first pass
+#pragma unroll
+      for (int j = 0; j < kC; ++j) {
+#pragma unroll
+        for (int k = 0; k < NB; ++k) {
+          if (!live(k)) continue;   // uniform
+          bool in[4];
+          uint64_t bal[4];
+          int32_t c = 0;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            in[e] = key[j][e] - pre[k] < span;
+            bal[e] = __ballot(in[e]);
+            c += __popcll(bal[e]);
+          }
+          if (c == 0) continue;   // uniform
+          int32_t at = lds_reserve(&s_nlist[k], c);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (in[e]) s_list[k][at + lanes_below(bal[e])] = key[j][e];
+            at += __popcll(bal[e]);
+          }
+        }
+      }
+      const int kb = tid / kPart, t = tid % kPart;
+      const int32_t rem = __builtin_amdgcn_readfirstlane(s_rem[kb]);   // before any thread rewrites it
+      __syncthreads();
+      const int32_t n = __builtin_amdgcn_readfirstlane(s_nlist[kb]);
+      if (bound_of(kb) < N && t < ((2 * n + kWave - 1) & ~(kWave - 1)))   // wavefronts holding a key
+        rank_in_list2(s_list[kb], n, t, rem, &s_prefix[kb], &s_rem[kb]);
+      __syncthreads();
+    }
+
+    // ---- assignment (as in select_lds_kernel)
+    uint32_t tk[NB], thr[NB];
+    int32_t need[NB];
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      tk[k] = live(k) ? __builtin_amdgcn_readfirstlane(s_prefix[k]) : kPad;
+      need[k] = live(k) ? __builtin_amdgcn_readfirstlane(s_rem[k]) : 0;
+      thr[k] = need[k] == 0 ? tk[k] : tk[k] + 1u;
+    }
+    uint32_t gp[kC];
+#pragma unroll
+    for (int j = 0; j < kC; ++j) {
+      uint32_t g = 0u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        uint32_t c = 0u;
+#pragma unroll
+        for (int k = 0; k < NB; ++k) c += key[j][e] >= thr[k] ? 1u : 0u;
+        g |= c << (8 * e);
+      }
+      gp[j] = g;
+    }
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      if (need[k] == 0) continue;   // uniform
+      // ties per (chunk, wavefront): index order is chunk-major, then
+      // wavefront, lane and element
+#pragma unroll
+      for (int j = 0; j < kC; ++j) {
+        int32_t c = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) c += __popcll(__ballot(key[j][e] == tk[k]));
+        if (lane == 0) tie_pre[j * kW + wave] = c;
+      }
+      __syncthreads();
+      if (wave == 0) {   // exclusive scan of the kC * kW counts, 64 lanes over runs
+        constexpr int E = kC * kW, PER = (E + kWave - 1) / kWave;
+        int32_t v[PER], sum = 0;
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+          const int i = lane * PER + q;
+          v[q] = i < E ? tie_pre[i] : 0;
+          sum += v[q];
+        }
+        const int32_t inc = wave_incl_scan(sum);
+        int32_t run = inc - sum;
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+          const int i = lane * PER + q;
+          if (i < E) tie_pre[i] = run;
+          run += v[q];
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < kC; ++j) {
+        int32_t before = tie_pre[j * kW + wave];
+        bool eq[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          eq[e] = key[j][e] == tk[k];
+          before += __popcll(__ballot(eq[e]) & lt_mask);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          gp[j] += (eq[e] && before >= need[k]) ? 1u << (8 * e) : 0u;
+          before += eq[e] ? 1 : 0;
+        }
+      }
+      __syncthreads();   // tie_pre is reused by the next boundary
+    }
+    uint8_t* out = group_out + (size_t)b * N;
+    const bool aligned4 = (reinterpret_cast<uintptr_t>(out) & 3u) == 0u;
+#pragma unroll
+    for (int j = 0; j < kC; ++j) {
+      const int32_t n = 4 * (tid + j * kT);
+      if (aligned4 && 4 * (j + 1) * kT <= N)   // uniform
+        *reinterpret_cast<uint32_t*>(out + n) = gp[j];
+      else if (n < N)
+        store_groups(out, n, N, gp[j], aligned4);
+    }
+    __syncthreads();   // the shared state is reset for the next row
+  }
+}
+
+}  // namespace two
+
 }  // namespace
 
 hsa_status launch_select(const float* score, int32_t B, int32_t N, const int32_t* count,
@@ -1116,6 +1499,15 @@ hsa_status launch_select(const float* score, int32_t B, int32_t N, const int32_t
     if (hipGetDevice(&dev) == hipSuccess)
       (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     const unsigned grid = (unsigned)(B < cus ? B : cus);
+    if (B > cus && K - 1 <= 2) {
+      // more rows than CUs: two 512-thread workgroups per CU, a row each
+      const unsigned grid2 = (unsigned)(B < 2 * cus ? B : 2 * cus);
+      if (K - 1 == 1)
+        two::select_two_kernel<1><<<grid2, two::kT, 0, s>>>(score, B, N, c, group_out);
+      else
+        two::select_two_kernel<2><<<grid2, two::kT, 0, s>>>(score, B, N, c, group_out);
+      return launch_status();
+    }
     // rows start on 16-byte boundaries: the next row can be loaded into LDS directly
     const bool dma = N % 4 == 0 && (reinterpret_cast<uintptr_t>(score) & 15u) == 0;
     switch (K - 1) {
