@@ -1109,7 +1109,9 @@ namespace two {
 constexpr int kT = 512;
 constexpr int kW = kT / kWave;       // wavefronts per workgroup
 constexpr int kC = 16;               // 16-byte chunks per thread: rows of up to 4 kC kT = 32768 tokens
-constexpr int kFirstBins = 4096;     // first pass; later passes take 2048 bins per boundary
+constexpr int kFirstBits = 14;       // first pass: 16384 bins (64 KB); later passes 2048 per boundary
+constexpr int kBins = 1 << kFirstBits;
+constexpr int kBinsPerThread = kBins / kT;   // 32, read as 8 16-byte vectors
 constexpr int kL = 512;              // list slots per boundary
 
 // 16-byte buffer loads of a row's raw score bits (zero past its 4N bytes);
@@ -1154,23 +1156,6 @@ __device__ int32_t block_scan(int32_t v, int32_t* wave_tmp, int32_t* total) {
   return off + inc - v;
 }
 
-// Bucket of this thread's eight bins (8t .. 8t + 7) that holds rank rem.
-__device__ __forceinline__ void take_bucket8(int32_t before, const int32_t (&h)[8], int32_t rem,
-                                             int sh, uint32_t* prefix, int32_t* rem_out,
-                                             int32_t* size_out) {
-  const int tid = threadIdx.x;
-  int32_t run = before;
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    if (run <= rem && rem < run + h[q]) {
-      *prefix |= (uint32_t)(8 * tid + q) << sh;
-      *rem_out = rem - run;
-      *size_out = h[q];
-    }
-    run += h[q];
-  }
-}
-
 // rank_in_list with two threads per key: lanes 2i, 2i + 1 take key i and half
 // of the list each (slots from n on hold kPad).
 __device__ __forceinline__ void rank_in_list2(const uint32_t* list, int32_t n, int t, int32_t rem,
@@ -1197,12 +1182,47 @@ __device__ __forceinline__ void rank_in_list2(const uint32_t* list, int32_t n, i
   }
 }
 
+// Bucket of this thread's first-pass bins (kBinsPerThread t onward; bin i
+// holds the keys with key >> sh == first + i) that holds rank rem, for the one
+// thread whose bins hold it: the 4-bin group first, then the bin inside it
+// (two rounds of reads, not one per bin).
+__device__ void take_bucket_first(const int32_t* hist, int32_t before, int32_t rem, uint32_t first,
+                                  int sh, uint32_t* prefix, int32_t* rem_out, int32_t* size_out) {
+  const int tid = threadIdx.x;
+  const int32_t* mine = hist + kBinsPerThread * tid;
+  int32_t gsum[kBinsPerThread / 4];
+#pragma unroll
+  for (int g = 0; g < kBinsPerThread / 4; ++g) {
+    const i32x4_t v = *reinterpret_cast<const i32x4_t*>(&mine[4 * g]);
+    gsum[g] = (v[0] + v[1]) + (v[2] + v[3]);
+  }
+  int32_t run = before, grp = 0;
+#pragma unroll
+  for (int g = 0; g < kBinsPerThread / 4 - 1; ++g) {
+    const bool past = run + gsum[g] <= rem;   // rank rem lies after group g
+    grp += past ? 1 : 0;
+    run += past ? gsum[g] : 0;
+    if (!past) break;
+  }
+  const i32x4_t v = *reinterpret_cast<const i32x4_t*>(&mine[4 * grp]);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if (q == 3 || rem < run + v[q]) {
+      *prefix = (first + (uint32_t)(kBinsPerThread * tid + 4 * grp + q)) << sh;
+      *rem_out = rem - run;
+      *size_out = v[q];
+      return;
+    }
+    run += v[q];
+  }
+}
+
 template <int NB>
 __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(4))) void select_two_kernel(const float* __restrict__ score,
                                                            int32_t B, int32_t N, Counts cnt,
                                                            uint8_t* __restrict__ group_out) {
   static_assert(NB >= 1 && NB <= 2, "two boundaries' histograms fit the first pass's bins");
-  __shared__ __attribute__((aligned(16))) int32_t hist[kFirstBins];
+  __shared__ __attribute__((aligned(16))) int32_t hist[kBins];
   __shared__ __attribute__((aligned(16))) uint32_t s_list[NB][kL];
   __shared__ int32_t wave_tmp[kW];
   __shared__ uint32_t red_min[kW], red_max[kW];
@@ -1256,8 +1276,8 @@ __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(4))) void se
       red_max[wave] = kmax;
     }
 #pragma unroll
-    for (int i = 0; i < kFirstBins / kT; i += 4)
-      *reinterpret_cast<i32x4_t*>(&hist[kFirstBins / kT * tid + i]) = i32x4_t{0, 0, 0, 0};
+    for (int i = 0; i < kBins / (4 * kT); ++i)   // consecutive lanes, consecutive 16 bytes
+      *reinterpret_cast<i32x4_t*>(&hist[4 * (i * kT + tid)]) = i32x4_t{0, 0, 0, 0};
 #pragma unroll
     for (int k = 0; k < NB; ++k) s_list[k][tid] = kPad;   // slots past a bucket's size
     if (tid < NB) {
@@ -1278,32 +1298,48 @@ __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(4))) void se
       if (4 * (j + 1) * kT > N)   // uniform: slots past the row's end take its largest key
 #pragma unroll
         for (int e = 0; e < 4; ++e) key[j][e] = key[j][e] == kPad ? kmax : key[j][e];
-    const uint32_t diff = kmin ^ kmax;
-    int lo = diff == 0u ? 0 : 32 - __clz(diff);
-    uint32_t fixed = lo == 32 ? 0u : ~((1u << lo) - 1u);
-    if (tid < NB) s_prefix[tid] = kmin & fixed;
-    __syncthreads();
+    kmin = __builtin_amdgcn_readfirstlane(kmin);
+    kmax = __builtin_amdgcn_readfirstlane(kmax);
+    // the bucket that holds a boundary is the keys with one value of
+    // key >> lo: its bits above lo are `fixed`
+    int lo = 0;
+    uint32_t fixed = ~0u;
+    if (tid < NB) s_prefix[tid] = kmin;   // every key equal: no pass
 
-    // ---- first pass over every key: a 12-bit digit, 4096 bins
-    if (lo > 0) {
-      const int width = lo < 12 ? lo : 12;
-      const int sh = lo - width;
-      const uint32_t dm = (1u << width) - 1u;
+    // ---- first pass over every key: bin (key >> sh) - (kmin >> sh) of
+    // kBins, sh the least shift that fits kmin .. kmax into them (so the bins
+    // follow the keys' actual range, not their common bit prefix)
+    if (kmin != kmax) {
+      int sh = 32 - __clz(kmax - kmin) - kFirstBits;
+      sh = sh < 0 ? 0 : sh;
+      if ((kmax >> sh) - (kmin >> sh) >= (uint32_t)kBins) ++sh;
+      const uint32_t first = kmin >> sh;
+      // LDS byte address of bin (key >> sh) - first: one shift-and-add per key
+      uint32_t at0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) int32_t*)hist - 4u * first;
+      asm volatile("" : "+s"(at0));   // kept an addend: one v_lshl_add per key
 #pragma unroll
       for (int j = 0; j < kC; ++j)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) atomicAdd(&hist[(key[j][e] >> sh) & dm], 1);
+        for (int e = 0; e < 4; ++e)
+          __hip_atomic_fetch_add((__attribute__((address_space(3))) int32_t*)(uintptr_t)(at0 + 4u * (key[j][e] >> sh)),
+                                 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       __syncthreads();
-      const i32x4_t ha = *reinterpret_cast<const i32x4_t*>(&hist[8 * tid]);
-      const i32x4_t hb = *reinterpret_cast<const i32x4_t*>(&hist[8 * tid + 4]);
-      const int32_t h8[8] = {ha[0], ha[1], ha[2], ha[3], hb[0], hb[1], hb[2], hb[3]};
+      // this thread's bins, read in a lane-rotated order (the sum does not
+      // care) so that one read spreads over the banks
+      int32_t mine = 0;
+#pragma unroll
+      for (int i = 0; i < kBinsPerThread / 4; ++i) {
+        const int r = (i + tid) & (kBinsPerThread / 4 - 1);
+        const i32x4_t v = *reinterpret_cast<const i32x4_t*>(&hist[kBinsPerThread * tid + 4 * r]);
+        mine += (v[0] + v[1]) + (v[2] + v[3]);
+      }
       int32_t tot;
-      const int32_t before = block_scan(((h8[0] + h8[1]) + (h8[2] + h8[3])) + ((h8[4] + h8[5]) + (h8[6] + h8[7])),
-                                        wave_tmp, &tot);
+      const int32_t before = block_scan(mine, wave_tmp, &tot);
 #pragma unroll
       for (int k = 0; k < NB; ++k)
-        if (live(k)) take_bucket8(before, h8, bnd[k], sh, &s_prefix[k], &s_rem[k], &s_size[k]);
-      fixed |= dm << sh;
+        if (live(k) && before <= bnd[k] && bnd[k] < before + mine)
+          take_bucket_first(hist, before, bnd[k], first, sh, &s_prefix[k], &s_rem[k], &s_size[k]);
+      fixed = ~0u << sh;   // sh <= 19: the range spans at most 2^32 keys
       lo = sh;
     }
     __syncthreads();
@@ -1325,8 +1361,8 @@ __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(4))) void se
       const int sh = lo - width;
       const uint32_t dm = (1u << width) - 1u;
 #pragma unroll
-      for (int i = 0; i < NB * 2048 / kT; i += 4)
-        *reinterpret_cast<i32x4_t*>(&hist[NB * 2048 / kT * tid + i]) = i32x4_t{0, 0, 0, 0};
+      for (int i = 0; i < NB * 2048 / (4 * kT); ++i)
+        *reinterpret_cast<i32x4_t*>(&hist[4 * (i * kT + tid)]) = i32x4_t{0, 0, 0, 0};
       __syncthreads();
 #pragma unroll
       for (int j = 0; j < kC; ++j)
@@ -1376,6 +1412,7 @@ __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(4))) void se
           int32_t at = lds_reserve(&s_nlist[k], c);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
+            if (bal[e] == 0ull) continue;   // uniform: no write issued for an empty element
             if (in[e]) s_list[k][at + lanes_below(bal[e])] = key[j][e];
             at += __popcll(bal[e]);
           }
