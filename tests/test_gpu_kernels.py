@@ -208,6 +208,12 @@ def _score_rows(kind, rs, B, N):
         return s
     if kind == "sorted":                # the bucket's keys in one chunk of the row
         return np.sort(rs.random((B, N)), axis=1).astype(np.float32)
+    if kind == "signed_zeros":          # 60% zeros of either sign: a boundary falls among them
+        s = rs.random((B, N)).astype(np.float32)
+        m = rs.random((B, N))
+        s[m < 0.3] = 0.0
+        s[(m >= 0.3) & (m < 0.6)] = -0.0
+        return s
     if kind == "specials":              # NaN, +-inf, +-0 mixed into normal scores
         s = rs.standard_normal((B, N)).astype(np.float32)
         m = rs.random((B, N))
@@ -220,10 +226,11 @@ def _score_rows(kind, rs, B, N):
 
 
 @pytest.mark.parametrize("kind", ["uniform", "abs_normal", "lognormal_wide", "signed", "narrow",
-                                  "few_values", "denormals", "sorted", "specials"])
+                                  "few_values", "denormals", "signed_zeros", "sorted", "specials"])
 def test_select_batch_distributions(kind):
     """Score distributions that drive the digit passes differently (wide and
-    narrow key ranges, heavy ties, special values, denormals, sorted rows),
+    narrow key ranges, heavy ties, special values, denormals, a boundary among
+    zeros of both signs, sorted rows),
     300 rows (more than the CUs: a workgroup ranks several rows, loading the
     next while it ranks the current one) at an aligned and a ragged row
     length, two and three groups; every row against the oracle."""

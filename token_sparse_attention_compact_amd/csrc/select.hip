@@ -1137,6 +1137,27 @@ __device__ __forceinline__ void load_row(const float* row, int32_t N, uint32_t (
   }
 }
 
+// A key whose ascending order is the score's descending order, as desc_key
+// but with other codes: the negated score, both zeros as +0 (0 - f) and NaN as
+// the negation of +inf (maxNum drops the NaN), mapped monotonically to an
+// unsigned integer.  Two VALU float operations and two integer ones.
+__device__ __forceinline__ uint32_t neg_key(float f) {
+  float h;
+  // written out: the compiler folds 0 - f into -f below maxNum (which may
+  // take either zero) and would quiet the difference again before the max
+  asm("v_sub_f32 %0, 0, %1\n\tv_max_f32 %0, 0xff800000, %0" : "=&v"(h) : "v"(f));
+  const uint32_t u = __float_as_uint(h);
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+}
+
+// 1 when x >= a + 1, else 0, for a < 0xffffffff: med3(x, a, a + 1) - a, with
+// no carry flag (a compare and add-with-carry needs hazard wait states).
+__device__ __forceinline__ uint32_t med3_u32(uint32_t x, uint32_t a, uint32_t a1) {
+  uint32_t r;
+  asm("v_med3_u32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(a), "v"(a1));
+  return r;
+}
+
 // Exclusive prefix over the workgroup's threads (thread order) and the total.
 __device__ int32_t block_scan(int32_t v, int32_t* wave_tmp, int32_t* total) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -1249,13 +1270,17 @@ __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(4))) void se
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     uint32_t key[kC][4];
     load_row(score + (size_t)b * N, N, key);
+    // chunks wholly inside the row: recomputed per row (kept opaque), not
+    // sixteen flags held across the loop
+    int32_t nfull = N / (4 * kT);
+    asm volatile("" : "+s"(nfull));
     // ---- keys, the smallest and largest
     uint32_t kmin = kPad, kmax = 0u;
 #pragma unroll
     for (int j = 0; j < kC; ++j) {
-      if (4 * (j + 1) * kT <= N) {   // uniform: the whole chunk lies inside the row
+      if (j < nfull) {   // uniform: the whole chunk lies inside the row
 #pragma unroll
-        for (int e = 0; e < 4; ++e) key[j][e] = desc_key(__uint_as_float(key[j][e]));
+        for (int e = 0; e < 4; ++e) key[j][e] = neg_key(__uint_as_float(key[j][e]));
         kmin = min(kmin, min(min(key[j][0], key[j][1]), min(key[j][2], key[j][3])));
         kmax = max(kmax, max(max(key[j][0], key[j][1]), max(key[j][2], key[j][3])));
         continue;
@@ -1263,7 +1288,7 @@ __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(4))) void se
       const int32_t left = N - 4 * (tid + j * kT);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        key[j][e] = desc_key(__uint_as_float(key[j][e])) | (e < left ? 0u : kPad);
+        key[j][e] = neg_key(__uint_as_float(key[j][e])) | (e < left ? 0u : kPad);
         if (key[j][e] != kPad) {
           kmin = min(kmin, key[j][e]);
           kmax = max(kmax, key[j][e]);
@@ -1295,7 +1320,7 @@ __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(4))) void se
     }
 #pragma unroll
     for (int j = 0; j < kC; ++j)
-      if (4 * (j + 1) * kT > N)   // uniform: slots past the row's end take its largest key
+      if (j >= nfull)   // uniform: slots past the row's end take its largest key
 #pragma unroll
         for (int e = 0; e < 4; ++e) key[j][e] = key[j][e] == kPad ? kmax : key[j][e];
     kmin = __builtin_amdgcn_readfirstlane(kmin);
@@ -1390,12 +1415,14 @@ __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(4))) void se
     // keys and wavefront), then each boundary's bucket ranked by two threads
     // per key
     if (lo > 0) {
-      uint32_t pre[NB];
+      uint32_t top[NB];   // a bucket is the keys with one value of key >> lo
 #pragma unroll
-      for (int k = 0; k < NB; ++k) pre[k] = __builtin_amdgcn_readfirstlane(s_prefix[k]);
-      const uint32_t span = 1u << lo;   // lo < 32 after the first pass
+      for (int k = 0; k < NB; ++k) top[k] = (uint32_t)__builtin_amdgcn_readfirstlane(s_prefix[k]) >> lo;
 #pragma unroll
       for (int j = 0; j < kC; ++j) {
+        uint32_t kt[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) kt[e] = key[j][e] >> lo;   // lo < 32 after the first pass
 #pragma unroll
         for (int k = 0; k < NB; ++k) {
           if (!live(k)) continue;   // uniform
@@ -1404,7 +1431,7 @@ __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(4))) void se
           int32_t c = 0;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            in[e] = key[j][e] - pre[k] < span;
+            in[e] = kt[e] == top[k];
             bal[e] = __ballot(in[e]);
             c += __popcll(bal[e]);
           }
@@ -1428,13 +1455,19 @@ __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(4))) void se
     }
 
     // ---- assignment (as in select_lds_kernel)
-    uint32_t tk[NB], thr[NB];
+    // key >= thr[k] counts boundary k (thr >= 1: keys of scores are at least
+    // 0x007fffff, a dead boundary's thr is kPad), as med3(key, thr - 1, thr)
+    // - (thr - 1)
+    uint32_t tk[NB], am[NB], ap[NB], asum = 0u;
     int32_t need[NB];
 #pragma unroll
     for (int k = 0; k < NB; ++k) {
       tk[k] = live(k) ? __builtin_amdgcn_readfirstlane(s_prefix[k]) : kPad;
       need[k] = live(k) ? __builtin_amdgcn_readfirstlane(s_rem[k]) : 0;
-      thr[k] = need[k] == 0 ? tk[k] : tk[k] + 1u;
+      const uint32_t thr = need[k] == 0 ? tk[k] : tk[k] + 1u;
+      am[k] = thr - 1u;
+      ap[k] = thr;
+      asum += am[k];
     }
     uint32_t gp[kC];
 #pragma unroll
@@ -1442,9 +1475,9 @@ __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(4))) void se
       uint32_t g = 0u;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        uint32_t c = 0u;
+        uint32_t c = 0u - asum;
 #pragma unroll
-        for (int k = 0; k < NB; ++k) c += key[j][e] >= thr[k] ? 1u : 0u;
+        for (int k = 0; k < NB; ++k) c += med3_u32(key[j][e], am[k], ap[k]);
         g |= c << (8 * e);
       }
       gp[j] = g;
@@ -1503,7 +1536,7 @@ __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(4))) void se
 #pragma unroll
     for (int j = 0; j < kC; ++j) {
       const int32_t n = 4 * (tid + j * kT);
-      if (aligned4 && 4 * (j + 1) * kT <= N)   // uniform
+      if (aligned4 && j < nfull)   // uniform
         *reinterpret_cast<uint32_t*>(out + n) = gp[j];
       else if (n < N)
         store_groups(out, n, N, gp[j], aligned4);
