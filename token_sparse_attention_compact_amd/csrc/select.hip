@@ -1274,13 +1274,17 @@ __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(4))) void se
     // sixteen flags held across the loop
     int32_t nfull = N / (4 * kT);
     asm volatile("" : "+s"(nfull));
-    // ---- keys, the smallest and largest
+    // ---- keys, the smallest and largest.  First 0x7fffffff - bits, one
+    // instruction, the key of a score in [+0, +inf] (larger score, smaller
+    // key, from kFastMin for +inf to kFastMax for +0); a row holding a
+    // negative score, -0 or NaN shows in its range and is keyed again below.
+    constexpr uint32_t kFastMin = 0x7fffffffu - 0x7f800000u, kFastMax = 0x7fffffffu;
     uint32_t kmin = kPad, kmax = 0u;
 #pragma unroll
     for (int j = 0; j < kC; ++j) {
       if (j < nfull) {   // uniform: the whole chunk lies inside the row
 #pragma unroll
-        for (int e = 0; e < 4; ++e) key[j][e] = neg_key(__uint_as_float(key[j][e]));
+        for (int e = 0; e < 4; ++e) key[j][e] = kFastMax - key[j][e];
         kmin = min(kmin, min(min(key[j][0], key[j][1]), min(key[j][2], key[j][3])));
         kmax = max(kmax, max(max(key[j][0], key[j][1]), max(key[j][2], key[j][3])));
         continue;
@@ -1288,10 +1292,12 @@ __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(4))) void se
       const int32_t left = N - 4 * (tid + j * kT);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        key[j][e] = neg_key(__uint_as_float(key[j][e])) | (e < left ? 0u : kPad);
-        if (key[j][e] != kPad) {
+        if (e < left) {
+          key[j][e] = kFastMax - key[j][e];
           kmin = min(kmin, key[j][e]);
           kmax = max(kmax, key[j][e]);
+        } else {
+          key[j][e] = kPad;
         }
       }
     }
@@ -1317,6 +1323,35 @@ __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(4))) void se
     for (int w = 1; w < kW; ++w) {
       kmin = min(kmin, red_min[w]);
       kmax = max(kmax, red_max[w]);
+    }
+    if (kmin < kFastMin || kmax > kFastMax) {   // uniform: keys of every score
+      uint32_t mn = kPad, mx = 0u;
+#pragma unroll
+      for (int j = 0; j < kC; ++j) {
+        const int32_t left = j < nfull ? 4 : N - 4 * (tid + j * kT);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (e < left) {
+            key[j][e] = neg_key(__uint_as_float(kFastMax - key[j][e]));
+            mn = min(mn, key[j][e]);
+            mx = max(mx, key[j][e]);
+          }
+        }
+      }
+      wave_min_max(mn, mx);
+      __syncthreads();   // every wavefront has read the first range
+      if (lane == 0) {
+        red_min[wave] = mn;
+        red_max[wave] = mx;
+      }
+      __syncthreads();
+      kmin = red_min[0];
+      kmax = red_max[0];
+#pragma unroll
+      for (int w = 1; w < kW; ++w) {
+        kmin = min(kmin, red_min[w]);
+        kmax = max(kmax, red_max[w]);
+      }
     }
 #pragma unroll
     for (int j = 0; j < kC; ++j)
@@ -1456,8 +1491,8 @@ __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(4))) void se
 
     // ---- assignment (as in select_lds_kernel)
     // key >= thr[k] counts boundary k (thr >= 1: keys of scores are at least
-    // 0x007fffff, a dead boundary's thr is kPad), as med3(key, thr - 1, thr)
-    // - (thr - 1)
+    // 0x007fffff in either form, a dead boundary's thr is kPad), as
+    // med3(key, thr - 1, thr) - (thr - 1)
     uint32_t tk[NB], am[NB], ap[NB], asum = 0u;
     int32_t need[NB];
 #pragma unroll
@@ -1469,17 +1504,16 @@ __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(4))) void se
       ap[k] = thr;
       asum += am[k];
     }
+    // the four bytes at once: sum of med3 << 8e, less asum in every byte
+    // (modulo 2^32; each byte's true sum is at most NB)
     uint32_t gp[kC];
 #pragma unroll
     for (int j = 0; j < kC; ++j) {
-      uint32_t g = 0u;
+      uint32_t g = 0u - asum * 0x01010101u;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        uint32_t c = 0u - asum;
+      for (int e = 0; e < 4; ++e)
 #pragma unroll
-        for (int k = 0; k < NB; ++k) c += med3_u32(key[j][e], am[k], ap[k]);
-        g |= c << (8 * e);
-      }
+        for (int k = 0; k < NB; ++k) g += med3_u32(key[j][e], am[k], ap[k]) << (8 * e);
       gp[j] = g;
     }
 #pragma unroll
