@@ -5,8 +5,9 @@
 // with float4 accesses, the row kept in registers when D is a multiple of
 // 256 (one read of the row from memory, statistics in float32 from the
 // registers), two passes otherwise.  Embed keeps each thread's weights in
-// registers across a block of rows; unembed keeps w_out in LDS and two rows
-// per wavefront in registers (other shapes: two passes per row).
+// registers across a block of rows; unembed (D <= 1536) runs the projection
+// on the fp32 matrix cores over shifted rows, other widths keep w_out in LDS
+// and a row per wavefront in registers (or two passes per row).
 // LayerNorm and unembed optionally apply the timestep modulation
 // LN(h) (1 + scale) + shift (MOD template flag; shift and scale are [D]
 // vectors read as float4 from L2, the same for every row).
@@ -365,6 +366,176 @@ __global__ __launch_bounds__(kUnembedWaves * kWave) void unembed_c16_reg_kernel(
   }
 }
 
+// C == 16, D = 128 G (G even, D <= 1536), on the fp32 matrix cores
+// (v_mfma_f32_16x16x4_f32: D[16x16] += A[16x4] B[4x16]; lane l holds
+// A[l%16][l/16], B[l/16][l%16] and D[4(l/16)+m][l%16], m = 0..3).  With
+// K = h[r][0], mean - K = S1/D, S1 = sum(h - K), var = S2/D - (S1/D)^2,
+// S2 = sum((h - K)^2) (shifted sums: no cancellation for rows far from 0),
+// and w' = w (1 + scale):
+//   v[r][c] = rstd_r (sum_d (h[r][d] - K) w'[c][d] - (S1/D) sum_d w'[c][d])
+//             + sum_d shift_d w[c][d],
+// the first sum on the matrix cores over (h - K), which also feeds S1 and S2.
+// A block takes 32 rows: two 16-row tiles, each split over the two halves
+// of D between two wavefronts (one per SIMD), whose partials meet in LDS.
+// Step (e, t) of group g takes d = half + 64 g + 16 e + 4 (l/16) + t on both
+// operands: one load instruction reads 64 contiguous bytes of each of 16 rows.
+constexpr int kUnMmRows = 32;
+template <typename WT, int G, bool MOD>
+__global__ __launch_bounds__(256) void unembed_mfma_kernel(const float* __restrict__ h,
+                                                           const WT* __restrict__ w_out,
+                                                           float* __restrict__ v_new, int32_t rows,
+                                                           ModVec shift, ModVec scale) {
+  constexpr int D = 128 * G, DP = D + 4;   // LDS row pitch: the 16 weight rows on distinct banks
+  __shared__ __attribute__((aligned(16))) float um_smem[16 * DP + 32 + 2 * 64 * 4 + 2 * 16 * 2 * 2];
+  float* ws = um_smem;              // w' [16][DP]
+  float* wsum = ws + 16 * DP;       // sum_d w'[c][d]
+  float* bsum = wsum + 16;          // sum_d shift_d w[c][d]
+  float* xacc = bsum + 16;          // [2 tiles][64 lanes][4]: the second half's partial products
+  float* xst = xacc + 2 * 64 * 4;   // [2 tiles][16 rows][2]: its S1, S2
+  float* st = xst + 2 * 16 * 2;     // [2 tiles][16 rows][2]: S1/D and rstd
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int tile = wave >> 1, kh = wave & 1;
+  const int i = lane & 15, q = lane >> 4;
+  const int32_t r0 = blockIdx.x * kUnMmRows + tile * 16;
+  const float* hr = h + (size_t)min(r0 + i, rows - 1) * D;   // rows past the end: a copy, not stored
+  // ---- the weights' loads first (L2-resident), then every row load of this
+  // half: loads return in order, so the weights' conversion below waits for
+  // its own loads only, while the rows stream in behind them
+  // thread t: weight row c = t / 16, 16-byte chunks (t % 16) + 16 j
+  const int c = tid >> 4;
+  constexpr int kPer = 16 / (int)sizeof(WT);   // weights per 16-byte load
+  constexpr int kChunks = D / kPer / 16;        // per thread
+  u32x4 wraw[kChunks];
+#pragma unroll
+  for (int j = 0; j < kChunks; ++j)
+    wraw[j] = *reinterpret_cast<const u32x4*>(w_out + (size_t)c * D + kPer * ((tid & 15) + 16 * j));
+  const float K = hr[0];
+  f32x4 hv[G][4];
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      hv[g][e] = *reinterpret_cast<const f32x4*>(hr + kh * (D / 2) + 64 * g + 16 * e + 4 * q);
+  {
+    float ps = 0.f, pb = 0.f;
+#pragma unroll
+    for (int j = 0; j < kChunks; ++j) {
+      const int d0 = kPer * ((tid & 15) + 16 * j);
+      const u32x4 raw = wraw[j];
+      float w[kPer];
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) {
+        if constexpr (sizeof(WT) == 2)
+          w[e] = __uint_as_float((e & 1) ? (raw[e >> 1] & 0xffff0000u) : (raw[e >> 1] << 16));
+        else
+          w[e] = __uint_as_float(raw[e]);
+      }
+#pragma unroll
+      for (int e4 = 0; e4 < kPer; e4 += 4) {
+        f32x4 o;
+        if constexpr (MOD) {
+          const f32x4 sh = load_mod4(shift, d0 + e4);
+          const f32x4 sc = load_mod4(scale, d0 + e4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            o[e] = w[e4 + e] * (1.0f + sc[e]);
+            pb = __builtin_fmaf(sh[e], w[e4 + e], pb);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = w[e4 + e];
+        }
+        ps += (o[0] + o[1]) + (o[2] + o[3]);
+        *reinterpret_cast<f32x4*>(ws + c * DP + d0 + e4) = o;
+      }
+    }
+    // the 16 threads of row c are 16 consecutive lanes
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) {
+      ps += __shfl_xor(ps, o, kWave);
+      pb += __shfl_xor(pb, o, kWave);
+    }
+    if ((tid & 15) == 0) {
+      wsum[c] = ps;
+      bsum[c] = pb;
+    }
+  }
+  __syncthreads();
+  // ---- this half's products and shifted sums
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float s1 = 0.f, s2 = 0.f;
+  const float* wrow = ws + i * DP + kh * (D / 2) + 4 * q;
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const f32x4 w4 = *reinterpret_cast<const f32x4*>(wrow + 64 * g + 16 * e);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const float a = hv[g][e][t] - K;
+        s1 += a;
+        s2 = __builtin_fmaf(a, a, s2);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, w4[t], acc, 0, 0, 0);
+      }
+    }
+  }
+  // a row's sums over its four lanes (i, i + 16, i + 32, i + 48)
+  s1 += __shfl_xor(s1, 16, kWave);
+  s2 += __shfl_xor(s2, 16, kWave);
+  s1 += __shfl_xor(s1, 32, kWave);
+  s2 += __shfl_xor(s2, 32, kWave);
+  if (kh == 1) {
+    *reinterpret_cast<f32x4*>(xacc + (tile * 64 + lane) * 4) = acc;
+    if (q == 0) {
+      xst[(tile * 16 + i) * 2] = s1;
+      xst[(tile * 16 + i) * 2 + 1] = s2;
+    }
+  }
+  __syncthreads();
+  if (kh == 1) return;
+  {
+    const f32x4 o = *reinterpret_cast<const f32x4*>(xacc + (tile * 64 + lane) * 4);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) acc[m] += o[m];
+    if (q == 0) {
+      s1 += xst[(tile * 16 + i) * 2];
+      s2 += xst[(tile * 16 + i) * 2 + 1];
+      const float mk = s1 / (float)D;                 // mean - K
+      const float var = fmaxf(s2 / (float)D - mk * mk, 0.f);
+      st[(tile * 16 + i) * 2] = mk;
+      st[(tile * 16 + i) * 2 + 1] = 1.0f / sqrtf(var + kLnEps);
+    }
+  }
+  // (LDS operations of one wavefront complete in order: no barrier)
+  const float wc = wsum[i], bc = MOD ? bsum[i] : 0.f;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int rr = 4 * q + m;
+    const float mk = st[(tile * 16 + rr) * 2], rs = st[(tile * 16 + rr) * 2 + 1];
+    if (r0 + rr < rows) v_new[(size_t)(r0 + rr) * 16 + i] = rs * (acc[m] - mk * wc) + bc;
+  }
+}
+
+template <typename WT, bool MOD>
+bool launch_unembed_mfma(const float* h, const WT* w_out, float* v_new, int32_t rows, int32_t D,
+                         ModVec shift, ModVec scale, hipStream_t s) {
+  if (D % 256 != 0 || D > 1536) return false;   // wider: the row loads would not fit the registers
+  const unsigned blocks = (unsigned)cdiv(rows, kUnMmRows);
+  auto launch = [&](auto g) {
+    constexpr int G = decltype(g)::value;
+    unembed_mfma_kernel<WT, G, MOD><<<blocks, 256, 0, s>>>(h, w_out, v_new, rows, shift, scale);
+  };
+  switch (D / 128) {
+    case 2: launch(std::integral_constant<int, 2>{}); break;
+    case 4: launch(std::integral_constant<int, 4>{}); break;
+    case 6: launch(std::integral_constant<int, 6>{}); break;
+    case 8: launch(std::integral_constant<int, 8>{}); break;
+    case 10: launch(std::integral_constant<int, 10>{}); break;
+    default: launch(std::integral_constant<int, 12>{}); break;
+  }
+  return true;
+}
+
 template <typename WT, bool MOD>
 bool launch_unembed_reg(const float* h, const WT* w_out, float* v_new, int32_t rows, int32_t D,
                         ModVec shift, ModVec scale, hipStream_t s) {
@@ -475,6 +646,11 @@ void unembed_dispatch(const float* h, const void* w_out, float* v_new, int32_t r
                       int32_t C, hsa_dtype dt, ModVec shift, ModVec scale, hipStream_t s) {
   const int blocks = cdiv(rows, kRowsPerBlock);
   if (C == 16) {
+    if (dt == HSA_BF16 ? launch_unembed_mfma<bf16, MOD>(h, (const bf16*)w_out, v_new, rows, D, shift,
+                                                        scale, s)
+                       : launch_unembed_mfma<float, MOD>(h, (const float*)w_out, v_new, rows, D,
+                                                         shift, scale, s))
+      return;
     if (dt == HSA_BF16 ? launch_unembed_reg<bf16, MOD>(h, (const bf16*)w_out, v_new, rows, D, shift,
                                                        scale, s)
                        : launch_unembed_reg<float, MOD>(h, (const float*)w_out, v_new, rows, D,
