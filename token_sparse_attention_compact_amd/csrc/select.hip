@@ -1463,14 +1463,13 @@ __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(4))) void se
           if (!live(k)) continue;   // uniform
           bool in[4];
           uint64_t bal[4];
-          int32_t c = 0;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             in[e] = kt[e] == top[k];
             bal[e] = __ballot(in[e]);
-            c += __popcll(bal[e]);
           }
-          if (c == 0) continue;   // uniform
+          if ((bal[0] | bal[1] | bal[2] | bal[3]) == 0ull) continue;   // uniform: the common case
+          const int32_t c = (__popcll(bal[0]) + __popcll(bal[1])) + (__popcll(bal[2]) + __popcll(bal[3]));
           int32_t at = lds_reserve(&s_nlist[k], c);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
