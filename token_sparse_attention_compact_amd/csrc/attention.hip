@@ -357,8 +357,14 @@ __device__ __forceinline__ void attn_bf16_body(
   // synchronises: that stage has landed and every wave is done with the
   // stage two back, which is refilled with the next tile.  The LDS ring keeps
   // two stages resident and two in flight.
+  // First K and V fragments of a step, read at the end of the one before
+  // (kin / vin: this step takes them; kout / vout: this step reads them for
+  // the next).  V of the next step's PV is always in a stage already waited
+  // for; K of the next step's scores only when that step opens no stage
+  // (after an odd step), so only odd steps read K ahead.
+  bf16x8 kpre, vpre;
   auto step = [&](f32x16& s_cur, f32x16& s_nxt, u32x4* pw_cur, const u32x4* pw_prev, int u,
-                  bool pv) {
+                  bool pv, bool kin, bool vin, bool kout, bool vout) {
     if (u & 1) {
       const int it = u >> 1;   // stage of sub-tile u; sub-tile u+1 opens stage it+1
       if (it + 2 < ntiles) wait_tiles_barrier<DH, 1>();
@@ -372,8 +378,8 @@ __device__ __forceinline__ void attn_bf16_body(
     const char* kt = k_sub(u + 1);
     const uint32_t vt = v_sub(u - 1);
     bf16x8 kf[2], vf[2];
-    kf[0] = kfrag(kt, 0);
-    if (pv) vf[0] = vfrag(vt, 0);
+    kf[0] = kin ? kpre : kfrag(kt, 0);
+    if (pv) vf[0] = vin ? vpre : vfrag(vt, 0);
     float l2[2] = {-0.f, -0.f};   // -0 + x == x: the first adds fold away
     // slot j: S^T MFMA j of sub-tile u+1, the first EPS/2 exponentials of the
     // slot's score elements of sub-tile u, PV MFMA j of sub-tile u-1, the rest
@@ -400,6 +406,8 @@ __device__ __forceinline__ void attn_bf16_body(
         l2[(j * (EPS / 2) + pr) & 1] += p[2 * pr] + p[2 * pr + 1];
       }
     }
+    if (vout) vpre = vfrag(v_sub(u), 0);
+    if (kout) kpre = kfrag(k_sub(u + 2), 0);
     float lt = l2[0] + l2[1];
     if (__ballot(lt > kRaiseSum) != 0ull) {   // after PV(u-1): O is complete up to sub-tile u-1
       raise(s_cur, &s_nxt);
@@ -443,7 +451,7 @@ __device__ __forceinline__ void attn_bf16_body(
   if (nsub == 1) {
     finish(sa, pwa, pwb, 0, false);
   } else {
-    step(sa, sb, pwa, pwb, 0, false);
+    step(sa, sb, pwa, pwb, 0, false, false, false, false, true);
     int u = 1;
     // whole ring cycles (2 * NST sub-tiles) unrolled from u = 1 mod 2 * NST:
     // every stage offset is then a constant that the LDS reads carry as an
@@ -452,17 +460,17 @@ __device__ __forceinline__ void attn_bf16_body(
       const int u0 = 2 * NST * cyc + 1;
 #pragma unroll
       for (int c = 0; c < 2 * NST; c += 2) {
-        step(sb, sa, pwb, pwa, u0 + c, true);
-        step(sa, sb, pwa, pwb, u0 + c + 1, true);
+        step(sb, sa, pwb, pwa, u0 + c, true, false, true, true, true);
+        step(sa, sb, pwa, pwb, u0 + c + 1, true, true, true, false, true);
       }
       u = u0 + 2 * NST;
     }
     for (; u + 2 < nsub; u += 2) {
-      step(sb, sa, pwb, pwa, u, true);
-      step(sa, sb, pwa, pwb, u + 1, true);
+      step(sb, sa, pwb, pwa, u, true, false, true, true, true);
+      step(sa, sb, pwa, pwb, u + 1, true, true, true, false, true);
     }
     if (u + 1 < nsub) {
-      step(sb, sa, pwb, pwa, u, true);
+      step(sb, sa, pwb, pwa, u, true, false, true, false, false);
       finish(sa, pwa, pwb, u + 1, true);
     } else {
       finish(sb, pwb, pwa, u, true);
