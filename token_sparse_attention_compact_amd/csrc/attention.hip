@@ -469,12 +469,18 @@ __device__ __forceinline__ void attn_bf16_body(
       step(sb, sa, pwb, pwa, u, true, false, true, true, true);
       step(sa, sb, pwa, pwb, u + 1, true, true, true, false, true);
     }
+    // one step more when two sub-tiles remain; its scores and P^T are then
+    // moved into the roles of the single finish below (a finish inlined once
+    // per parity leaves the registers of the two copies in swapped roles,
+    // which the allocator resolves with spills)
     if (u + 1 < nsub) {
       step(sb, sa, pwb, pwa, u, true, false, true, false, false);
-      finish(sa, pwa, pwb, u + 1, true);
-    } else {
-      finish(sb, pwb, pwa, u, true);
+      sb = sa;
+      pwa[0] = pwb[0];
+      pwa[1] = pwb[1];
+      ++u;
     }
+    finish(sb, pwb, pwa, u, true);
   }
 
   float l_tot;
