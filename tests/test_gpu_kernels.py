@@ -382,7 +382,7 @@ def test_layernorm_embed_unembed(dtype):
     assert rel_l2(host(vn), O.layer_norm(h) @ w_out.T.astype(np.float64)) < 1e-5
 
 
-@pytest.mark.parametrize("D", [128, 256, 512, 1280, 1536, 2048, 5120])
+@pytest.mark.parametrize("D", [128, 256, 512, 1024, 1280, 1536, 2048, 5120])
 @pytest.mark.parametrize("rows", [1, 17, 8190])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_embed_unembed_widths(D, rows, dtype):

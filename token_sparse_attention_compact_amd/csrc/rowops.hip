@@ -5,7 +5,8 @@
 // with float4 accesses, the row kept in registers when D is a multiple of
 // 256 (one read of the row from memory, statistics in float32 from the
 // registers), two passes otherwise.  Embed keeps each thread's weights in
-// registers across a block of rows; unembed (D <= 1536) runs the projection
+// registers across a block of rows, the columns spread so that every SIMD
+// carries the same share of the FMAs; unembed (D <= 1536) runs the projection
 // on the fp32 matrix cores over shifted rows, other widths keep w_out in LDS
 // and a row per wavefront in registers (or two passes per row).
 // LayerNorm and unembed optionally apply the timestep modulation
@@ -238,6 +239,72 @@ __global__ __launch_bounds__(kEmbedThreads) void embed_kernel_c16(const float* _
       out[o] = acc;
     }
     *reinterpret_cast<f32x4*>(h + (size_t)(r0 + j) * D + 4 * q) = out;
+  }
+}
+
+// C == 16, D == 512 P: a block of 256 threads takes kEmbedPairRows rows over
+// all D columns; thread t owns the column pairs t + 256 p (p < P) and keeps
+// their 2 x 16 weights in registers, so each of the chip's SIMDs issues the
+// same share of the 16 D FMAs per row (D / 4 threads per row would leave half
+// the SIMDs with a second wavefront at D = 1536); 8-byte stores, 512
+// contiguous bytes per wavefront and store.
+constexpr int kEmbedPairRows = 16;
+template <typename WT, int P>
+__global__ __launch_bounds__(256) void embed_pairs_kernel(const float* __restrict__ x,
+                                                          const int32_t* __restrict__ idx,
+                                                          const WT* __restrict__ w_in,
+                                                          float* __restrict__ h, int32_t rows) {
+  constexpr int D = 512 * P;
+  __shared__ f32x4 sx[kEmbedPairRows][4];
+  const int32_t r0 = blockIdx.x * kEmbedPairRows;
+  const int32_t nr = min(rows - r0, kEmbedPairRows);
+  const int t = threadIdx.x;
+  const bool gx = t < 4 * nr;   // thread t gathers chunk t % 4 of row t / 4
+  const int32_t src = gx ? idx[r0 + t / 4] : 0;
+  float w[2 * P][16];
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    // rows 2q, 2q + 1 of w_in (q = t + 256 p): 32 consecutive values
+    constexpr int kPer = 16 / (int)sizeof(WT);
+    const u32x4* wr = reinterpret_cast<const u32x4*>(w_in + (size_t)(t + 256 * p) * 32);
+#pragma unroll
+    for (int i = 0; i < 32 / kPer; ++i) {
+      const u32x4 raw = wr[i];
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) {
+        const int f = i * kPer + e;
+        if constexpr (sizeof(WT) == 2) {
+          const uint32_t word = raw[e >> 1];
+          w[2 * p + (f >> 4)][f & 15] = __uint_as_float((e & 1) ? (word & 0xffff0000u) : (word << 16));
+        } else {
+          w[2 * p + (f >> 4)][f & 15] = __uint_as_float(raw[e]);
+        }
+      }
+    }
+  }
+  if (gx) sx[t / 4][t % 4] = reinterpret_cast<const f32x4*>(x + (size_t)src * 16)[t % 4];
+  __syncthreads();
+  for (int32_t j = 0; j < nr; ++j) {
+    float xv[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x4 v = sx[j][i];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) xv[4 * i + e] = v[e];
+    }
+    float* hr = h + (size_t)(r0 + j) * D + 2 * t;
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      f32x2 out;
+#pragma unroll
+      for (int o = 0; o < 2; ++o) {
+        float acc = 0.f;
+#pragma unroll
+        for (int c = 0; c < 16; ++c) acc = __builtin_fmaf(xv[c], w[2 * p + o][c], acc);
+        out[o] = acc;
+      }
+      *reinterpret_cast<f32x2*>(hr + 512 * p) = out;
+    }
   }
 }
 
@@ -687,6 +754,20 @@ hsa_status launch_layernorm(const float* h, void* out, int32_t rows, int32_t D, 
 hsa_status launch_embed(const float* x, const int32_t* idx, const void* w_in, float* h,
                         int32_t rows, int32_t C, int32_t D, hsa_dtype dt, hipStream_t s) {
   if (rows == 0) return HSA_OK;
+  if (C == 16 && D % 512 == 0 && D <= 2048) {
+    const unsigned grid = (unsigned)cdiv(rows, kEmbedPairRows);
+#define HSA_EMBED_CASE(P)                                                                           \
+  case P:                                                                                          \
+    if (dt == HSA_BF16)                                                                            \
+      embed_pairs_kernel<bf16, P><<<grid, 256, 0, s>>>(x, idx, (const bf16*)w_in, h, rows);        \
+    else                                                                                           \
+      embed_pairs_kernel<float, P><<<grid, 256, 0, s>>>(x, idx, (const float*)w_in, h, rows);      \
+    return launch_status();
+    switch (D / 512) {
+      HSA_EMBED_CASE(1) HSA_EMBED_CASE(2) HSA_EMBED_CASE(3) HSA_EMBED_CASE(4)
+    }
+#undef HSA_EMBED_CASE
+  }
   if (C == 16 && D % 4 == 0) {
     const dim3 grid((unsigned)cdiv(rows, kEmbedRows), (unsigned)cdiv(D / 4, kEmbedThreads));
     if (dt == HSA_BF16)
