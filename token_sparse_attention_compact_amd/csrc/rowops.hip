@@ -465,9 +465,9 @@ __global__ __launch_bounds__(256) void unembed_mfma_kernel(const float* __restri
   const int i = lane & 15, q = lane >> 4;
   const int32_t r0 = blockIdx.x * kUnMmRows + tile * 16;
   const float* hr = h + (size_t)min(r0 + i, rows - 1) * D;   // rows past the end: a copy, not stored
-  // ---- the weights' loads first (L2-resident), then every row load of this
-  // half: loads return in order, so the weights' conversion below waits for
-  // its own loads only, while the rows stream in behind them
+  // ---- the weights' loads first (L2-resident), then the first row loads of
+  // this half: loads return in order, so the weights' conversion below waits
+  // for its own loads only, while the rows stream in behind them
   // thread t: weight row c = t / 16, 16-byte chunks (t % 16) + 16 j
   const int c = tid >> 4;
   constexpr int kPer = 16 / (int)sizeof(WT);   // weights per 16-byte load
@@ -476,13 +476,20 @@ __global__ __launch_bounds__(256) void unembed_mfma_kernel(const float* __restri
 #pragma unroll
   for (int j = 0; j < kChunks; ++j)
     wraw[j] = *reinterpret_cast<const u32x4*>(w_out + (size_t)c * D + kPer * ((tid & 15) + 16 * j));
+  // the rows stream through a ring of LA groups (4 loads each): a wavefront
+  // issues in order, so with every load of the half issued up front the
+  // matrix-core chain could not start before the last load had been accepted
+  // by the memory pipeline, and ran after the data instead of beside it
   const float K = hr[0];
   f32x4 hv[G][4];
-#pragma unroll
-  for (int g = 0; g < G; ++g)
+  constexpr int LA = G < 4 ? G : 4;
+  auto load_group = [&](int g) {
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       hv[g][e] = *reinterpret_cast<const f32x4*>(hr + kh * (D / 2) + 64 * g + 16 * e + 4 * q);
+  };
+#pragma unroll
+  for (int g = 0; g < LA; ++g) load_group(g);
   {
     float ps = 0.f, pb = 0.f;
 #pragma unroll
@@ -534,6 +541,7 @@ __global__ __launch_bounds__(256) void unembed_mfma_kernel(const float* __restri
   const float* wrow = ws + i * DP + kh * (D / 2) + 4 * q;
 #pragma unroll
   for (int g = 0; g < G; ++g) {
+    if (g + LA < G) load_group(g + LA);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const f32x4 w4 = *reinterpret_cast<const f32x4*>(wrow + 64 * g + 16 * e);
@@ -545,6 +553,7 @@ __global__ __launch_bounds__(256) void unembed_mfma_kernel(const float* __restri
         acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, w4[t], acc, 0, 0, 0);
       }
     }
+    if (LA < G) __builtin_amdgcn_sched_barrier(0);
   }
   // a row's sums over its four lanes (i, i + 16, i + 32, i + 48)
   s1 += __shfl_xor(s1, 16, kWave);
