@@ -152,6 +152,31 @@ __device__ __forceinline__ void issue_tile(const bf16* k, const bf16* v, int32_t
   }
 }
 
+// One of the 2 LOADS loads of a K / V tile pair (part p: K for even p, V for
+// odd p, slice p / 2), for loads spread over the MFMA stream of a step.
+// Loads at or past nkv return zero (row0 = nkv: zero-byte loads).
+struct TileLoads {
+  i32x4 rk, rv;
+  uint32_t sk, sv;
+};
+template <int DH>
+__device__ __forceinline__ TileLoads tile_loads(const bf16* k, const bf16* v, int32_t row0,
+                                                int32_t nkv, int32_t ldk, int32_t h, uint32_t sk,
+                                                uint32_t sv) {
+  const int32_t rows_left = nkv - row0;
+  const uint32_t nbytes = rows_left > 0 ? (uint32_t)rows_left * (uint32_t)ldk * 2u : 0u;
+  const size_t off = ((size_t)row0 * ldk + (size_t)h * DH) * 2;
+  return TileLoads{buffer_rsrc(reinterpret_cast<const char*>(k) + off, nbytes),
+                   buffer_rsrc(reinterpret_cast<const char*>(v) + off, nbytes), sk, sv};
+}
+__device__ __forceinline__ void tile_part(const TileLoads& t, int p, const uint32_t* voff_k,
+                                          const uint32_t* voff_v, int wave) {
+  const int j = p >> 1;
+  const uint32_t blk = (uint32_t)__builtin_amdgcn_readfirstlane((j * NW + wave) * 1024);
+  if (p & 1) dma16(t.sv + blk, voff_v[j], t.rv);
+  else dma16(t.sk + blk, voff_k[j], t.rk);
+}
+
 // Wait until at most OUT tiles' loads of this wave are in flight, then
 // synchronise the workgroup.  No memory fence: the only LDS writes are the
 // tile loads, whose completion vmcnt reports.
@@ -355,8 +380,9 @@ __device__ __forceinline__ void attn_bf16_body(
   // sub-tile u next to each, so the VALU work is spread evenly over the MFMA
   // stream.  Before the first sub-tile of a stage is scored, the workgroup
   // synchronises: that stage has landed and every wave is done with the
-  // stage two back, which is refilled with the next tile.  The LDS ring keeps
-  // two stages resident and two in flight.
+  // stage two back, which is refilled with the next tile (one load after
+  // every second score MFMA of that step).  The LDS ring keeps two stages
+  // resident and two in flight.
   // First K and V fragments of a step, read at the end of the one before
   // (kin / vin: this step takes them; kout / vout: this step reads them for
   // the next).  V of the next step's PV is always in a stage already waited
@@ -365,15 +391,17 @@ __device__ __forceinline__ void attn_bf16_body(
   bf16x8 kpre, vpre;
   auto step = [&](f32x16& s_cur, f32x16& s_nxt, u32x4* pw_cur, const u32x4* pw_prev, int u,
                   bool pv, bool kin, bool vin, bool kout, bool vout) {
+    TileLoads tl;
     if (u & 1) {
       const int it = u >> 1;   // stage of sub-tile u; sub-tile u+1 opens stage it+1
       if (it + 2 < ntiles) wait_tiles_barrier<DH, 1>();
       else wait_tiles_barrier<DH, 0>();
-      if (it + NST - 1 < ntiles) {
-        const int ns = (it + NST - 1) & (NST - 1);
-        issue_tile<DH>(k, v, kv_begin + (it + NST - 1) * BKV, nkv, D, h, sK_lds + ns * TILEB,
-                   sV_lds + ns * TILEB, voff_k, voff_v, wave);
-      }
+      // the refill of the stage two back: tile it+NST-1, or past the last
+      // tile zero-byte loads into that (free) stage, so the issue needs no
+      // branch; its loads are spread over the step's MFMA slots below
+      const int ns = (it + NST - 1) & (NST - 1);
+      const int32_t r0 = it + NST - 1 < ntiles ? kv_begin + (it + NST - 1) * BKV : nkv;
+      tl = tile_loads<DH>(k, v, r0, nkv, D, h, sK_lds + ns * TILEB, sV_lds + ns * TILEB);
     }
     const char* kt = k_sub(u + 1);
     const uint32_t vt = v_sub(u - 1);
@@ -388,6 +416,10 @@ __device__ __forceinline__ void attn_bf16_body(
     for (int j = 0; j < NS; ++j) {
       if (j + 1 < NS) kf[(j + 1) & 1] = kfrag(kt, j + 1);
       s_nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[j & 1], qf[j], j == 0 ? negm : s_nxt, 0, 0, 0);
+      // one refill load after every second score MFMA of an odd step: a
+      // wavefront issues in order, and the loads issued together at the
+      // step's start held back the MFMAs behind them
+      if ((u & 1) && j % 2 == 1 && j / 2 < 2 * LOADS) tile_part(tl, j / 2, voff_k, voff_v, wave);
       float p[EPS];
 #pragma unroll
       for (int e = 0; e < EPS / 2; ++e) p[e] = __builtin_amdgcn_exp2f(s_cur[EPS * j + e]);
@@ -483,6 +515,7 @@ __device__ __forceinline__ void attn_bf16_body(
     finish(sb, pwb, pwa, u, true);
   }
 
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // zero-byte tile loads land before exit
   float l_tot;
   {
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
