@@ -11,7 +11,8 @@ cached Euler + score.  Inputs (random-init weights, mid-run K/V caches and
 sampler state) are generated on the device before timing.
 
 Also measured in the same run: the attention kernel alone (HIP events on its
-stream), also at other active fractions and at the 14B-shaped layer, the full
+stream), also at other active fractions, at the 14B-shaped layer and on
+all-zero operands (the clock it runs at depends on the operand values), the full
 T = 40 sampling loop from fresh latents (also under other schedules and
 against dense sampling), iteration time
 against the active fraction, the Euler pass on a working set past the
@@ -362,6 +363,38 @@ def attention_sweep(H, model, c, fracs=(1.0, 0.5, 0.25, 0.125, 0.0625, 0.05), re
         rows.append({"n_active": nA, "ms": round(t * 1e3, 3), "tflops": round(4.0 * nA * c.N * D / t / 1e12, 1)})
     out["heads_64_wide"] = {"N": c.N, "heads": Hh, "head_dim": Dh, "runs": rows}
     del kc, vc
+    return out
+
+
+def attention_operand_data(H, c, n_active: int, reps: int = 10, rounds: int = 3):
+    """The attention launch of the step (|A| queries over N cached rows, the
+    stack's heads) on two inputs of the same shapes: N(0,1) caches and
+    queries, as in the workload, and all-zero ones.  Same kernel, grid and
+    instruction stream; only the operand values differ, and with them the
+    switching power of the matrix cores and so the clock the chip holds.
+    Interleaved rounds, HIP events; the fastest round of each is kept."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7 * 1000 + 11)
+    bf = torch.bfloat16
+    data = {"normal": [torch.randn((c.N, c.D), generator=g, device="cuda").to(bf) for _ in range(2)]
+                      + [torch.randn((n_active, c.D), generator=g, device="cuda").to(bf)],
+            "zero": [torch.zeros((c.N, c.D), dtype=bf, device="cuda") for _ in range(2)]
+                    + [torch.zeros((n_active, c.D), dtype=bf, device="cuda")]}
+    o = torch.empty((n_active, c.D), dtype=bf, device="cuda")
+    ws = torch.empty(max(1, H.hsa_attn_workspace_size(n_active, c.N, c.H, c.Dh)), dtype=torch.uint8,
+                     device="cuda")
+    best = {}
+    for _ in range(rounds):
+        for name, (kc, vc, q) in data.items():
+            t = _event_time(lambda: H.hsa_attn_active(q, kc, vc, o, c.H, c.Dh, ws=ws), reps)
+            best[name] = min(best.get(name, t), t)
+    flop = 4.0 * n_active * c.N * c.D
+    out = {"n_active": n_active, "N": c.N}
+    for name, t in best.items():
+        out[name] = {"us": round(t * 1e6, 1), "tflops": round(flop / t / 1e12, 1)}
+    out["zero_over_normal_speed"] = round(best["normal"] / best["zero"], 3)
+    del data, o, ws
+    torch.cuda.empty_cache()
     return out
 
 
@@ -771,6 +804,7 @@ def main():
         out["roofline"]["frac_of_attainable"] = round(attn_tflops / peaks["mfma_bf16_tflops"], 4)
     if not args.no_sweep:
         out["attention_sweep"] = attention_sweep(H, model, c)
+        out["attention_operand_data"] = attention_operand_data(H, c, n_active)
     if not args.no_loop:
         out["sampling_loop"] = sampling_loop(H, model, c, sigma)
         if not args.no_presets:
