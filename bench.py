@@ -71,8 +71,8 @@ def parse():
                    help="skip the iteration with the Wan-style block features switched on")
     p.add_argument("--no-stages", action="store_true",
                    help="skip the per-stage timing of one block at four active fractions")
-    p.add_argument("--wan14b", action="store_true",
-                   help="also time the whole 14B-shaped iteration (40 blocks, N=75600; ~155 GB of HBM)")
+    p.add_argument("--no-wan14b", action="store_true",
+                   help="skip the whole 14B-shaped iteration (40 blocks, N=75600; ~155 GB of HBM)")
     p.add_argument("--no-scaling", action="store_true", help="skip the iteration-time vs active-fraction sweep")
     p.add_argument("--no-hbm-sweep", action="store_true",
                    help="skip the Euler and batched-select bandwidth sweeps")
@@ -660,7 +660,7 @@ def gemm_bench(H, model, c, fracs=(1.0, 0.25, 0.0625)):
 
 
 def wan14b_iteration(H, steps: int = 2):
-    """The whole 14B-shaped iteration (opt-in, --wan14b): 40 blocks, N = 75600
+    """The whole 14B-shaped iteration (--no-wan14b skips it): 40 blocks, N = 75600
     (21 x 45 x 80), D 5120, 40 x 128 heads, F 13824, 512-token cross-attention,
     iteration 11 of the {40, 20, 10} schedule (|A| = 18900, 25%), regroup on;
     (a) the plain block with cross-attention, (b) with qk-RMSNorm, 3D RoPE,
@@ -670,13 +670,19 @@ def wan14b_iteration(H, steps: int = 2):
     sched = H.make_schedule(c.T, c.budgets, c.counts())
     sigma = synth.sigma_schedule(c.T)
     base, state = device_inputs(c, H, seed_base=5)
+    nA = H.hsa_n_active(sched, ITER)
+    # model FLOPs of one block stack: self-attention over all N cached rows, the
+    # block's GEMMs and the cross-attention (q and out projections, 512 text rows)
+    flop = c.L * (4.0 * nA * c.N * c.D + 2.0 * nA * c.D * (3 * c.D + c.D + 2 * c.F)
+                  + 2.0 * nA * c.D * 2 * c.D + 4.0 * nA * c.n_text * c.D)
     out = {"workload": "wan14b-shaped 40-block stack, N=75600 (21x45x80), 25% active, 512 text tokens",
-           "n_active": H.hsa_n_active(sched, ITER)}
+           "n_active": nA, "model_tflop_per_iter": round(flop / 1e12, 1)}
     for name, feats in (("xattn", ()), ("xattn_qk_rope_adaln_cfg", ("qk_norm", "rope3d", "adaln", "cfg"))):
         fm = featured_model(H, base, c, feats, c.n_text)
         fs = H.DeviceState(fm.dims, state.x, state.group, state.v_hat, state.score)
         t = timed_steps(H, fm, sched, fs, sigma, steps, 1) / steps
         out[name + "_s_per_iter"] = round(t, 3)
+        out[name + "_model_tflops"] = round(flop * (2 if "cfg" in feats else 1) / t / 1e12, 1)
         del fm, fs
         torch.cuda.empty_cache()
     return out
@@ -826,10 +832,14 @@ def main():
         if "attainable" in out:
             out["wan_features"]["qk_norm_rope"]["frac_of_attainable_copy"] = round(
                 out["wan_features"]["qk_norm_rope"]["gbs"] / out["attainable"]["copy_gbs"], 4)
-    if args.wan14b:
+    if not args.no_wan14b:
         del model, state
         torch.cuda.empty_cache()
-        out["wan14b_iteration"] = wan14b_iteration(H)
+        try:
+            out["wan14b_iteration"] = wan14b_iteration(H)
+        except (RuntimeError, torch.cuda.OutOfMemoryError) as e:   # keep the rest of the line
+            out["wan14b_iteration"] = {"error": str(e)[:200]}
+            torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(c, args.cpu_rows)
     print(json.dumps(out), flush=True)
