@@ -382,15 +382,16 @@ def test_layernorm_embed_unembed(dtype):
     assert rel_l2(host(vn), O.layer_norm(h) @ w_out.T.astype(np.float64)) < 1e-5
 
 
-@pytest.mark.parametrize("D", [128, 256, 512, 1024, 1280, 1536, 2048, 5120])
+@pytest.mark.parametrize("D", [128, 256, 512, 1024, 1280, 1536, 2048, 2304, 5120])
 @pytest.mark.parametrize("rows", [1, 17, 8190])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_embed_unembed_widths(D, rows, dtype):
     """Gather + embed (weights held per thread across a block of rows) and
     final LayerNorm + unembed (on the fp32 matrix cores when D <= 1536 is a
-    multiple of 256; weights in LDS as float32 for D = 2048; the two-pass
-    kernel otherwise), C = 16, row counts that leave partial blocks, every
-    row within tolerance."""
+    multiple of 256; weights in LDS as float32 for D = 2048; one pass with
+    four rows per wavefront for wider multiples of 256; the two-pass kernel
+    otherwise), C = 16, row counts that leave partial blocks, every row
+    within tolerance."""
     rs = np.random.default_rng(D + rows)
     C, N = 16, max(2 * rows, 64)
     x = rs.standard_normal((N, C)).astype(np.float32)

@@ -636,6 +636,176 @@ bool launch_unembed_reg(const float* h, const WT* w_out, float* v_new, int32_t r
   return true;
 }
 
+// Sum of v[0..15] over the wavefront, reduced and scattered: lane L returns the
+// total of channel ((L >> 2) & 15) (four lanes hold each), in 17 exchanges
+// instead of 16 full reductions: each halving step keeps the half of the
+// channels that the lane's next address bit selects.
+__device__ __forceinline__ float wave_sum16_scatter(const float (&v)[16]) {
+  const int lane = threadIdx.x & (kWave - 1);
+  float a[8];
+  {
+    const bool hi = (lane >> 5) & 1;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float keep = hi ? v[8 + k] : v[k], give = hi ? v[k] : v[8 + k];
+      a[k] = keep + __shfl_xor(give, 32, kWave);
+    }
+  }
+  float b[4];
+  {
+    const bool hi = (lane >> 4) & 1;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float keep = hi ? a[4 + k] : a[k], give = hi ? a[k] : a[4 + k];
+      b[k] = keep + __shfl_xor(give, 16, kWave);
+    }
+  }
+  float c2[2];
+  {
+    const bool hi = (lane >> 3) & 1;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const float keep = hi ? b[2 + k] : b[k], give = hi ? b[k] : b[2 + k];
+      c2[k] = keep + __shfl_xor(give, 8, kWave);
+    }
+  }
+  float d;
+  {
+    const bool hi = (lane >> 2) & 1;
+    const float keep = hi ? c2[1] : c2[0], give = hi ? c2[0] : c2[1];
+    d = keep + __shfl_xor(give, 4, kWave);
+  }
+  d += __shfl_xor(d, 2, kWave);
+  d += __shfl_xor(d, 1, kWave);
+  return d;
+}
+
+// Channel held by lane L after wave_sum16_scatter: bits 5, 4, 3, 2 of L are
+// bits 3, 2, 1, 0 of the channel.
+__device__ __forceinline__ int scatter_channel(int lane) {
+  return (((lane >> 5) & 1) << 3) | (((lane >> 4) & 1) << 2) | (((lane >> 3) & 1) << 1) |
+         ((lane >> 2) & 1);
+}
+
+// C = 16, wide rows (D % 256 == 0, weights too large for the LDS forms): one
+// pass over each row.  A wavefront takes kWideRows rows, so each weight load
+// from the cache feeds that many rows.  With K = h[r][0], a = (h - K)(1 + scale)
+// (a = h - K unmodulated), S1 = sum (h - K), S2 = sum (h - K)^2:
+// v[r][c] = rstd (sum_d a w[c] - (S1 / D) sum_d (1 + scale) w[c]) + sum_d shift w[c],
+// rstd = 1 / sqrt(S2 / D - (S1 / D)^2 + eps).  Rows far from zero lose nothing to
+// cancellation since the sums are shifted by a value of the row.
+constexpr int kWideRows = 4;
+template <typename WT, bool MOD>
+__global__ __launch_bounds__(256) void unembed_c16_wide_kernel(const float* __restrict__ h,
+                                                               const WT* __restrict__ w_out,
+                                                               float* __restrict__ v_new,
+                                                               int32_t rows, int32_t D,
+                                                               ModVec shift, ModVec scale) {
+  constexpr int R = kWideRows;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int32_t r0 = (blockIdx.x * (256 / kWave) + threadIdx.x / kWave) * R;
+  if (r0 >= rows) return;
+  const int nr = min(R, rows - r0);
+  const f32x4* hr[R];
+  float K[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {   // rows past the end repeat the last one (not stored)
+    hr[r] = reinterpret_cast<const f32x4*>(h + (size_t)(r0 + min(r, nr - 1)) * D);
+    K[r] = h[(size_t)(r0 + min(r, nr - 1)) * D];
+  }
+  float acc[R][16], s1[R], s2[R], ws[16], bs[16];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    s1[r] = 0.f;
+    s2[r] = 0.f;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) acc[r][c] = 0.f;
+  }
+#pragma unroll
+  for (int c = 0; c < 16; ++c) {
+    ws[c] = 0.f;
+    bs[c] = 0.f;
+  }
+  // Every load of a chunk is issued before any of its arithmetic (the rows'
+  // chunks and sixteen weight loads in flight together): issued one at a time
+  // with a wait each, the loads of a chunk would be a chain of cache round
+  // trips.
+  typedef typename std::conditional<sizeof(WT) == 2, u32x2, f32x4>::type WRaw;
+  const int nv = D / 4;
+  // a modulation vector's optional second term: read from the first when absent, weighted 0
+  const float* sc_add = MOD && scale.add ? scale.add : scale.base;
+  const float* sh_add = MOD && shift.add ? shift.add : shift.base;
+  const float sc_on = MOD && scale.add ? 1.f : 0.f, sh_on = MOD && shift.add ? 1.f : 0.f;
+  for (int i = lane; i < nv; i += kWave) {
+    f32x4 hv[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) hv[r] = hr[r][i];
+    WRaw wr[16];
+#pragma unroll
+    for (int c = 0; c < 16; ++c) wr[c] = *reinterpret_cast<const WRaw*>(w_out + (size_t)c * D + 4 * i);
+    f32x4 g = {1.f, 1.f, 1.f, 1.f}, sh = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (MOD) {   // base + (add or nothing), with no branch in the loop
+      const f32x4 sc0 = *reinterpret_cast<const f32x4*>(scale.base + 4 * i);
+      const f32x4 sc1 = *reinterpret_cast<const f32x4*>(sc_add + 4 * i);
+      const f32x4 sh0 = *reinterpret_cast<const f32x4*>(shift.base + 4 * i);
+      const f32x4 sh1 = *reinterpret_cast<const f32x4*>(sh_add + 4 * i);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        g[e] = 1.0f + __builtin_fmaf(sc_on, sc1[e], sc0[e]);
+        sh[e] = __builtin_fmaf(sh_on, sh1[e], sh0[e]);
+      }
+    }
+    f32x4 a[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float d = hv[r][e] - K[r];
+        s1[r] += d;
+        s2[r] = __builtin_fmaf(d, d, s2[r]);
+        a[r][e] = MOD ? d * g[e] : d;
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+      f32x4 w;
+      if constexpr (sizeof(WT) == 2) {
+        w[0] = __uint_as_float(wr[c][0] << 16);
+        w[1] = __uint_as_float(wr[c][0] & 0xffff0000u);
+        w[2] = __uint_as_float(wr[c][1] << 16);
+        w[3] = __uint_as_float(wr[c][1] & 0xffff0000u);
+      } else {
+        w = wr[c];
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[r][c] = __builtin_fmaf(a[r][e], w[e], acc[r][c]);
+      if constexpr (MOD) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          ws[c] = __builtin_fmaf(g[e], w[e], ws[c]);
+          bs[c] = __builtin_fmaf(sh[e], w[e], bs[c]);
+        }
+      } else {
+        ws[c] += (w[0] + w[1]) + (w[2] + w[3]);
+      }
+    }
+  }
+  const int ch = scatter_channel(lane);
+  const float wsum = wave_sum16_scatter(ws);
+  const float bsum = MOD ? wave_sum16_scatter(bs) : 0.f;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const float dot = wave_sum16_scatter(acc[r]);
+    const float t1 = wave_sum(s1[r]), t2 = wave_sum(s2[r]);
+    const float mk = t1 / (float)D;                           // mean - K
+    const float var = fmaxf(t2 / (float)D - mk * mk, 0.f);
+    const float rstd = 1.0f / sqrtf(var + kLnEps);
+    if (r < nr && (lane & 3) == 0) v_new[(size_t)(r0 + r) * 16 + ch] = rstd * (dot - mk * wsum) + bsum;
+  }
+}
+
 // v_new[j][c] = sum_d LN(h[j])[d] * w_out[c][d], C == CC known at compile time.
 template <typename WT, int CC, bool MOD>
 __global__ __launch_bounds__(256) void unembed_kernel(const float* __restrict__ h,
@@ -732,6 +902,16 @@ void unembed_dispatch(const float* h, const void* w_out, float* v_new, int32_t r
                        : launch_unembed_reg<float, MOD>(h, (const float*)w_out, v_new, rows, D,
                                                         shift, scale, s))
       return;
+    if (D % 256 == 0) {
+      const unsigned wblocks = (unsigned)cdiv(rows, (256 / kWave) * kWideRows);
+      if (dt == HSA_BF16)
+        unembed_c16_wide_kernel<bf16, MOD><<<wblocks, 256, 0, s>>>(h, (const bf16*)w_out, v_new,
+                                                                    rows, D, shift, scale);
+      else
+        unembed_c16_wide_kernel<float, MOD><<<wblocks, 256, 0, s>>>(h, (const float*)w_out, v_new,
+                                                                     rows, D, shift, scale);
+      return;
+    }
     if (dt == HSA_BF16)
       unembed_kernel<bf16, 16, MOD><<<blocks, 256, 0, s>>>(h, (const bf16*)w_out, v_new, rows, D,
                                                            shift, scale);
