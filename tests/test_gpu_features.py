@@ -102,13 +102,15 @@ def tiny(features, dtype="f32", Dh=64, H_=2, grid=(3, 5, 7), **kw):
 # ---------------------------------------------------------------- kernels
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("Dh", [64, 128])
+@pytest.mark.parametrize("Dh,H_", [(64, 3), (128, 2), (128, 12), (64, 32), (128, 40)])
 @pytest.mark.parametrize("features", [("qk_norm",), ("rope3d",), ("qk_norm", "rope3d")])
-def test_qk_norm_rope_kernel(dtype, Dh, features):
+def test_qk_norm_rope_kernel(dtype, Dh, H_, features):
     """q rows and the K-cache rows of 61 active tokens (of 105 on a 3x5x7 grid,
     ragged against the 4-row blocks) against the oracle's RMSNorm + rotation;
-    cache rows of skipped tokens stay bit-identical."""
-    c = tiny(features, dtype, Dh=Dh, H_=3 if Dh == 64 else 2)
+    cache rows of skipped tokens stay bit-identical.  Widths D = 192, 256,
+    1536 and 2048 (the loop form) and 5120 (bf16: both rows held in
+    registers, 10 chunks of 16 bytes per lane; float32: the loop form)."""
+    c = tiny(features, dtype, Dh=Dh, H_=H_)
     say(f"qk_norm_rope {dtype} Dh={Dh} {features}")
     dt = tdt(c)
     rs = np.random.default_rng(11)

@@ -13,6 +13,8 @@
 // 16-byte vector accesses.
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.h"
 
 namespace hsa {
@@ -86,11 +88,81 @@ __device__ __forceinline__ void norm_rotate_row(T* __restrict__ row, const float
   }
 }
 
+// Both rows of a token at once, held in registers: D = 64 NCH CN (NCH chunks of
+// 16 bytes per lane).  Each row is read once (its sum of squares and its
+// transform from the same registers), and the two rows' loads are in flight
+// together: for wide rows, where the loop form's second pass over a row no
+// longer finds it in the cache.
+template <typename T, bool NORM, bool ROPE, int NCH>
+__device__ __forceinline__ void norm_rotate_rows_reg(T* __restrict__ qrow, T* __restrict__ krow,
+                                                     const float* __restrict__ q_gain,
+                                                     const float* __restrict__ k_gain,
+                                                     const float2* __restrict__ cs, int32_t D,
+                                                     int32_t Dh, int lane) {
+  constexpr int CN = Chunk<T>::N;
+  typedef typename Chunk<T>::V V;
+  V v[2][NCH];
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    v[0][i] = reinterpret_cast<const V*>(qrow)[lane + kWave * i];
+    v[1][i] = reinterpret_cast<const V*>(krow)[lane + kWave * i];
+  }
+  float rs[2] = {1.0f, 1.0f};
+  if constexpr (NORM) {
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      float ss = 0.f;
+#pragma unroll
+      for (int i = 0; i < NCH; ++i)
+#pragma unroll
+        for (int e = 0; e < CN; ++e) {
+          const float x = to_f32(v[w][i][e]);
+          ss = __builtin_fmaf(x, x, ss);
+        }
+      rs[w] = 1.0f / sqrtf(wave_sum(ss) / (float)D + kRmsEps);
+    }
+  }
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {
+    const float* gain = w == 0 ? q_gain : k_gain;
+    T* row = w == 0 ? qrow : krow;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int c = lane + kWave * i;
+      float x[CN];
+#pragma unroll
+      for (int e = 0; e < CN; ++e) x[e] = to_f32(v[w][i][e]);
+      if constexpr (NORM) {
+#pragma unroll
+        for (int g4 = 0; g4 < CN / 4; ++g4) {
+          const f32x4 g = reinterpret_cast<const f32x4*>(gain + (size_t)c * CN)[g4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[4 * g4 + e] = x[4 * g4 + e] * rs[w] * g[e];
+        }
+      }
+      if constexpr (ROPE) {
+        const int pair0 = ((c * CN) % Dh) / 2;
+#pragma unroll
+        for (int pr = 0; pr < CN / 2; ++pr) {
+          const float2 t = cs[pair0 + pr];
+          const float a = x[2 * pr], b = x[2 * pr + 1];
+          x[2 * pr] = a * t.x - b * t.y;
+          x[2 * pr + 1] = a * t.y + b * t.x;
+        }
+      }
+      V o;
+#pragma unroll
+      for (int e = 0; e < CN; ++e) o[e] = from_f32<T>(x[e]);
+      reinterpret_cast<V*>(row)[c] = o;
+    }
+  }
+}
+
 // One wavefront per active token j: its q row j and its K-cache row idx[j].
 // The token's rotation (cos, sin) per pair of a head is evaluated once into
 // the wave's LDS table (one pair per lane, precise sincosf) and shared by all
 // heads of both rows.
-template <typename T, bool NORM, bool ROPE>
+template <typename T, bool NORM, bool ROPE, int NCH>
 __global__ __launch_bounds__(256) void qk_norm_rope_kernel(
     T* __restrict__ q, T* __restrict__ kc, const int32_t* __restrict__ idx, int32_t rows,
     int32_t D, int32_t Dh, const float* __restrict__ q_gain, const float* __restrict__ k_gain,
@@ -126,8 +198,13 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(
     __syncthreads();
   }
   if (!valid) return;
-  norm_rotate_row<T, NORM, ROPE>(q + (size_t)j * D, q_gain, s_cs[wid], D, Dh, lane);
-  norm_rotate_row<T, NORM, ROPE>(kc + (size_t)tok * D, k_gain, s_cs[wid], D, Dh, lane);
+  if constexpr (NCH > 0) {
+    norm_rotate_rows_reg<T, NORM, ROPE, NCH>(q + (size_t)j * D, kc + (size_t)tok * D, q_gain, k_gain,
+                                             s_cs[wid], D, Dh, lane);
+  } else {
+    norm_rotate_row<T, NORM, ROPE>(q + (size_t)j * D, q_gain, s_cs[wid], D, Dh, lane);
+    norm_rotate_row<T, NORM, ROPE>(kc + (size_t)tok * D, k_gain, s_cs[wid], D, Dh, lane);
+  }
 }
 
 __device__ __forceinline__ float silu(float x) { return x / (1.0f + expf(-x)); }
@@ -203,15 +280,28 @@ void qk_dispatch(T* q, T* kc, const int32_t* idx, int32_t rows, int32_t D, int32
                  bool rope, const float* qg, const float* kg, int32_t gh, int32_t gw,
                  hipStream_t s) {
   const int blocks = cdiv(rows, kRows);
-  if (norm && rope)
-    qk_norm_rope_kernel<T, true, true>
-        <<<blocks, 256, 0, s>>>(q, kc, idx, rows, D, Dh, qg, kg, gh, gw);
-  else if (norm)
-    qk_norm_rope_kernel<T, true, false>
-        <<<blocks, 256, 0, s>>>(q, kc, idx, rows, D, Dh, qg, kg, gh, gw);
-  else
-    qk_norm_rope_kernel<T, false, true>
-        <<<blocks, 256, 0, s>>>(q, kc, idx, rows, D, Dh, qg, kg, gh, gw);
+  // wide rows of 64 NCH 16-byte chunks (NCH 8, 10 or 12; bf16 D = 4096, 5120,
+  // 6144): both rows held in registers.  Narrower rows take the loop form,
+  // whose second read of a row hits the cache and which keeps more waves per
+  // SIMD (D = 1536 bf16: 20.0 us loop form against 20.9 us in registers,
+  // D = 5120: 202 against 162 us, at |A| = 8190 and 18900)
+  const int nch = D / Chunk<T>::N;
+  const int reg = nch % kWave == 0 ? nch / kWave : 0;
+  auto run = [&](auto nc) {
+    constexpr int NC = decltype(nc)::value;
+    if (norm && rope)
+      qk_norm_rope_kernel<T, true, true, NC><<<blocks, 256, 0, s>>>(q, kc, idx, rows, D, Dh, qg, kg, gh, gw);
+    else if (norm)
+      qk_norm_rope_kernel<T, true, false, NC><<<blocks, 256, 0, s>>>(q, kc, idx, rows, D, Dh, qg, kg, gh, gw);
+    else
+      qk_norm_rope_kernel<T, false, true, NC><<<blocks, 256, 0, s>>>(q, kc, idx, rows, D, Dh, qg, kg, gh, gw);
+  };
+  switch (reg) {
+    case 8: run(std::integral_constant<int, 8>{}); break;
+    case 10: run(std::integral_constant<int, 10>{}); break;
+    case 12: run(std::integral_constant<int, 12>{}); break;
+    default: run(std::integral_constant<int, 0>{}); break;
+  }
 }
 
 }  // namespace
