@@ -680,12 +680,9 @@ __device__ __forceinline__ float wave_sum16_scatter(const float (&v)[16]) {
   return d;
 }
 
-// Channel held by lane L after wave_sum16_scatter: bits 5, 4, 3, 2 of L are
-// bits 3, 2, 1, 0 of the channel.
-__device__ __forceinline__ int scatter_channel(int lane) {
-  return (((lane >> 5) & 1) << 3) | (((lane >> 4) & 1) << 2) | (((lane >> 3) & 1) << 1) |
-         ((lane >> 2) & 1);
-}
+// Channel held by lane L after wave_sum16_scatter: lane bits 5..2, as the
+// halving steps on lane bits 5, 4, 3, 2 chose channel bits 3, 2, 1, 0.
+__device__ __forceinline__ int scatter_channel(int lane) { return (lane >> 2) & 15; }
 
 // C = 16, wide rows (D % 256 == 0, weights too large for the LDS forms): one
 // pass over each row.  A wavefront takes kWideRows rows, so each weight load
