@@ -131,6 +131,16 @@ def attainable_peaks(reps: int = 3):
     torch.cuda.synchronize()
     t = s.elapsed_time(e) / 1e3 / reps
     mfma_tflops = n_wg * 8 * 16 * iters * 32768.0 / t / 1e12
+    rcall = lambda: lib.hsa_probe_mfma_peak_random(n_wg, iters, ct.c_void_p(out.data_ptr()), stream)
+    assert rcall() == 0
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(reps):
+        assert rcall() == 0
+    e.record()
+    torch.cuda.synchronize()
+    t = s.elapsed_time(e) / 1e3 / reps
+    mfma_random_tflops = n_wg * 8 * 16 * iters * 32768.0 / t / 1e12
     src = torch.ones(256 << 20, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
     nbytes = src.numel() * 4
@@ -151,9 +161,12 @@ def attainable_peaks(reps: int = 3):
         if best is None or gbs > best[0]:
             best = (gbs, per_thread, max_blocks)
     del src, dst, out
-    return {"mfma_bf16_tflops": round(mfma_tflops, 1), "copy_gbs": round(best[0], 1),
+    return {"mfma_bf16_tflops": round(mfma_tflops, 1),
+            "mfma_bf16_random_operands_tflops": round(mfma_random_tflops, 1),
+            "copy_gbs": round(best[0], 1),
             "copy_variant": {"loads_per_thread": best[1], "max_blocks": best[2] or "uncapped"},
-            "probe": "MFMA-only loop, 1024 workgroups x 8 waves x 64000 MFMAs; 1 GiB streaming copy "
+            "probe": "MFMA-only loop, 1024 workgroups x 8 waves x 64000 MFMAs, on one repeated operand pair "
+                     "and on four random operand pairs per lane in turn; 1 GiB streaming copy "
                      "(16-byte non-temporal accesses, read + write bytes), best of "
                      f"{len(COPY_VARIANTS)} launch shapes"}
 
@@ -808,6 +821,8 @@ def main():
         peaks = attainable_peaks()
         out["attainable"] = peaks
         out["roofline"]["frac_of_attainable"] = round(attn_tflops / peaks["mfma_bf16_tflops"], 4)
+        out["roofline"]["frac_of_attainable_random_operands"] = round(
+            attn_tflops / peaks["mfma_bf16_random_operands_tflops"], 4)
     if not args.no_sweep:
         out["attention_sweep"] = attention_sweep(H, model, c)
         out["attention_operand_data"] = attention_operand_data(H, c, n_active)

@@ -1,7 +1,8 @@
 // Attainable-peak probes (measurement only, not part of the HSA path):
 //  * a register-only loop of v_mfma_f32_32x32x16_bf16 with four independent
 //    accumulators per wavefront, eight wavefronts per workgroup: what the
-//    matrix cores deliver at the clock they hold under MFMA load;
+//    matrix cores deliver at the clock they hold under MFMA load, on one
+//    repeated operand pair and on random operands taken in turn;
 //  * a streaming copy (16-byte non-temporal loads and stores, four per
 //    thread in flight): what HBM delivers to a plain read + write stream.
 #include <hip/hip_runtime.h>
@@ -30,6 +31,54 @@ __global__ __launch_bounds__(512, 1) void mfma_peak_kernel(float* __restrict__ o
 #pragma unroll
     for (int j = 0; j < 16; ++j)
       acc[j & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[j & 3], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += acc[j][r];
+  out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+// The same loop with random operands: four (a, b) pairs of pseudo-random
+// bf16 values per lane (random sign, exponent and mantissa, magnitudes in
+// [0.5, 4)), used in turn, so that consecutive MFMAs switch their operand
+// logic as a workload's do (the loop above repeats one pair, whose MFMAs
+// switch little and draw less power, and the chip then holds a higher clock).
+__device__ __forceinline__ uint32_t probe_hash(uint32_t x) {
+  x ^= x >> 16;
+  x *= 0x7feb352dU;
+  x ^= x >> 15;
+  x *= 0x846ca68bU;
+  x ^= x >> 16;
+  return x;
+}
+
+__global__ __launch_bounds__(512, 1) void mfma_peak_random_kernel(float* __restrict__ out,
+                                                                  int32_t iters) {
+  const uint32_t tid = blockIdx.x * blockDim.x + threadIdx.x;
+  bf16x8 a[4], b[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t ha = probe_hash(tid * 64u + (uint32_t)(q * 16 + e));
+      const uint32_t hb = probe_hash(tid * 64u + (uint32_t)(q * 16 + 8 + e) + 0x9e3779b9u);
+      // bf16 bits: sign, exponent 126..128, 7 mantissa bits
+      const uint16_t ba = (uint16_t)(((ha >> 31) << 15) | ((126u + (ha >> 8) % 3u) << 7) | (ha & 0x7fu));
+      const uint16_t bb = (uint16_t)(((hb >> 31) << 15) | ((126u + (hb >> 8) % 3u) << 7) | (hb & 0x7fu));
+      a[q][e] = __builtin_bit_cast(__bf16, ba);
+      b[q][e] = __builtin_bit_cast(__bf16, bb);
+    }
+  f32x16 acc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
+  for (int32_t it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      acc[j & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j & 3], b[(j >> 2) & 3], acc[j & 3], 0, 0, 0);
   }
   float s = 0.f;
 #pragma unroll
@@ -68,6 +117,13 @@ __global__ __launch_bounds__(256) void copy_kernel(const u32x4* __restrict__ src
 extern "C" int hsa_probe_mfma_peak(int32_t n_wg, int32_t iters, float* out, void* stream) {
   if (n_wg <= 0 || iters <= 0 || out == nullptr) return -1;
   mfma_peak_kernel<<<n_wg, 512, 0, (hipStream_t)stream>>>(out, iters);
+  return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+// As hsa_probe_mfma_peak, on random operands (four operand pairs per lane in turn).
+extern "C" int hsa_probe_mfma_peak_random(int32_t n_wg, int32_t iters, float* out, void* stream) {
+  if (n_wg <= 0 || iters <= 0 || out == nullptr) return -1;
+  mfma_peak_random_kernel<<<n_wg, 512, 0, (hipStream_t)stream>>>(out, iters);
   return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 
